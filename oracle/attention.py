@@ -1,0 +1,214 @@
+"""fp64 CPU oracle for the fused attention forward (test infrastructure only).
+
+What it computes, per batch ``b`` and query head ``hq``::
+
+    S   = Q[b,hq] · K[b,hk]^T · scale  (+ bias[b,hq])      logits
+    S_ij = -inf  where causal and j > i                     mask
+    m_i = max_j S_ij,  l_i = sum_j exp(S_ij - m_i)           two-pass softmax
+    P   = exp(S - m) / l,  O = P · V[b,hk],  LSE_i = m_i + ln l_i
+
+This is the plain, materialising definition of attention:
+  * "FlashAttention principles and Triton practice" (xnwp.cn/news/15505), §2.1:
+    S = Q K^T, P = softmax(S), O = P V, with S and P held whole;
+  * FlashAttention forward tutorial (kwkr.cn/news/592482), §1.1 (the 1/sqrt(d)
+    scale), §2.1 (softmax taken as max, then sum of exp(x - max), then divide),
+    §3.4 (causal mask = strict upper triangle set to -inf);
+  * Day 26 operator acceleration (blog.ans20xx.com/posts/ai/day26), the naive
+    attention wrapper (scale, lower-triangular keep-mask, softmax, times V);
+  * "Block Attention Residual" Triton kernel post (iqiancheng.github.io), the
+    A_i formula: the additive term is added to the already-scaled logits,
+    before softmax.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of this repository):
+  * causal alignment is top-left: key j is visible to query i iff j <= i;
+  * the bias is not multiplied by ``scale`` and masked entries stay -inf
+    whatever the bias;
+  * GQA groups are contiguous: hk = hq // (Hq // Hkv);
+  * the softmax statistic emitted is one natural-log LSE = m + ln l, in the
+    units of the scaled-plus-bias logits;
+  * a row with no finite logit yields O = 0 and LSE = -inf.
+
+The tiled method reaches this same result in exact arithmetic (kwkr.cn
+tutorial, §2.2-§2.3), so the oracle is the definition itself.  The blocked
+online-softmax form below is kept only so that tests can pin the two against
+each other.
+
+Inputs are arrays of any float dtype; they are upcast to float64 exactly
+(bf16/fp16/fp32 values are representable in fp64), so the oracle sees the same
+rounded inputs the GPU path sees.
+
+This module is test infrastructure.  Only ``tests/``, ``__graft_entry__.smoke``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it; the product path
+never does.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "softmax_two_pass",
+    "attention_head_rows",
+    "attention_forward",
+    "online_attention_forward",
+    "merge_states",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def softmax_two_pass(s):
+    """Row-wise softmax over the last axis, two passes (kwkr.cn tutorial, §2.1).
+
+    Pass one takes the row max m; pass two sums exp(s - m) into l and divides.
+    Returns ``(p, m, l)``.  A row whose entries are all -inf has m = -inf,
+    l = 0 and p = 0 (no NaN is produced).
+    """
+    s = _f64(s)
+    m = s.max(axis=-1)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m_safe[..., None])
+    l = e.sum(axis=-1)
+    l_div = np.where(l > 0, l, 1.0)
+    p = np.where((l > 0)[..., None], e / l_div[..., None], 0.0)
+    return p, m, l
+
+
+def attention_head_rows(q_rows, k, v, *, rows, scale, causal, bias_rows=None):
+    """O and LSE for selected query rows of one (batch, query head).
+
+    q_rows    [n, D]  the query rows
+    rows      [n]     their absolute query indices (used by the causal mask)
+    k, v      [Nk, D] the key/value rows of the KV head these queries read
+    bias_rows [n, Nk] additive logit term for those rows, or None
+
+    Row i of the output depends only on q_i, on K, V and on bias row i, so a
+    subset of rows is the same definition evaluated on fewer rows.
+    """
+    q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
+    rows = np.asarray(rows, dtype=np.int64)
+    nk = k.shape[0]
+    s = (q_rows @ k.T) * float(scale)
+    if bias_rows is not None:
+        s = s + _f64(bias_rows)
+    if causal:
+        j = np.arange(nk, dtype=np.int64)
+        s = np.where(j[None, :] > rows[:, None], -np.inf, s)
+    p, m, l = softmax_two_pass(s)
+    o = p @ v
+    lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return o, lse
+
+
+def _check_shapes(q, k, v, bias):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, D]")
+    b, hq, nq, d = q.shape
+    bk, hkv, nk, dk = k.shape
+    if v.shape != k.shape or bk != b or dk != d:
+        raise ValueError("k and v must be [B, Hkv, Nk, D] matching q")
+    if hkv < 1 or hq % hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if bias is not None and tuple(bias.shape) != (b, hq, nq, nk):
+        raise ValueError("bias must be [B, Hq, Nq, Nk]")
+    return b, hq, hkv, nq, nk, d
+
+
+def attention_forward(q, k, v, bias=None, *, scale=None, causal=False):
+    """Full attention forward, one (b, hq) at a time.
+
+    q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D], bias [B,Hq,Nq,Nk] or None.
+    ``scale=None`` means 1/sqrt(D).  Returns ``(O [B,Hq,Nq,D], LSE [B,Hq,Nq])``
+    in float64.
+    """
+    b_, hq_, hkv, nq, nk, d = _check_shapes(q, k, v, bias)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    group = hq_ // hkv
+    o = np.empty((b_, hq_, nq, d), dtype=np.float64)
+    lse = np.empty((b_, hq_, nq), dtype=np.float64)
+    rows = np.arange(nq, dtype=np.int64)
+    for b in range(b_):
+        for h in range(hq_):
+            hk = h // group
+            o[b, h], lse[b, h] = attention_head_rows(
+                q[b, h], k[b, hk], v[b, hk], rows=rows, scale=scale, causal=causal,
+                bias_rows=None if bias is None else bias[b, h])
+    return o, lse
+
+
+def merge_states(m_a, l_a, o_a, m_b, l_b, o_b):
+    """Combine two partial softmax states over disjoint key sets.
+
+    Each state is (running max m, running sum l, un-normalised output o).
+    The combined max is the larger of the two; each side's sum and output are
+    re-expressed against it by the factor exp(m_side - m).  This is the
+    symmetric form of the merge in the kwkr.cn tutorial, §2.2.  A side whose
+    max is -inf (it saw no finite logit) contributes nothing.
+    """
+    m_a, l_a, o_a = _f64(m_a), _f64(l_a), _f64(o_a)
+    m_b, l_b, o_b = _f64(m_b), _f64(l_b), _f64(o_b)
+    m = np.maximum(m_a, m_b)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    fa = np.where(np.isfinite(m_a), np.exp(m_a - m_safe), 0.0)
+    fb = np.where(np.isfinite(m_b), np.exp(m_b - m_safe), 0.0)
+    return m, l_a * fa + l_b * fb, o_a * fa[..., None] + o_b * fb[..., None]
+
+
+def online_attention_forward(q, k, v, bias=None, *, scale=None, causal=False,
+                             block_m=64, block_n=64):
+    """Blocked forward with the online softmax update, in fp64.
+
+    Follows the kwkr.cn tutorial, §2.2-§2.3: an outer loop over row blocks of
+    Q and an inner loop over column blocks of K/V.  For each column block the
+    running max becomes m_new = max(m_old, rowmax(S_ij)); the old sum and the
+    old output are both multiplied by alpha = exp(m_old - m_new); the block's
+    exp(S_ij - m_new) is added to the sum and its product with V_j to the
+    output; the division by l happens once, after the last block.  While the
+    running max is still -inf, alpha is taken as 0 instead of exp(-inf + inf)
+    (the NaN trap of "FlashAttention principles and Triton practice", §5.1).
+
+    Only tests use this, to pin the two-pass definition against the merge
+    formula on small inputs; it is not a model of any GPU kernel.
+    """
+    b_, hq_, hkv, nq, nk, d = _check_shapes(q, k, v, bias)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    bias = None if bias is None else _f64(bias)
+    group = hq_ // hkv
+    o = np.zeros((b_, hq_, nq, d))
+    lse = np.zeros((b_, hq_, nq))
+    for b in range(b_):
+        for h in range(hq_):
+            hk = h // group
+            for r0 in range(0, nq, block_m):
+                r1 = min(r0 + block_m, nq)
+                rows = np.arange(r0, r1)
+                m_i = np.full(r1 - r0, -np.inf)
+                l_i = np.zeros(r1 - r0)
+                acc = np.zeros((r1 - r0, d))
+                for c0 in range(0, nk, block_n):
+                    c1 = min(c0 + block_n, nk)
+                    s = (q[b, h, r0:r1] @ k[b, hk, c0:c1].T) * scale
+                    if bias is not None:
+                        s = s + bias[b, h, r0:r1, c0:c1]
+                    if causal:
+                        cols = np.arange(c0, c1)
+                        s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
+                    m_new = np.maximum(m_i, s.max(axis=1))
+                    m_use = np.where(np.isfinite(m_new), m_new, 0.0)
+                    alpha = np.where(np.isfinite(m_i), np.exp(m_i - m_use), 0.0)
+                    p = np.exp(s - m_use[:, None])
+                    l_i = l_i * alpha + p.sum(axis=1)
+                    acc = acc * alpha[:, None] + p @ v[b, hk, c0:c1]
+                    m_i = m_new
+                ok = l_i > 0
+                o[b, h, r0:r1] = np.where(ok[:, None], acc / np.where(ok, l_i, 1.0)[:, None], 0.0)
+                lse[b, h, r0:r1] = np.where(ok, m_i + np.log(np.where(ok, l_i, 1.0)), -np.inf)
+    return o, lse
