@@ -70,6 +70,8 @@ def softmax_two_pass(s):
     l = 0 and p = 0 (no NaN is produced).
     """
     s = _f64(s)
+    if s.shape[-1] == 0:  # no key at all: the "no finite logit" case
+        return s.copy(), np.full(s.shape[:-1], -np.inf), np.zeros(s.shape[:-1])
     m = s.max(axis=-1)
     m_safe = np.where(np.isfinite(m), m, 0.0)
     e = np.exp(s - m_safe[..., None])

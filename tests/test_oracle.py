@@ -103,3 +103,12 @@ def test_shape_errors():
         attention_forward(q, k, k, None, scale=1.0)
     with pytest.raises(ValueError):
         attention_forward(q, np.zeros((1, 3, 4, 4)), np.zeros((1, 3, 4, 4)), None, scale=1.0)
+
+
+def test_no_keys_gives_zero_output_and_minus_inf_lse():
+    """Nk = 0: no row sees a key; by the no-finite-logit reading O = 0 and LSE = -inf."""
+    q = np.ones((1, 2, 3, 4))
+    k = np.zeros((1, 1, 0, 4))
+    for causal in (False, True):
+        o, lse = attention_forward(q, k, k, None, scale=1.0, causal=causal)
+        assert o.shape == (1, 2, 3, 4) and np.all(o == 0) and np.all(lse == -np.inf)
