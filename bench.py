@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one fa_forward call (one kernel launch) over the whole workload, with
+inputs already resident in HBM.  The default workload is B=2, H=16, S=4096,
+D=64, bf16, causal.  Timing follows the CUDA-event method of the Day 26 post
+(blog.ans20xx.com/posts/ai/day26): W untimed warm-up steps, then K steps, each
+bracketed by its own pair of events on the stream the kernel runs on, plus one
+pair around all K.  Prints one JSON line.
+
+value     = 4*B*H*S^2*D / t_step in TFLOP/s (the post's formula, not halved
+            for causal), t_step = wall time of the K steps / K;
+roofline  = the kernel's own rate against the chip's peak: useful flops
+            (visible query-key pairs only) per launch / mean launch time for
+            matrix-core-bound workloads, or algorithmic bytes / launch time for
+            the bias-streaming workload;
+cpu_baseline = the fp64 oracle, timed on the host on a bounded sample of the
+            same workload (whole heads), scaled to the same metric.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# Same workload, same metric, measured on an H100-SXM by the Day 26 post
+# (flash-attn v2 row of its report): context, not a target.
+PAGE_FLASH_ATTN_V2_TFLOPS = 11.57
+METRIC = ("attention TFLOPS (4·B·H·S²·D/t) and % MFMA bf16 peak at "
+          "B2 H16 S4096 D64 causal")
+KERNEL_SOURCE = os.path.join(ROOT, "tiled_attention_forward_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target host time for the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(w, q, k, v, bias, target_s: float):
+    """Time the oracle on whole heads of the same workload until about target_s."""
+    import numpy as np
+    import torch
+
+    from oracle import attention_head_rows
+
+    grp = w.Hq // w.Hkv
+    rows = np.arange(w.Nq)
+    done, t_used = 0, 0.0
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    for b, h in heads:
+        hk = h // grp
+        qh = q[b, h].float().cpu().numpy().astype(np.float64)
+        kh = k[b, hk].float().cpu().numpy().astype(np.float64)
+        vh = v[b, hk].float().cpu().numpy().astype(np.float64)
+        bh = None if bias is None else bias[b, h].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        attention_head_rows(qh, kh, vh, rows=rows, scale=w.scale, causal=w.causal, bias_rows=bh)
+        t_used += time.perf_counter() - t0
+        done += 1
+        if t_used >= target_s:
+            break
+    per_head_flops = w.metric_flops() / (w.B * w.Hq)
+    return {"value": round(per_head_flops * done / t_used / 1e12, 6), "unit": "TFLOPS",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hq} (batch, head) slices of {w.name}, fp64 NumPy, "
+                      f"{t_used:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the forward has no "
+              f"cross-GPU path to measure", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from tiled_attention_forward_amd import binding, metrics
+    from tiled_attention_forward_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    dev = torch.device("cuda:0")
+    lib = binding.load_library()
+    q, k, v, bias = make_inputs(w, seed=args.seed, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    dtype_code = binding._dtype_code(q)
+    call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                 bias.data_ptr() if bias is not None else None, o.data_ptr(), lse.data_ptr(),
+                 w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal), dtype_code,
+                 stream.cuda_stream)
+
+    def step():
+        st = lib.fa_forward(*call_args)
+        if st != 0:
+            raise binding.FaError(st, binding.fa_status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    ms_per_step = total_ms / K
+    launch_ms = statistics.fmean(per)
+    assert torch.isfinite(lse).all(), "non-finite LSE in the benchmark output"
+
+    value = w.metric_flops() / (ms_per_step / 1e3) / 1e12
+    peak = metrics.MFMA_PEAK_TFLOPS[w.dtype]
+    if w.bias:
+        achieved = w.io_bytes() / (launch_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": metrics.HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / metrics.HBM_PEAK_GBS, 4)}
+    else:
+        achieved = w.useful_flops() / (launch_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    roof["traffic"] = traffic_for(w.name)
+
+    out = {
+        "metric": METRIC if w.name == HEADLINE else
+        f"attention TFLOPS (4·B·H·Nq·Nk·D/t) at {w.name}",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGE_FLASH_ATTN_V2_TFLOPS, 2) if w.name == HEADLINE else None,
+        "dtype": w.dtype,
+        "data": "synthetic: i.i.d. N(0,1) inputs from a seeded generator",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
+                   "Nk": w.Nk, "D": w.D, "causal": w.causal, "bias": w.bias,
+                   "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100.0 * value / metrics.MFMA_PEAK_TFLOPS["bf16"], 2),
+        "useful_tflops": round(w.useful_flops() / (ms_per_step / 1e3) / 1e12, 2),
+        "launch_ms": {"mean": round(launch_ms, 5), "median": round(statistics.median(per), 5),
+                      "p90": round(per[int(len(per) * 0.9)], 5), "min": round(per[0], 5)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, bias, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

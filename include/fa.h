@@ -1,0 +1,109 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused attention forward library (libfa.so).
+ *
+ * The operation, per batch b and query head hq (hk = hq / (Hq / Hkv)):
+ *
+ *     S   = Q[b,hq] . K[b,hk]^T * scale  (+ bias[b,hq])          [Nq x Nk]
+ *     S_ij = -inf  if causal and j > i   (top-left aligned)
+ *     O[b,hq]   = softmax_rows(S) . V[b,hk]                        [Nq x D]
+ *     LSE[b,hq] = log(sum_j exp(S_ij))  (natural log, per row)     [Nq]
+ *
+ * This is the attention of "FlashAttention principles and Triton practice"
+ * (xnwp.cn/news/15505, §2.1) computed the tiled way of §2.2 there and of the
+ * kwkr.cn/news/592482 tutorial (§2.2-§2.3): K/V column blocks are streamed past
+ * a resident Q row block with the online softmax update, so S and P are never
+ * written to memory.  The per-row statistic kept for a recompute-based backward
+ * (kwkr.cn §2.4) is emitted as one LSE value per row.  The optional additive
+ * logit term is the fused "logit residual" of the Block Attention Residual post
+ * (iqiancheng.github.io): it is added to the already-scaled logits, tile by
+ * tile, before the softmax.  Grouped-query attention maps query head hq to KV
+ * head hq / (Hq / Hkv), i.e. contiguous groups.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are dense, contiguous, row-major device memory owned by the
+ *    caller:  q, o [B, Hq, Nq, D];  k, v [B, Hkv, Nk, D];
+ *    bias [B, Hq, Nq, Nk] (may be NULL);  lse [B, Hq, Nq] float32.
+ *  - q, k, v, bias and o share one element type (fa_dtype); lse is float32.
+ *  - q, k, v, o and bias must be 16-byte aligned; lse 4-byte aligned.
+ *  - o and lse must not overlap each other or any input.
+ *  - scale is used as given (pass 1/sqrt(D) for the usual attention); any
+ *    finite value, including 0 and negative values, is accepted.
+ *  - A row that sees no key (Nk == 0) gets O = 0 and LSE = -inf.
+ *  - B == 0, Hq == 0 or Nq == 0 is an empty problem: nothing is launched.
+ *  - The library allocates no memory, keeps no state between calls, never
+ *    synchronises and never copies between host and device.  It is reentrant.
+ *  - Errors in the arguments are reported synchronously, as a nonzero status,
+ *    before anything is launched.  A launch failure reported by the runtime is
+ *    FA_ERR_HIP.  Faults during execution surface at the caller's next
+ *    synchronisation on the stream.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v, bias and o. */
+typedef enum fa_dtype {
+  FA_DTYPE_BF16 = 0,
+  FA_DTYPE_FP16 = 1,
+  FA_DTYPE_FP32 = 2
+} fa_dtype;
+
+/* Status codes returned by fa_check_args and fa_forward. */
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL_POINTER = 1, /* q, o or lse is NULL while the problem is not empty, or    */
+                           /* k or v is NULL while Nk > 0                             */
+  FA_ERR_BAD_SIZE = 2,     /* a size is negative, or Hkv < 1 while Hq > 0                */
+  FA_ERR_HEAD_GROUPS = 3,  /* Hq is not a multiple of Hkv                                */
+  FA_ERR_HEAD_DIM = 4,     /* D is not 64 or 128 (other head sizes are rejected, never   */
+                           /* silently truncated)                                        */
+  FA_ERR_DTYPE = 5,        /* dtype is not one of fa_dtype                               */
+  FA_ERR_SCALE = 6,        /* scale is NaN or infinite                                   */
+  FA_ERR_ALIGNMENT = 7,    /* a tensor pointer is not aligned as required above          */
+  FA_ERR_OVERLAP = 8,      /* o or lse overlaps another buffer                           */
+  FA_ERR_TOO_LARGE = 9,    /* a size exceeds the kernel's index range: B, Hq, Nq and Nk  */
+                           /* must be < 2^30 and B*Hq*ceil(Nq/128) < 2^31                */
+  FA_ERR_HIP = 10          /* the HIP runtime rejected the launch                        */
+} fa_status;
+
+/*
+ * Validate the arguments of fa_forward without touching the GPU (pure host
+ * code: no HIP call, no pointer dereference).  Returns FA_OK or the first
+ * fa_status that applies.
+ */
+int fa_check_args(const void* q, const void* k, const void* v, const void* bias,
+                  const void* o, const float* lse,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                  float scale, int causal, int dtype);
+
+/*
+ * Fused attention forward.  Writes o (dtype, rounded to nearest even) and lse
+ * (float32) for every (b, hq, row).  bias may be NULL.  causal != 0 applies the
+ * top-left causal mask.  stream is a hipStream_t (NULL = the null stream); the
+ * work is enqueued on it and the call returns without waiting.
+ *
+ * Arithmetic: products in the input type on the matrix cores with float32
+ * accumulation; softmax statistics in float32; the probabilities are rounded to
+ * the input type before the P.V product (float32 inputs keep them in float32).
+ */
+int fa_forward(const void* q, const void* k, const void* v, const void* bias,
+               void* o, float* lse,
+               int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+               float scale, int causal, int dtype, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* Static version string of the library, e.g. "fa 0.1.0 gfx950". */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,84 @@
+"""Helpers shared by the GPU parity tests: run the HIP path, run the oracle on
+the same input bits, compare against the stated tolerances.
+
+Tolerances (absolute, on O upcast to float64, and on LSE):
+  bf16 / fp16 inputs: max |O - O_ref| <= 1e-2 and mean |O - O_ref| <= 1e-3
+  fp32 inputs:        max |O - O_ref| <= 1e-5
+  LSE (all dtypes):   max |LSE - LSE_ref| <= 1e-3
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import attention_forward, attention_head_rows
+from tiled_attention_forward_amd import binding
+
+O_TOL = {"bf16": (1e-2, 1e-3), "fp16": (1e-2, 1e-3), "fp32": (1e-5, 1e-5)}
+LSE_TOL = 1e-3
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def errors(o, lse, o_ref, lse_ref):
+    o, lse = np.asarray(o, np.float64), np.asarray(lse, np.float64)
+    assert np.isfinite(o).all(), "non-finite output"
+    d = np.abs(o - o_ref)
+    both = np.isinf(lse) & np.isinf(lse_ref) & (np.sign(lse) == np.sign(lse_ref))
+    dl = np.where(both, 0.0, np.abs(lse - lse_ref))
+    return {"max_abs": float(d.max(initial=0.0)), "mean_abs": float(d.mean()) if d.size else 0.0,
+            "lse_max": float(dl.max(initial=0.0)), "n": int(d.size)}
+
+
+def assert_within(stats, dtype, what=""):
+    mx, mean = O_TOL[dtype]
+    assert np.isfinite(stats["lse_max"]), f"{what}: LSE mismatch in infinities {stats}"
+    assert stats["max_abs"] <= mx, f"{what}: max abs {stats}"
+    assert stats["mean_abs"] <= mean, f"{what}: mean abs {stats}"
+    assert stats["lse_max"] <= LSE_TOL, f"{what}: LSE {stats}"
+
+
+def run_gpu(q, k, v, bias, scale, causal):
+    o, lse = binding.forward(q, k, v, bias, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def full_check(q, k, v, bias, scale, causal, dtype, what=""):
+    """Whole-tensor comparison with the oracle (small problems)."""
+    o, lse = run_gpu(q, k, v, bias, scale, causal)
+    o_ref, lse_ref = attention_forward(f64(q), f64(k), f64(v),
+                                       None if bias is None else f64(bias),
+                                       scale=scale, causal=causal)
+    st = errors(f64(o), lse.cpu().numpy(), o_ref, lse_ref)
+    assert_within(st, dtype, what)
+    return st, o, lse
+
+
+def sampled_check(q, k, v, bias, scale, causal, dtype, heads, rows, o, lse, what=""):
+    """Compare selected (b, hq, rows) of a full-size GPU result with the oracle,
+    which evaluates exactly those rows (each row depends only on its own query,
+    its bias row and the whole K/V of its KV head)."""
+    B, Hq, Nq, D = q.shape
+    grp = Hq // k.shape[1]
+    rows_t = torch.as_tensor(rows, device=q.device)
+    worst = {"max_abs": 0.0, "mean_abs": 0.0, "lse_max": 0.0, "n": 0}
+    sum_abs = 0.0
+    for b, h in heads:
+        hk = h // grp
+        o_ref, l_ref = attention_head_rows(
+            f64(q[b, h].index_select(0, rows_t)), f64(k[b, hk]), f64(v[b, hk]), rows=rows,
+            scale=scale, causal=causal,
+            bias_rows=None if bias is None else f64(bias[b, h].index_select(0, rows_t)))
+        st = errors(f64(o[b, h].index_select(0, rows_t)),
+                    lse[b, h].index_select(0, rows_t).cpu().numpy(), o_ref, l_ref)
+        worst["max_abs"] = max(worst["max_abs"], st["max_abs"])
+        worst["lse_max"] = max(worst["lse_max"], st["lse_max"])
+        sum_abs += st["mean_abs"] * st["n"]
+        worst["n"] += st["n"]
+    worst["mean_abs"] = sum_abs / max(worst["n"], 1)
+    assert_within(worst, dtype, what)
+    return worst

@@ -1,0 +1,124 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before anything is launched.
+
+Nothing here launches a kernel: fa_check_args is pure host code, and
+fa_forward returns its validation status before it reaches HIP.
+"""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from tiled_attention_forward_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# Fake, well-separated, 256-byte-aligned device addresses (never dereferenced).
+Q, K, V, BIAS, O, L = (0x100000000 * (i + 1) for i in range(6))
+OK_ARGS = dict(q=Q, k=K, v=V, bias=None, o=O, lse=L, B=2, Hq=4, Hkv=2, Nq=100, Nk=77, D=64,
+               scale=0.125, causal=1, dtype=binding.FA_DTYPE_BF16)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fa_\w+)\s*\(", text, re.M)))
+
+
+def check(**over):
+    a = dict(OK_ARGS, **over)
+    return binding.fa_check_args(a["q"], a["k"], a["v"], a["bias"], a["o"], a["lse"], a["B"],
+                                 a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"],
+                                 a["causal"], a["dtype"])
+
+
+def forward_status(**over):
+    a = dict(OK_ARGS, **over)
+    return binding.fa_forward(a["q"], a["k"], a["v"], a["bias"], a["o"], a["lse"], a["B"],
+                              a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"],
+                              a["causal"], a["dtype"], None)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = binding.load_library()
+    names = declared_functions()
+    assert set(names) == {"fa_check_args", "fa_forward", "fa_status_string", "fa_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(fa_\w+)$", out, re.M))
+    assert set(names) <= exported, set(names) - exported
+
+
+def test_version_and_status_strings():
+    assert binding.fa_version().startswith("fa ") and "gfx950" in binding.fa_version()
+    for code in range(0, 11):
+        s = binding.fa_status_string(code)
+        assert s and s != "unknown status", code
+    assert binding.fa_status_string(99) == "unknown status"
+
+
+def test_valid_arguments_pass():
+    assert check() == 0
+    assert check(bias=BIAS) == 0
+    assert check(D=128, dtype=binding.FA_DTYPE_FP32, causal=0) == 0
+    assert check(dtype=binding.FA_DTYPE_FP16, Hq=20, Hkv=4) == 0
+    assert check(scale=0.0) == 0 and check(scale=-1.0) == 0
+    assert check(Nk=0) == 0   # rows with no key: O = 0, LSE = -inf
+    assert check(Nk=0, k=None, v=None) == 0   # K and V are not read when Nk = 0
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
+def test_null_pointer(field):
+    assert check(**{field: None}) == 1
+    assert forward_status(**{field: None}) == 1
+
+
+def test_empty_problem_needs_no_pointers_and_launches_nothing():
+    for over in (dict(B=0), dict(Hq=0, Hkv=0), dict(Nq=0)):
+        assert check(q=None, k=None, v=None, o=None, lse=None, **over) == 0
+        assert forward_status(q=None, k=None, v=None, o=None, lse=None, **over) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), 2), (dict(Nq=-5), 2), (dict(Nk=-1), 2), (dict(Hkv=0), 2),
+    (dict(Hq=5, Hkv=2), 3), (dict(Hq=4, Hkv=3), 3),
+    (dict(D=80), 4), (dict(D=96), 4), (dict(D=32), 4), (dict(D=256), 4), (dict(D=0), 4),
+    (dict(dtype=3), 5), (dict(dtype=-1), 5),
+    (dict(scale=math.nan), 6), (dict(scale=math.inf), 6), (dict(scale=-math.inf), 6),
+    (dict(q=Q + 8), 7), (dict(k=K + 4), 7), (dict(v=V + 2), 7), (dict(o=O + 8), 7),
+    (dict(bias=BIAS + 8), 7), (dict(lse=L + 2), 7),
+    (dict(o=Q), 8), (dict(o=K + 64), 8), (dict(lse=V), 8), (dict(lse=O + 256), 8),
+    (dict(bias=BIAS, o=BIAS + 1024), 8), (dict(lse=Q + 1024), 8),
+    (dict(Nq=1 << 30), 9), (dict(Nk=1 << 30), 9), (dict(B=1 << 22, Hq=1 << 10, Hkv=1), 9),
+])
+def test_rejections(over, code):
+    assert check(**over) == code
+    assert forward_status(**over) == code  # returned before any launch
+
+
+def test_head_dim_pitfall_is_an_error_not_a_truncation():
+    """A 96-wide head with a 64-wide kernel block silently drops columns in the
+    kernel of the xnwp.cn post (§5.1, §6.4); here every unsupported D is refused."""
+    for d in (1, 16, 63, 65, 80, 96, 127, 129, 192):
+        assert check(D=d) == 4
+
+
+def test_forward_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.forward(q, q, q)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setenv("FA_LIBRARY", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load_library()
+    monkeypatch.setattr(binding, "_lib", None)

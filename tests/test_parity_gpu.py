@@ -1,0 +1,144 @@
+"""GPU parity: fa_forward (through the C ABI) against the fp64 oracle.
+
+Small problems are compared element by element over the whole output; the
+full-size workloads run in exactly the configuration bench.py times and are
+compared on sampled rows (the oracle evaluates those rows one by one) plus
+properties that hold at any size.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from tests.parity import (assert_within, errors, f64, full_check, run_gpu, sampled_check)
+from tiled_attention_forward_amd import binding
+from tiled_attention_forward_amd.workloads import WORKLOADS, custom, make_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["b1_h1_s256_d64_fp32", "b2_h16_s512_d64_fp16", "b2_h16_s512_d64_fp16_causal"]
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+@pytest.mark.parametrize("name", SMALL)
+def test_small_workloads_full(gpu_device, name, seed):
+    w = WORKLOADS[name]
+    _log(f"case {name} seed {seed}")
+    q, k, v, bias = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed))
+    st, _, _ = full_check(q, k, v, bias, w.scale, w.causal, w.dtype, f"{name}/{seed}")
+    _log(st)
+
+
+EDGE = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, causal, bias
+    (1, 1, 1, 1, 1, 64, "bf16", False, False),
+    (1, 1, 1, 1, 1, 128, "bf16", True, True),
+    (1, 2, 2, 1000, 1000, 64, "fp16", True, False),
+    (1, 2, 2, 1000, 1000, 128, "bf16", False, True),
+    (1, 2, 1, 333, 517, 64, "bf16", False, True),
+    (1, 2, 1, 517, 333, 128, "fp16", True, False),
+    (2, 10, 2, 200, 300, 64, "bf16", True, True),
+    (1, 4, 2, 130, 70, 128, "fp32", True, True),
+    (1, 3, 3, 64, 64, 64, "fp32", False, False),
+    (1, 1, 1, 127, 129, 64, "bf16", True, False),
+    (2, 4, 4, 128, 128, 64, "bf16", True, False),
+    (1, 8, 1, 256, 256, 128, "bf16", False, False),
+    (1, 2, 2, 1, 700, 64, "bf16", False, False),
+    (1, 2, 2, 700, 1, 64, "bf16", True, False),
+    (1, 2, 2, 70, 70, 64, "fp32", True, False),
+    (1, 2, 1, 129, 131, 128, "fp16", False, True),
+    (3, 2, 2, 65, 63, 64, "fp16", True, True),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: "-".join(map(str, c)))
+def test_edge_shapes(gpu_device, case):
+    B, Hq, Hkv, Nq, Nk, D, dt, causal, bias = case
+    w = custom(B, Hq, Hkv, Nq, Nk, D, dt, causal, bias)
+    _log(f"case {case}")
+    q, k, v, b = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=7))
+    st, _, _ = full_check(q, k, v, b, w.scale, causal, dt, str(case))
+    _log(st)
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 1.0, 1e-3, -2.0])
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_scale_values(gpu_device, scale, dt):
+    """Any finite scale: negative (Q sign flip), zero (uniform softmax), large."""
+    w = custom(1, 2, 1, 150, 150, 64, dt, True, False)
+    _log(f"scale {scale} {dt}")
+    q, k, v, _ = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=3))
+    full_check(q, k, v, None, scale, True, dt, f"scale={scale}")
+    w2 = custom(1, 2, 2, 90, 77, 128, dt, False, True)
+    q, k, v, b = (t.to(gpu_device) for t in make_inputs(w2, seed=4))
+    full_check(q, k, v, b, scale, False, dt, f"bias scale={scale}")
+
+
+def test_no_keys(gpu_device):
+    """Nk = 0: every row sees no key, O = 0 and LSE = -inf."""
+    q = torch.randn(1, 2, 40, 64, device=gpu_device).to(torch.bfloat16)
+    k = torch.empty(1, 2, 0, 64, device=gpu_device, dtype=torch.bfloat16)
+    for causal in (False, True):
+        o, lse = run_gpu(q, k, k, None, 0.125, causal)
+        assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_empty_batch(gpu_device):
+    q = torch.empty(0, 2, 16, 64, device=gpu_device, dtype=torch.bfloat16)
+    o, lse = run_gpu(q, q, q, None, 0.125, True)
+    assert o.shape == q.shape and lse.shape == (0, 2, 16)
+
+
+def test_bias_minus_inf_row(gpu_device):
+    """A row whose bias is -inf everywhere has no finite logit: O = 0, LSE = -inf."""
+    w = custom(1, 1, 1, 70, 66, 64, "bf16", False, True)
+    q, k, v, b = (t.to(gpu_device) for t in make_inputs(w, seed=5))
+    b[0, 0, 3, :] = float("-inf")
+    st, o, lse = full_check(q, k, v, b, w.scale, False, "bf16", "-inf bias row")
+    assert torch.all(o[0, 0, 3] == 0) and torch.isneginf(lse[0, 0, 3])
+
+
+def test_deterministic_and_stream(gpu_device):
+    """Same inputs, same bits; a side stream gives the same result."""
+    w = custom(2, 4, 2, 300, 300, 64, "bf16", True, True)
+    q, k, v, b = (t.to(gpu_device) for t in make_inputs(w, seed=9))
+    o1, l1 = run_gpu(q, k, v, b, w.scale, True)
+    o2, l2 = run_gpu(q, k, v, b, w.scale, True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o3, l3 = binding.forward(q, k, v, b, causal=True, scale=w.scale)
+    s.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+FULL = ["b2_h16_s512_d64_fp16", "b2_h16_s512_d64_fp16_causal", "b2_h16_s4096_d64_bf16_causal",
+        "b8_h32_s2048_d128_bf16", "b1_hq20_hkv4_s8192_d128_bf16_causal_bias"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(gpu_device, name):
+    """Full-size run as bench.py times it; oracle on sampled rows of several heads."""
+    w = WORKLOADS[name]
+    _log(f"full-size {name}")
+    q, k, v, bias = make_inputs(w, seed=0, device=gpu_device)
+    o, lse = run_gpu(q, k, v, bias, w.scale, w.causal)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    heads = sorted({(0, 0), (w.B - 1, w.Hq - 1), (0, w.Hq // 2), (w.B // 2, 1 % w.Hq)})
+    rows = sample_rows(w.Nq, 40, seed=1)
+    st = sampled_check(q, k, v, bias, w.scale, w.causal, w.dtype, heads, rows, o, lse, name)
+    _log(st)
+    if w.causal:
+        # row 0 sees only key 0: O_0 = V_0 exactly in every head
+        grp = w.Hq // w.Hkv
+        v0 = v[:, :, 0, :].repeat_interleave(grp, dim=1)
+        assert torch.equal(o[:, :, 0, :], v0)
+    del q, k, v, bias, o, lse
+    torch.cuda.empty_cache()

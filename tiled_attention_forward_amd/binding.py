@@ -1,0 +1,129 @@
+"""ctypes binding of libfa.so (argument marshalling only).
+
+``fa_forward``, ``fa_check_args``, ``fa_status_string`` and ``fa_version`` take
+the same arguments as the C functions of ``include/fa.h`` (device pointers as
+Python ints).  ``forward`` is the tensor-level convenience: it checks the torch
+tensors, allocates O and LSE with torch, and calls ``fa_forward`` on the
+current stream.  Every step of the attention runs in the library's kernels; if
+the library is missing or does not load, the call raises instead of computing
+anything some other way.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+FA_DTYPE_BF16, FA_DTYPE_FP16, FA_DTYPE_FP32 = 0, 1, 2
+FA_OK = 0
+STATUS_NAMES = {
+    0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_BAD_SIZE", 3: "FA_ERR_HEAD_GROUPS",
+    4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_DTYPE", 6: "FA_ERR_SCALE", 7: "FA_ERR_ALIGNMENT",
+    8: "FA_ERR_OVERLAP", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP",
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("FA_LIBRARY", os.path.join(PKG, "libfa.so"))
+
+
+def load_library():
+    """Load libfa.so once; raise FaError-like RuntimeError if it is absent or broken."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m tiled_attention_forward_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    lib.fa_check_args.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32, i32, i32]
+    lib.fa_check_args.restype = i32
+    lib.fa_forward.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32, i32, i32, p]
+    lib.fa_forward.restype = i32
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype) -> int:
+    return load_library().fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D,
+                                        float(scale), int(causal), int(dtype))
+
+
+def fa_forward(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype,
+               stream) -> int:
+    return load_library().fa_forward(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D,
+                                     float(scale), int(causal), int(dtype), stream)
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_version() -> str:
+    return load_library().fa_version().decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_FP16,
+             torch.float32: FA_DTYPE_FP32}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def forward(q, k, v, bias=None, *, causal=False, scale=None, out=None, lse=None, stream=None):
+    """O, LSE = attention(q, k, v [, bias]) on the GPU through fa_forward.
+
+    q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D], bias [B,Hq,Nq,Nk] or None: contiguous
+    CUDA tensors of one dtype (bf16, fp16 or fp32).  ``scale=None`` means
+    1/sqrt(D).  ``out``/``lse`` may be preallocated ([B,Hq,Nq,D] dtype and
+    [B,Hq,Nq] float32).  Runs on ``stream`` (a torch.cuda.Stream) or the
+    current stream.
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)) + ((("bias", bias),) if bias is not None else ()):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("k and v must be [B, Hkv, Nk, D] matching q")
+    if bias is not None and tuple(bias.shape) != (B, Hq, Nq, Nk):
+        raise ValueError("bias must be [B, Hq, Nq, Nk]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                        bias.data_ptr() if bias is not None else None,
+                        out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, D, float(scale),
+                        int(bool(causal)), _dtype_code(q), stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+    return out, lse

@@ -1,0 +1,72 @@
+"""Build libfa.so in-tree with hipcc for gfx950.
+
+    python -m tiled_attention_forward_amd.build
+
+compiles ``csrc/fa_api.cpp`` and ``csrc/fa_fwd.hip`` into
+``tiled_attention_forward_amd/libfa.so``.  Packed-fp32 code generation is
+switched off for all device code.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libfa.so")
+ARCH = "gfx950"
+
+SOURCES = ["fa_api.cpp", "fa_fwd.hip"]
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    f"-I{os.path.join(ROOT, 'include')}",
+]
+DEVICE = [
+    f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libfa.so)")
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every source and link libfa.so; returns its path.  Always rebuilds."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
+        objs = []
+        for src in SOURCES:
+            path = os.path.join(CSRC, src)
+            obj = os.path.join(tmp, src + ".o")
+            lang = ["-x", "hip"] if src.endswith(".hip") else []
+            cmd = [cc, *COMMON, *DEVICE, *extra_flags, *lang, "-c", path, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
+            objs.append(obj)
+        tmp_lib = LIB + ".tmp"
+        cmd = [cc, *DEVICE, "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    try:
+        print(build(verbose="-v" in sys.argv))
+    except subprocess.CalledProcessError as e:
+        err = e.stderr.decode() if isinstance(e.stderr, bytes) else ""
+        sys.stderr.write(err)
+        sys.exit(1)
