@@ -146,16 +146,28 @@ __device__ __forceinline__ int vt_pos_of_group(int kg) {  // kg = key / 4
   return (kg >> 2) * 16 + sigma * 4;
 }
 
+// {own value, value of lane l^32} in some order, via v_permlane32_swap.  The
+// two results are copied out of the returned vector as values before being
+// reinterpreted: applying __builtin_bit_cast to the element lvalue r[1] reads
+// the vector's first element instead (seen with this ROCm clang).
+__device__ __forceinline__ void own_and_partner(float x, float& a, float& b) {
+  const u32 xi = __builtin_bit_cast(u32, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  const u32 r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+
 __device__ __forceinline__ float partner_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(u32, x),
-                                                  __builtin_bit_cast(u32, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  float a, b;
+  own_and_partner(x, a, b);
+  return fmaxf(a, b);
 }
 
 __device__ __forceinline__ float partner_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(u32, x),
-                                                  __builtin_bit_cast(u32, x), false, false);
-  return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+  float a, b;
+  own_and_partner(x, a, b);
+  return a + b;
 }
 
 template <typename T, int D, bool CAUSAL, bool BIAS>
