@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time for the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before timing, run one plain device copy of MIB MiB (a reference "
+                         "dispatch for scaling HBM byte counters); untimed")
     return ap.parse_args()
 
 
@@ -138,6 +141,15 @@ def main():
                  bias.data_ptr() if bias is not None else None, o.data_ptr(), lse.data_ptr(),
                  w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal), dtype_code,
                  stream.cuda_stream)
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         st = lib.fa_forward(*call_args)

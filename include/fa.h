@@ -66,8 +66,10 @@ typedef enum fa_status {
   FA_ERR_SCALE = 6,        /* scale is NaN or infinite                                   */
   FA_ERR_ALIGNMENT = 7,    /* a tensor pointer is not aligned as required above          */
   FA_ERR_OVERLAP = 8,      /* o or lse overlaps another buffer                           */
-  FA_ERR_TOO_LARGE = 9,    /* a size exceeds the kernel's index range: B, Hq, Nq and Nk  */
-                           /* must be < 2^30 and B*Hq*ceil(Nq/128) < 2^31                */
+  FA_ERR_TOO_LARGE = 9,    /* a size exceeds the kernel's index range: B, Hq, Nq, Nk     */
+                           /* < 2^30; B*Hq*ceil(Nq/128) < 2^31; one head's Q and one     */
+                           /* head's K (Nq*D or Nk*D elements) < 2^31 bytes; with a bias, */
+                           /* 128*Nk elements < 2^31 bytes                               */
   FA_ERR_HIP = 10          /* the HIP runtime rejected the launch                        */
 } fa_status;
 

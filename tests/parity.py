@@ -82,3 +82,21 @@ def sampled_check(q, k, v, bias, scale, causal, dtype, heads, rows, o, lse, what
     worst["mean_abs"] = sum_abs / max(worst["n"], 1)
     assert_within(worst, dtype, what)
     return worst
+
+
+def rounding_bound_check(q, k, v, bias, scale, causal, dtype, o, lse, what=""):
+    """For logit spreads wider than the pages' workloads, check the bound the
+    arithmetic gives instead of the fixed bar.  With u the unit roundoff of the
+    input type (2^-8 bf16, 2^-11 fp16), each probability is rounded before P.V
+    (relative error <= u per term) and O is rounded once (<= u relative), so
+    elementwise |dO| <= u * (P.|V|) + u * |O| + 1e-4, the last term covering fp32
+    accumulation and the exp2 approximation.  LSE keeps its 1e-3 bar."""
+    u = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}[dtype]
+    bq, bk, bv = f64(q), f64(k), f64(v)
+    bb = None if bias is None else f64(bias)
+    o_ref, l_ref = attention_forward(bq, bk, bv, bb, scale=scale, causal=causal)
+    o_abs, _ = attention_forward(bq, bk, np.abs(bv), bb, scale=scale, causal=causal)
+    bound = u * o_abs + u * np.abs(o_ref) + 1e-4
+    err = np.abs(f64(o) - o_ref)
+    assert np.all(err <= bound), f"{what}: worst err/bound {float((err / bound).max())}"
+    assert np.abs(lse.cpu().numpy() - l_ref).max() <= LSE_TOL, f"{what}: LSE"

@@ -52,7 +52,13 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             cmd = [cc, *COMMON, *DEVICE, *extra_flags, *lang, "-c", path, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
-            subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
+            res = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
+            if res.returncode != 0:
+                errs = "\n".join(l for l in res.stderr.splitlines()
+                                 if "packed-fp32-ops' is not a recognized" not in l)
+                raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
+            if verbose and res.stderr:
+                print(res.stderr, flush=True)
             objs.append(obj)
         tmp_lib = LIB + ".tmp"
         cmd = [cc, *DEVICE, "-shared", "-fPIC", *objs, "-o", tmp_lib]
@@ -66,7 +72,6 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 if __name__ == "__main__":
     try:
         print(build(verbose="-v" in sys.argv))
-    except subprocess.CalledProcessError as e:
-        err = e.stderr.decode() if isinstance(e.stderr, bytes) else ""
-        sys.stderr.write(err)
+    except (RuntimeError, subprocess.CalledProcessError) as e:
+        sys.stderr.write(f"{e}\n")
         sys.exit(1)

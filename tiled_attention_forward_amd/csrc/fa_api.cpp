@@ -51,6 +51,11 @@ extern "C" int fa_check_args(const void* q, const void* k, const void* v, const 
   if (Nq >= lim || Nk >= lim || B >= lim || Hq >= lim) return FA_ERR_TOO_LARGE;
   const int64_t tiles = (Nq + fa::kRowsPerBlock - 1) / fa::kRowsPerBlock;
   if (B * Hq > (int64_t(1) << 31) / tiles) return FA_ERR_TOO_LARGE;
+  // Byte offsets inside one head's Q/K/V, and inside one block of bias rows,
+  // are 32-bit in the kernel's buffer loads.
+  const int64_t lim31 = int64_t(1) << 31;
+  if (Nq * D * esz >= lim31 || Nk * D * esz >= lim31) return FA_ERR_TOO_LARGE;
+  if (bias != nullptr && int64_t(fa::kRowsPerBlock) * Nk * esz >= lim31) return FA_ERR_TOO_LARGE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       (bias != nullptr && !aligned(bias, 16)) || !aligned(lse, 4))
     return FA_ERR_ALIGNMENT;

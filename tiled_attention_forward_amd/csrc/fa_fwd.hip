@@ -60,11 +60,26 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;              // waves per workgroup
-constexpr int kQW = 32;                // query rows per wave
-constexpr int kBM = kWaves * kQW;      // query rows per workgroup
-constexpr int kBN = 64;                // keys per K/V tile
 constexpr int kThreads = kWaves * 64;
-static_assert(kBM == kRowsPerBlock, "grid-size validation assumes this block height");
+#ifndef FA_BN64
+#define FA_BN64 64
+#endif
+#ifndef FA_BN128
+#define FA_BN128 64
+#endif
+#ifndef FA_QB64
+#define FA_QB64 1
+#endif
+#ifndef FA_QB128
+#define FA_QB128 1
+#endif
+constexpr int kBN64 = FA_BN64;         // keys per K/V tile, D = 64
+constexpr int kBN128 = FA_BN128;       // keys per K/V tile, D = 128
+constexpr int kQB64 = FA_QB64;         // 32-row query blocks per wave, D = 64
+constexpr int kQB128 = FA_QB128;       // 32-row query blocks per wave, D = 128
+constexpr float kTau = 8.f;            // lazy-rescale threshold (log2 units)
+static_assert(kWaves * 32 >= kRowsPerBlock,
+              "grid-size validation assumes at least this block height");
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -131,7 +146,7 @@ struct Params {
   int Hq, Hkv, Nq, Nk;
   int BH;        // B * Hq
   int group;     // Hq / Hkv
-  int n_qtiles;  // ceil(Nq / kBM)
+  int n_qtiles;  // ceil(Nq / rows per workgroup)
   float c;       // |scale| * log2(e), never 0 (see the launcher)
   u32 q_sign;    // sign bits XORed into Q when scale < 0
   int bias_vec;  // bias rows allow 4-element vector loads
@@ -170,7 +185,14 @@ __device__ __forceinline__ float partner_sum(float x) {
   return a + b;
 }
 
-template <typename T, int D, bool CAUSAL, bool BIAS>
+// Raw buffer resource over [base, base + bytes): loads past the end return 0
+// (the hardware range check), so tails need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
+                                           0x00020000);
+}
+
+template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
@@ -181,15 +203,17 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   constexpr int ESZ = sizeof(T);
   constexpr int VEC = 16 / ESZ;      // elements per 16-byte vector
   constexpr int KSTR = D + VEC;      // K tile row stride, elements
-  constexpr int VSTR = kBN + VEC;    // V^T tile row stride, elements
-  constexpr int KT = kBN * KSTR;     // elements per K buffer
+  constexpr int VSTR = BN + VEC;     // V^T tile row stride, elements
+  constexpr int KT = BN * KSTR;      // elements per K buffer
   constexpr int VT = D * VSTR;       // elements per V^T buffer
-  constexpr int NKB = kBN / 32;      // 32-key blocks per tile
+  constexpr int NKB = BN / 32;       // 32-key blocks per tile
   constexpr int NDB = D / 32;        // 32-wide column blocks of the output
-  constexpr int KCH = kBN * D / VEC / kThreads;           // K vectors per thread
-  constexpr int VTASKS = (kBN / 4) * (D / VEC);           // 4-key x VEC-column tasks
+  constexpr int QW = 32 * QB;        // query rows per wave
+  constexpr int BM = kWaves * QW;    // query rows per workgroup
+  constexpr int KCH = BN * D / VEC / kThreads;            // K vectors per thread
+  constexpr int VTASKS = (BN / 4) * (D / VEC);            // 4-key x VEC-column tasks
   constexpr int VTPT = (VTASKS + kThreads - 1) / kThreads;
-  static_assert(KCH * kThreads * VEC == kBN * D, "K tile must split evenly");
+  static_assert(KCH * kThreads * VEC == BN * D, "K tile must split evenly");
 
   __shared__ __attribute__((aligned(16))) T smem[2 * (KT + VT)];
 
@@ -197,116 +221,136 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, ln = lane & 31;
 
+  // Workgroup -> (head, query block).  Consecutive ids walk the heads, so
+  // with B*Hq a multiple of 8 all blocks of a head share one XCD (ids are
+  // dealt round-robin to the 8 XCDs).  Causal: the first half of the ranks
+  // take the heavy blocks in descending order and the second half the light
+  // ones in ascending order, so the two workgroups a CU receives from the
+  // two halves add up to about the same number of key tiles.
   const int bh = int(blockIdx.x % unsigned(p.BH));
   const int rank = int(blockIdx.x / unsigned(p.BH));
-  const int tile = CAUSAL ? (p.n_qtiles - 1 - rank) : rank;
+  int tile = rank;
+  if (CAUSAL) {
+    const int half = (p.n_qtiles + 1) / 2;
+    tile = rank < half ? p.n_qtiles - 1 - rank : rank - half;
+  }
   const int b = bh / p.Hq, hq = bh - b * p.Hq, hk = hq / p.group;
-
   const int64_t kv_head = int64_t(b) * p.Hkv + hk;
-  const T* __restrict__ Qh = static_cast<const T*>(p.q) + int64_t(bh) * p.Nq * D;
-  const T* __restrict__ Kh = static_cast<const T*>(p.k) + kv_head * p.Nk * D;
-  const T* __restrict__ Vh = static_cast<const T*>(p.v) + kv_head * p.Nk * D;
-  T* __restrict__ Oh = static_cast<T*>(p.o) + int64_t(bh) * p.Nq * D;
-  float* __restrict__ Lh = p.lse + int64_t(bh) * p.Nq;
 
-  const int q_blk = tile * kBM;
-  const int wq0 = q_blk + wave * kQW;     // first row of this wave
-  const int qi = wq0 + ln;                // the row this lane owns
-  const bool row_ok = qi < p.Nq;
+  const T* Qh = static_cast<const T*>(p.q) + int64_t(bh) * p.Nq * D;
+  const T* Kh = static_cast<const T*>(p.k) + kv_head * p.Nk * D;
+  const T* Vh = static_cast<const T*>(p.v) + kv_head * p.Nk * D;
+  T* Oh = static_cast<T*>(p.o) + int64_t(bh) * p.Nq * D;
+  float* Lh = p.lse + int64_t(bh) * p.Nq;
+  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(Qh, uint32_t(p.Nq) * D * ESZ);
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh, uint32_t(p.Nk) * D * ESZ);
+  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh, uint32_t(p.Nk) * D * ESZ);
+  const float c = p.c;
+
+  const int q_blk = tile * BM;
+  const int wq0 = q_blk + wave * QW;      // first row of this wave
   const bool wave_has_rows = wq0 < p.Nq;
-  const int wq_last = min(wq0 + kQW, p.Nq) - 1;
-  const int blk_last = min(q_blk + kBM, p.Nq) - 1;
-
-  int n_kv = (p.Nk + kBN - 1) / kBN;
-  if (CAUSAL) n_kv = min(n_kv, blk_last / kBN + 1);
-
-  // ---- Q fragments: B operand of S^T = K Q^T, loaded once --------------------
-  Frag qf[NS];
+  const int wq_last = min(wq0 + QW, p.Nq) - 1;
+  const int blk_last = min(q_blk + BM, p.Nq) - 1;
+  int qi[QB];                             // the row this lane owns in block qb
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int64_t off = int64_t(qi) * D + s * KS + g * KP;
-    if constexpr (F32) {
-      const u32 raw = row_ok ? __builtin_bit_cast(u32, Qh[off]) : 0u;
-      qf[s] = __builtin_bit_cast(float, raw ^ p.q_sign);
-    } else {
-      u32x4 raw = row_ok ? *reinterpret_cast<const u32x4*>(Qh + off) : u32x4{0, 0, 0, 0};
-      raw ^= p.q_sign;
-      qf[s] = __builtin_bit_cast(Frag, raw);
+  for (int qb = 0; qb < QB; ++qb) qi[qb] = wq0 + 32 * qb + ln;
+
+  int n_kv = (p.Nk + BN - 1) / BN;
+  if (CAUSAL) n_kv = min(n_kv, blk_last / BN + 1);
+
+  // ---- Q fragments: B operand of S^T = K Q^T, loaded once ---------------------
+  Frag qf[QB][NS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int off = (qi[qb] * D + s * KS + g * KP) * ESZ;  // rows past Nq read 0
+      if constexpr (F32) {
+        const u32 raw = __builtin_amdgcn_raw_buffer_load_b32(q_rs, off, 0, 0);
+        qf[qb][s] = __builtin_bit_cast(float, raw ^ p.q_sign);
+      } else {
+        u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(q_rs, off, 0, 0);
+        raw ^= p.q_sign;
+        qf[qb][s] = __builtin_bit_cast(Frag, raw);
+      }
     }
-  }
 
-  // ---- bias row pointer and per-tile register block -------------------------
-  const T* __restrict__ brow = nullptr;
-  if constexpr (BIAS) {
-    brow = static_cast<const T*>(p.bias) + (int64_t(bh) * p.Nq + (row_ok ? qi : 0)) * p.Nk;
-  }
-  // bias values for this lane's 4-key runs: [kb][q4] -> 4 elements
-  using BiasVec = typename std::conditional<F32, f32x4, u32x2>::type;
-  BiasVec bcur[NKB][4], bnext[NKB][4];
-
-  auto load_bias = [&](BiasVec (&dst)[NKB][4], int j) {
+  // ---- bias: rows of this query block, read once, non-temporal -----------------
+  using BiasVec = typename std::conditional<F32, u32x4, u32x2>::type;
+  BiasVec bcur[QB][NKB][4], bnext[QB][NKB][4];
+  // (without a bias the resource is built over an empty range and never read)
+  const T* bblk = BIAS ? static_cast<const T*>(p.bias) + (int64_t(bh) * p.Nq + q_blk) * p.Nk
+                       : static_cast<const T*>(p.q);
+  const __amdgpu_buffer_rsrc_t b_rs =
+      make_rsrc(bblk, BIAS ? uint32_t(blk_last - q_blk + 1) * uint32_t(p.Nk) * ESZ : 0u);
+  auto load_bias = [&](BiasVec (&dst)[QB][NKB][4], int j) {
     if constexpr (BIAS) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int key = j * kBN + kb * 32 + 8 * q4 + 4 * g;
-          BiasVec val{};
-          if (row_ok) {
-            if (p.bias_vec && key + 3 < p.Nk) {
-              val = __builtin_nontemporal_load(reinterpret_cast<const BiasVec*>(brow + key));
-            } else {
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int key = j * BN + kb * 32 + 8 * q4 + 4 * g;
+            const int off = ((qi[qb] - q_blk) * p.Nk + key) * ESZ;
+            if (p.bias_vec) {
               if constexpr (F32) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = (key + e < p.Nk) ? brow[key + e] : 0.f;
+                dst[qb][kb][q4] = __builtin_amdgcn_raw_buffer_load_b128(b_rs, off, 0, 2);
               } else {
-                const u16* b16 = reinterpret_cast<const u16*>(brow);
+                dst[qb][kb][q4] = __builtin_amdgcn_raw_buffer_load_b64(b_rs, off, 0, 2);
+              }
+            } else {
+              // rows not 4-element aligned: element loads (values past the
+              // row end belong to masked keys; past the block they read 0)
+              if constexpr (F32) {
+                BiasVec v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  v[e] = __builtin_amdgcn_raw_buffer_load_b32(b_rs, off + 4 * e, 0, 2);
+                dst[qb][kb][q4] = v;
+              } else {
                 u32 w[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (key + e < p.Nk) ? u32(b16[key + e]) : 0u;
-                val = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+                for (int e = 0; e < 4; ++e)
+                  w[e] = __builtin_amdgcn_raw_buffer_load_b16(b_rs, off + 2 * e, 0, 2);
+                dst[qb][kb][q4] = BiasVec{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
               }
             }
           }
-          dst[kb][q4] = val;
-        }
-      }
     }
   };
-  auto bias_at = [&](const BiasVec (&src)[NKB][4], int kb, int r) -> float {
+  auto bias_at = [&](int qb, int kb, int r) -> float {
     if constexpr (F32) {
-      return src[kb][r >> 2][r & 3];
+      const u32 w = bcur[qb][kb][r >> 2][r & 3];
+      return __builtin_bit_cast(float, w);
     } else {
-      const u32 w = src[kb][r >> 2][(r & 3) >> 1];
+      const u32 w = bcur[qb][kb][r >> 2][(r & 3) >> 1];
       return E::widen((r & 1) ? (w >> 16) : (w & 0xffffu));
     }
   };
 
-  // ---- K/V staging through registers -----------------------------------------
+  // ---- K/V staging through registers -------------------------------------------
   u32x4 kreg[KCH];
   u32x4 vreg[VTPT][4];
 
   auto gload = [&](int j) {
-    const int key0 = j * kBN;
+    const int key0 = j * BN;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / (D / VEC), col = (c % (D / VEC)) * VEC;
-      const int key = key0 + row;
-      kreg[i] = (key < p.Nk) ? *reinterpret_cast<const u32x4*>(Kh + int64_t(key) * D + col)
-                             : u32x4{0, 0, 0, 0};
+      const int cidx = tid + i * kThreads;
+      const int row = cidx / (D / VEC), col = (cidx % (D / VEC)) * VEC;
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(k_rs, ((key0 + row) * D + col) * ESZ, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < VTPT; ++i) {
       const int t = tid + i * kThreads;
-      const int kg = t % (kBN / 4), dc = t / (kBN / 4);
+      const int kg = t % (BN / 4), dc = t / (BN / 4);
       if (VTASKS % kThreads == 0 || t < VTASKS) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = key0 + kg * 4 + r;
-          vreg[i][r] = (key < p.Nk)
-                           ? *reinterpret_cast<const u32x4*>(Vh + int64_t(key) * D + dc * VEC)
-                           : u32x4{0, 0, 0, 0};
+          vreg[i][r] = __builtin_amdgcn_raw_buffer_load_b128(
+              v_rs, ((key0 + kg * 4 + r) * D + dc * VEC) * ESZ, 0, 0);
         }
       }
     }
@@ -317,14 +361,14 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     T* sV = sK + KT;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c / (D / VEC), col = (c % (D / VEC)) * VEC;
+      const int cidx = tid + i * kThreads;
+      const int row = cidx / (D / VEC), col = (cidx % (D / VEC)) * VEC;
       *reinterpret_cast<u32x4*>(sK + row * KSTR + col) = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < VTPT; ++i) {
       const int t = tid + i * kThreads;
-      const int kg = t % (kBN / 4), dc = t / (kBN / 4);
+      const int kg = t % (BN / 4), dc = t / (BN / 4);
       if (VTASKS % kThreads == 0 || t < VTASKS) {
         T* dst = sV + (dc * VEC) * VSTR + vt_pos_of_group(kg);
         if constexpr (F32) {
@@ -352,24 +396,29 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     }
   };
 
-  // ---- online-softmax state ---------------------------------------------------
-  float m_run = -INFINITY;  // running row max, base-2 logit units (same in both lane halves)
-  float l_run = 0.f;        // this lane's share of the running row sum
-  f32x16 acc[NDB];
+  // ---- online-softmax state --------------------------------------------------
+  // m_ref: the reference max the exponents are taken against (base-2 logit
+  // units, same in both lane halves).  It is raised only when a tile's row
+  // max exceeds it by more than kTau, so p = 2^(t - m_ref) <= 2^kTau and the
+  // rescale of the accumulator is skipped for most tiles.  O = acc / l and
+  // LSE = m_ref + log2(l) do not depend on which reference is used.
+  float m_ref[QB], l_run[QB];
+  f32x16 acc[QB][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-
-  const float c = p.c;
+  for (int qb = 0; qb < QB; ++qb) {
+    m_ref[qb] = -INFINITY;
+    l_run[qb] = 0.f;  // this lane's share of the running row sum
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x16{};
+  }
 
   auto compute = [&](int j, int buf) {
     const T* sK = smem + buf * (KT + VT);
     const T* sV = sK + KT;
-    const int key0 = j * kBN;
+    const int key0 = j * BN;
 
-    // S^T = K_j Q^T  (rows: keys of the tile, columns: this wave's 32 query rows)
-    f32x16 s[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    // S^T = K_j Q^T  (rows: keys of the tile, columns: 32 query rows per block)
+    f32x16 s[QB][NKB];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
 #pragma unroll
@@ -381,59 +430,78 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
         } else {
           kf = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(src));
         }
-        s[kb] = E::mma(kf, qf[st], s[kb]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = E::mma(kf, qf[qb][st], st == 0 ? f32x16{} : s[qb][kb]);
       }
     }
 
     // Register r of block kb holds key key0 + kb*32 + 8*(r/4) + 4*g + r%4 of row qi.
-    if constexpr (BIAS) {
+    float m_tile[QB];
+    bool grow_any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[qb][kb][r] = fmaf(s[qb][kb][r], c, bias_at(qb, kb, r) * kLog2e);
+      }
+      const bool need_mask =
+          (key0 + BN > p.Nk) || (CAUSAL && key0 + BN - 1 > wq0 + 32 * qb);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool dead = key >= p.Nk || (CAUSAL && key > qi[qb]);
+            if (dead) s[qb][kb][r] = -INFINITY;
+          }
+      }
+      // row max over the tile: in-lane, then across the two lane halves
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[kb][r] = fmaf(s[kb][r], c, bias_at(bcur, kb, r) * kLog2e);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+      mx = partner_max(mx);
+      m_tile[qb] = BIAS ? mx : mx * c;  // c > 0, so max(s)*c = max(s*c)
+      grow_any = grow_any || (m_tile[qb] > m_ref[qb] + kTau);  // -inf + kTau stays -inf
     }
-    const bool need_mask = (key0 + kBN > p.Nk) || (CAUSAL && key0 + kBN - 1 > wq0);
-    if (need_mask) {
+    if (__builtin_amdgcn_ballot_w64(grow_any) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bool grow = m_tile[qb] > m_ref[qb] + kTau;
+        // rows that grow: alpha = 2^(m_ref - m_tile), which is 0 while m_ref = -inf
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref[qb] - m_tile[qb]) : 1.f;
+        m_ref[qb] = grow ? m_tile[qb] : m_ref[qb];
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+      }
+    }
+
+    // p = 2^(t - m_ref); row sums; P rounded to the input type for the P.V product
+    float rs[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float neg_m = (m_ref[qb] == -INFINITY) ? 0.f : -m_ref[qb];  // no exp(-inf + inf)
+      rs[qb] = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool dead = key >= p.Nk || (CAUSAL && key > qi);
-          if (dead) s[kb][r] = -INFINITY;
+          const float x = BIAS ? (s[qb][kb][r] + neg_m) : fmaf(s[qb][kb][r], c, neg_m);
+          const float e = __builtin_amdgcn_exp2f(x);
+          s[qb][kb][r] = e;
+          rs[qb] += e;
         }
+      l_run[qb] += rs[qb];
     }
-
-    // Row max over the tile: in-lane over 2*16 values, then across the lane halves.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = partner_max(mx);
-    const float m_tile = BIAS ? mx : mx * c;  // c > 0, so max(s)*c = max(s*c)
-    const float m_new = fmaxf(m_run, m_tile);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // no exp(-inf + inf)
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    const float neg_m = -m_use;
-
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = BIAS ? (s[kb][r] + neg_m) : fmaf(s[kb][r], c, neg_m);
-        const float e = __builtin_amdgcn_exp2f(x);
-        s[kb][r] = e;
-        rs += e;
-      }
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
 
     // O^T += V_j^T P^T
 #pragma unroll
@@ -445,28 +513,34 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
             const float vf = sV[(db * 32 + ln) * VSTR + pos];
-            acc[db] = E::mma(vf, s[kb][cc], acc[db]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) acc[qb][db] = E::mma(vf, s[qb][kb][cc], acc[qb][db]);
           }
         }
       } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          f32x8 pv;
+          Frag pf[QB];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) pv[i] = s[kb][8 * h + i];
-          const Frag pf = E::pack8(pv);
+          for (int qb = 0; qb < QB; ++qb) {
+            f32x8 pv;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pv[i] = s[qb][kb][8 * h + i];
+            pf[qb] = E::pack8(pv);
+          }
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
             const T* src = sV + (db * 32 + ln) * VSTR + kb * 32 + 16 * h + 8 * g;
             const Frag vf = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(src));
-            acc[db] = E::mma(vf, pf, acc[db]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) acc[qb][db] = E::mma(vf, pf[qb], acc[qb][db]);
           }
         }
       }
     }
   };
 
-  // ---- main loop: double-buffered K/V tiles -----------------------------------
+  // ---- main loop: double-buffered K/V tiles -------------------------------------
   if (n_kv > 0) {
     gload(0);
     if constexpr (BIAS) load_bias(bcur, 0);
@@ -477,64 +551,114 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     const int cur = j & 1;
     const bool has_next = j + 1 < n_kv;
     if (has_next) gload(j + 1);
-    const bool active = wave_has_rows && (!CAUSAL || j * kBN <= wq_last);
+    const bool active = wave_has_rows && (!CAUSAL || j * BN <= wq_last);
     if constexpr (BIAS) {
-      const bool next_active = has_next && wave_has_rows && (!CAUSAL || (j + 1) * kBN <= wq_last);
+      const bool next_active = has_next && wave_has_rows && (!CAUSAL || (j + 1) * BN <= wq_last);
       if (next_active) load_bias(bnext, j + 1);
     }
     if (active) compute(j, cur);
     if constexpr (BIAS) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) bcur[kb][q4] = bnext[kb][q4];
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) bcur[qb][kb][q4] = bnext[qb][kb][q4];
     }
     if (has_next) sstore(cur ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue: O = acc / l, LSE = m ln2 + ln l ---------------------------------
-  const float l_tot = partner_sum(l_run);
-  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  if (row_ok) {
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 -----------------------------
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const bool row_ok = qi[qb] < p.Nq;
+    const float l_tot = partner_sum(l_run[qb]);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    // Lane half g holds d = 8*q4 + 4*g + 0..3 of each 32-wide block.  One swap
+    // per word gives lane half 0 the 8 values d = 16*pr + 0..7 and lane half 1
+    // d = 16*pr + 8..15, so each lane writes whole 16-byte (bf16/fp16) or
+    // 32-byte (fp32) runs.
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = db * 32 + 8 * q4 + 4 * g;
-        f32x4 o4;
+      for (int pr = 0; pr < 2; ++pr) {
+        f32x4 a4, b4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = acc[db][4 * q4 + e] * inv;
-        T* dst = Oh + int64_t(qi) * D + d0;
+        for (int e = 0; e < 4; ++e) {
+          a4[e] = acc[qb][db][8 * pr + e] * inv;
+          b4[e] = acc[qb][db][8 * pr + 4 + e] * inv;
+        }
+        T* dst = Oh + int64_t(qi[qb]) * D + db * 32 + 16 * pr + 8 * g;
         if constexpr (F32) {
-          *reinterpret_cast<f32x4*>(dst) = o4;
+          const u32x4 aw = __builtin_bit_cast(u32x4, a4), bw = __builtin_bit_cast(u32x4, b4);
+          u32x4 ao, bo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const auto r = __builtin_amdgcn_permlane32_swap(u32(aw[e]), u32(bw[e]), false, false);
+            const u32 r0 = r[0], r1 = r[1];
+            ao[e] = r0;
+            bo[e] = r1;
+          }
+          if (row_ok) {
+            reinterpret_cast<u32x4*>(dst)[0] = ao;
+            reinterpret_cast<u32x4*>(dst)[1] = bo;
+          }
         } else {
-          *reinterpret_cast<u32x2*>(dst) = E::narrow4(o4);
+          const u32x2 aw = E::narrow4(a4), bw = E::narrow4(b4);
+          u32x4 out;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const auto r = __builtin_amdgcn_permlane32_swap(u32(aw[e]), u32(bw[e]), false, false);
+            const u32 r0 = r[0], r1 = r[1];
+            out[e] = r0;
+            out[2 + e] = r1;
+          }
+          if (row_ok) *reinterpret_cast<u32x4*>(dst) = out;
         }
       }
-    if (g == 0) Lh[qi] = (l_tot > 0.f) ? m_run * kLn2 + logf(l_tot) : -INFINITY;
+    if (row_ok && g == 0)
+      Lh[qi[qb]] = (l_tot > 0.f) ? m_ref[qb] * kLn2 + logf(l_tot) : -INFINITY;
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool BIAS>
+template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS>
 hipError_t launch_one(const Params& p, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&p)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_kernel<T, D, CAUSAL, BIAS>),
-                         dim3(grid), dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(
+      reinterpret_cast<const void*>(&fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS>), dim3(grid),
+      dim3(kThreads), args, 0, stream);
 }
 
-template <typename T, int D>
+template <typename T, int D, int BN, int QB>
 hipError_t launch_d(const Params& p, unsigned grid, hipStream_t s, bool causal, bool bias) {
   if (causal) {
-    return bias ? launch_one<T, D, true, true>(p, grid, s) : launch_one<T, D, true, false>(p, grid, s);
+    return bias ? launch_one<T, D, BN, QB, true, true>(p, grid, s)
+                : launch_one<T, D, BN, QB, true, false>(p, grid, s);
   }
-  return bias ? launch_one<T, D, false, true>(p, grid, s) : launch_one<T, D, false, false>(p, grid, s);
+  return bias ? launch_one<T, D, BN, QB, false, true>(p, grid, s)
+              : launch_one<T, D, BN, QB, false, false>(p, grid, s);
+}
+
+// 32-row query blocks per wave.  Two blocks (64 rows) halve the K/V operand
+// reads per MFMA, but only fit in registers for 16-bit inputs with D = 64 and
+// no bias tile; every other instance keeps one.
+constexpr int query_blocks(int dtype, int D, bool bias) {
+  return (dtype != FA_DTYPE_FP32 && D == 64 && !bias) ? kQB64 : (D == 64 ? 1 : kQB128);
 }
 
 template <typename T>
 hipError_t launch_t(const Params& p, unsigned grid, hipStream_t s, int D, bool causal, bool bias) {
-  return D == 64 ? launch_d<T, 64>(p, grid, s, causal, bias)
-                 : launch_d<T, 128>(p, grid, s, causal, bias);
+  if (D == 64) {
+    if constexpr (!std::is_same<T, float>::value) {
+      if (!bias) {
+        return causal ? launch_one<T, 64, kBN64, kQB64, true, false>(p, grid, s)
+                      : launch_one<T, 64, kBN64, kQB64, false, false>(p, grid, s);
+      }
+    }
+    return launch_d<T, 64, kBN64, 1>(p, grid, s, causal, bias);
+  }
+  return launch_d<T, 128, kBN128, kQB128>(p, grid, s, causal, bias);
 }
 
 }  // namespace
@@ -553,7 +677,8 @@ int launch_forward(const LaunchArgs& a) {
   p.Nk = a.Nk;
   p.BH = a.B * a.Hq;
   p.group = a.Hq / a.Hkv;
-  p.n_qtiles = (a.Nq + kBM - 1) / kBM;
+  const int bm = kWaves * 32 * query_blocks(a.dtype, a.D, a.bias != nullptr);
+  p.n_qtiles = (a.Nq + bm - 1) / bm;
   // The kernel folds the scale into base-2 exponents and needs a positive
   // factor: a negative scale is realised by flipping the sign of Q (exact), and
   // a zero (or vanishing) one by a factor so small that every finite logit
