@@ -73,6 +73,9 @@ constexpr int kThreads = kWaves * 64;
 #ifndef FA_QB128
 #define FA_QB128 1
 #endif
+#ifndef FA_MINB64
+#define FA_MINB64 2
+#endif
 constexpr int kBN64 = FA_BN64;         // keys per K/V tile, D = 64
 constexpr int kBN128 = FA_BN128;       // keys per K/V tile, D = 128
 constexpr int kQB64 = FA_QB64;         // 32-row query blocks per wave, D = 64
@@ -149,7 +152,7 @@ struct Params {
   int n_qtiles;  // ceil(Nq / rows per workgroup)
   float c;       // |scale| * log2(e), never 0 (see the launcher)
   u32 q_sign;    // sign bits XORed into Q when scale < 0
-  int bias_vec;  // bias rows allow 4-element vector loads
+  int bias_vec;  // bias rows allow 16-byte vector loads
 };
 
 // Key position inside a V^T tile row.  Within each group of 16 keys the 4-key
@@ -193,7 +196,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_kernel(Params p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
   constexpr bool F32 = std::is_same<T, float>::value;
@@ -227,12 +230,28 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
   // take the heavy blocks in descending order and the second half the light
   // ones in ascending order, so the two workgroups a CU receives from the
   // two halves add up to about the same number of key tiles.
-  const int bh = int(blockIdx.x % unsigned(p.BH));
-  const int rank = int(blockIdx.x / unsigned(p.BH));
-  int tile = rank;
+  // Workgroup id -> (head, query block).
+  //  * causal: ids are rank-major (id = rank * B*Hq + head) and the first
+  //    half of the ranks take the heavy query blocks in descending order,
+  //    the second half the light ones ascending, so co-resident workgroups
+  //    carry complementary amounts of work; with B*Hq a multiple of 8 all
+  //    blocks of a head also land on one XCD (ids are dealt round-robin to
+  //    the 8 XCDs), where they share the L2 copy of K and V;
+  //  * non-causal (all blocks equal): the ids one XCD receives are renumbered
+  //    to be consecutive in head-major order, so the query blocks of a head
+  //    run at the same time on one XCD and re-read K and V from its L2.
+  int bh, tile;
   if (CAUSAL) {
+    bh = int(blockIdx.x % unsigned(p.BH));
+    const int rank = int(blockIdx.x / unsigned(p.BH));
     const int half = (p.n_qtiles + 1) / 2;
     tile = rank < half ? p.n_qtiles - 1 - rank : rank - half;
+  } else {
+    const unsigned nblk = gridDim.x, full = nblk & ~7u;
+    unsigned logical = blockIdx.x;
+    if (logical < full) logical = (logical & 7u) * (full >> 3) + (logical >> 3);
+    bh = int(logical / unsigned(p.n_qtiles));
+    tile = int(logical % unsigned(p.n_qtiles));
   }
   const int b = bh / p.Hq, hq = bh - b * p.Hq, hk = hq / p.group;
   const int64_t kv_head = int64_t(b) * p.Hkv + hk;
@@ -276,7 +295,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
       }
     }
 
-  // ---- bias: rows of this query block, read once, non-temporal -----------------
+  // ---- bias: rows of this query block ----------------------------------------
+  // Read once overall, but each 128-byte line is touched by several of a
+  // wave's loads in a row, so the loads keep the default cache policy (a
+  // non-temporal hint lets lines go before the next touch).
   using BiasVec = typename std::conditional<F32, u32x4, u32x2>::type;
   BiasVec bcur[QB][NKB][4], bnext[QB][NKB][4];
   // (without a bias the resource is built over an empty range and never read)
@@ -286,38 +308,80 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
       make_rsrc(bblk, BIAS ? uint32_t(blk_last - q_blk + 1) * uint32_t(p.Nk) * ESZ : 0u);
   auto load_bias = [&](BiasVec (&dst)[QB][NKB][4], int j) {
     if constexpr (BIAS) {
+      if (p.bias_vec) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb) {
+            const int row_off = (qi[qb] - q_blk) * p.Nk + j * BN + kb * 32;
+            if constexpr (F32) {
+              // 4 keys per load: keys 8*q4 + 4*g + 0..3, the score layout itself
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int key = j * BN + kb * 32 + 8 * q4 + 4 * g;
-            const int off = ((qi[qb] - q_blk) * p.Nk + key) * ESZ;
-            if (p.bias_vec) {
-              if constexpr (F32) {
-                dst[qb][kb][q4] = __builtin_amdgcn_raw_buffer_load_b128(b_rs, off, 0, 2);
-              } else {
-                dst[qb][kb][q4] = __builtin_amdgcn_raw_buffer_load_b64(b_rs, off, 0, 2);
-              }
+              for (int q4 = 0; q4 < 4; ++q4)
+                dst[qb][kb][q4] = __builtin_amdgcn_raw_buffer_load_b128(
+                    b_rs, (row_off + 8 * q4 + 4 * g) * ESZ, 0, 0);
             } else {
-              // rows not 4-element aligned: element loads (values past the
-              // row end belong to masked keys; past the block they read 0)
+              // 8 keys per load: keys 16*h + 8*g + 0..7 land in slots 2h
+              // (first 4) and 2h+1 (last 4); swap_bias_halves puts them where
+              // the score registers expect them
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(
+                    b_rs, (row_off + 16 * h + 8 * g) * ESZ, 0, 0);
+                dst[qb][kb][2 * h] = u32x2{raw[0], raw[1]};
+                dst[qb][kb][2 * h + 1] = u32x2{raw[2], raw[3]};
+              }
+            }
+          }
+      } else {
+        // rows not aligned for vector loads: element loads (values past the
+        // row end belong to masked keys; past the block they read 0)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int off = ((qi[qb] - q_blk) * p.Nk + j * BN + kb * 32 + 8 * q4 + 4 * g) * ESZ;
               if constexpr (F32) {
                 BiasVec v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                  v[e] = __builtin_amdgcn_raw_buffer_load_b32(b_rs, off + 4 * e, 0, 2);
+                  v[e] = __builtin_amdgcn_raw_buffer_load_b32(b_rs, off + 4 * e, 0, 0);
                 dst[qb][kb][q4] = v;
               } else {
                 u32 w[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                  w[e] = __builtin_amdgcn_raw_buffer_load_b16(b_rs, off + 2 * e, 0, 2);
+                  w[e] = __builtin_amdgcn_raw_buffer_load_b16(b_rs, off + 2 * e, 0, 0);
                 dst[qb][kb][q4] = BiasVec{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
               }
             }
-          }
+      }
+    }
+  };
+  // After a 16-byte load, lane half 0 holds keys 16h+0..7 of its row and lane
+  // half 1 keys 16h+8..15; the score layout wants keys 16h+0..3 and 16h+8..11
+  // in half 0 and 16h+4..7 and 16h+12..15 in half 1.  One swap per word pair
+  // exchanges the middle quarters.
+  auto swap_bias_halves = [&]() {
+    if constexpr (BIAS && !F32) {
+      if (p.bias_vec) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int w = 0; w < 2; ++w) {
+                const u32 x = bcur[qb][kb][2 * h][w], y = bcur[qb][kb][2 * h + 1][w];
+                const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+                const u32 r0 = r[0], r1 = r[1];
+                bcur[qb][kb][2 * h][w] = r0;
+                bcur[qb][kb][2 * h + 1][w] = r1;
+              }
+      }
     }
   };
   auto bias_at = [&](int qb, int kb, int r) -> float {
@@ -439,6 +503,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(Params p) {
     // Register r of block kb holds key key0 + kb*32 + 8*(r/4) + 4*g + r%4 of row qi.
     float m_tile[QB];
     bool grow_any = false;
+    swap_bias_halves();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if constexpr (BIAS) {
@@ -688,7 +753,7 @@ int launch_forward(const LaunchArgs& a) {
   p.c = c;
   const bool neg = a.scale < 0.f;
   p.q_sign = !neg ? 0u : (a.dtype == FA_DTYPE_FP32 ? 0x80000000u : 0x80008000u);
-  p.bias_vec = (a.Nk % 4) == 0;
+  p.bias_vec = (a.dtype == FA_DTYPE_FP32) ? (a.Nk % 4) == 0 : (a.Nk % 8) == 0;
   const unsigned grid = unsigned(p.n_qtiles) * unsigned(p.BH);
   hipStream_t s = static_cast<hipStream_t>(a.stream);
   const bool bias = a.bias != nullptr;
