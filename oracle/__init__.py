@@ -8,6 +8,8 @@ It shares no code with the HIP path and imports nothing from it.
 from .attention import (  # noqa: F401
     attention_forward,
     attention_head_rows,
+    attention_partial,
+    merge_partials,
     merge_states,
     online_attention_forward,
     softmax_two_pass,

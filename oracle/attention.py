@@ -55,6 +55,8 @@ __all__ = [
     "attention_forward",
     "online_attention_forward",
     "merge_states",
+    "attention_partial",
+    "merge_partials",
 ]
 
 
@@ -214,3 +216,66 @@ def online_attention_forward(q, k, v, bias=None, *, scale=None, causal=False,
                 o[b, h, r0:r1] = np.where(ok[:, None], acc / np.where(ok, l_i, 1.0)[:, None], 0.0)
                 lse[b, h, r0:r1] = np.where(ok, m_i + np.log(np.where(ok, l_i, 1.0)), -np.inf)
     return o, lse
+
+
+def attention_partial(q, k, v, bias=None, *, scale=None, causal=False, key_begin=0,
+                      key_end=None):
+    """Attention of every query over the keys [key_begin, key_end) only.
+
+    The definition above with every logit outside the key range set to -inf:
+    the state of one disjoint key subset, normalised by its own sum.  Returns
+    ``(O_part [B,Hq,Nq,D], LSE_part [B,Hq,Nq])``; rows that see no key of the
+    range get O_part = 0 and LSE_part = -inf.  Causal positions stay global
+    (key j is visible to query i iff j <= i), so the partials of a partition
+    of the keys describe the same rows as the whole.
+    """
+    b_, hq_, hkv, nq, nk, d = _check_shapes(q, k, v, bias)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    key_end = nk if key_end is None else min(int(key_end), nk)
+    key_begin = max(0, min(int(key_begin), key_end))
+    group = hq_ // hkv
+    o = np.zeros((b_, hq_, nq, d), dtype=np.float64)
+    lse = np.full((b_, hq_, nq), -np.inf, dtype=np.float64)
+    if key_end == key_begin:
+        return o, lse
+    cols = np.arange(nk)
+    outside = (cols < key_begin) | (cols >= key_end)
+    rows = np.arange(nq, dtype=np.int64)
+    for b in range(b_):
+        for h in range(hq_):
+            hk = h // group
+            extra = np.where(outside[None, :], -np.inf, 0.0)
+            if bias is not None:
+                extra = extra + _f64(bias[b, h])
+            o[b, h], lse[b, h] = attention_head_rows(
+                q[b, h], k[b, hk], v[b, hk], rows=rows, scale=scale, causal=causal,
+                bias_rows=np.broadcast_to(extra, (nq, nk)))
+    return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine normalised partial results over disjoint key sets into one.
+
+    o_parts [P, ..., D], lse_parts [P, ...].  A normalised partial (O_s,
+    LSE_s) is the state (m = LSE_s, l = 1, o = O_s): its sum times e^m is
+    e^LSE_s, the same total weight.  The states are folded one after another
+    with ``merge_states`` (the merge of the kwkr.cn tutorial, §2.2), and the
+    result is normalised once at the end: O = o / l, LSE = m + ln l.  A
+    partial with LSE = -inf (no visible key) carries l = 0 and adds nothing;
+    with no partial at all, or only such ones, O = 0 and LSE = -inf.
+    """
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    if o_parts.shape[:-1] != lse_parts.shape:
+        raise ValueError("o_parts must be lse_parts' shape plus a trailing D axis")
+    shape = lse_parts.shape[1:]
+    m = np.full(shape, -np.inf)
+    l = np.zeros(shape)
+    o = np.zeros(o_parts.shape[1:])
+    for o_s, lse_s in zip(o_parts, lse_parts):
+        l_s = np.where(np.isfinite(lse_s), 1.0, 0.0)
+        m, l, o = merge_states(m, l, o, lse_s, l_s, o_s * l_s[..., None])
+    ok = l > 0
+    o_out = np.where(ok[..., None], o / np.where(ok, l, 1.0)[..., None], 0.0)
+    lse_out = np.where(ok, m + np.log(np.where(ok, l, 1.0)), -np.inf)
+    return o_out, lse_out
