@@ -4,7 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 A step is one fa_forward call (one kernel launch) over the whole workload, with
-inputs already resident in HBM.  The default workload is B=2, H=16, S=4096,
+inputs already resident in HBM; for the key-split workloads it is one
+fa_forward_split call (the split kernel and the merge kernel, workspace
+allocated beforehand).  The default workload is B=2, H=16, S=4096,
 D=64, bf16, causal.  Timing follows the CUDA-event method of the Day 26 post
 (blog.ans20xx.com/posts/ai/day26): W untimed warm-up steps, then K steps, each
 bracketed by its own pair of events on the stream the kernel runs on, plus one
@@ -12,10 +14,11 @@ pair around all K.  Prints one JSON line.
 
 value     = 4*B*H*S^2*D / t_step in TFLOP/s (the post's formula, not halved
             for causal), t_step = wall time of the K steps / K;
-roofline  = the kernel's own rate against the chip's peak: useful flops
-            (visible query-key pairs only) per launch / mean launch time for
-            matrix-core-bound workloads, or algorithmic bytes / launch time for
-            the bias-streaming workload;
+roofline  = the step's own rate against the chip's peak: useful flops
+            (visible query-key pairs only) per step / mean step time where the
+            workload's arithmetic intensity (useful flops per algorithmic byte)
+            is above the chip's ridge point (peak flops / peak HBM bandwidth),
+            else algorithmic bytes (Q, K, V, visible bias, O, LSE) / step time;
 cpu_baseline = the fp64 oracle, timed on the host on a bounded sample of the
             same workload (whole heads), scaled to the same metric.
 """
@@ -141,8 +144,17 @@ def main():
     dtype_code = binding._dtype_code(q)
     call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(),
                  bias.data_ptr() if bias is not None else None, o.data_ptr(), lse.data_ptr(),
-                 w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal), dtype_code,
-                 stream.cuda_stream)
+                 w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal), dtype_code)
+    splits = None
+    if w.path == "split":
+        splits = binding.fa_split_count(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D)
+        ws_bytes = binding.fa_split_workspace_bytes(w.B, w.Hq, w.Nq, w.D, splits)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        entry = lib.fa_forward_split
+        call_args = call_args + (splits, workspace.data_ptr(), ws_bytes, stream.cuda_stream)
+    else:
+        entry = lib.fa_forward
+        call_args = call_args + (stream.cuda_stream,)
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
@@ -154,7 +166,7 @@ def main():
         del src, dst
 
     def step():
-        st = lib.fa_forward(*call_args)
+        st = entry(*call_args)
         if st != 0:
             raise binding.FaError(st, binding.fa_status_string(st))
 
@@ -182,7 +194,8 @@ def main():
 
     value = w.metric_flops() / (ms_per_step / 1e3) / 1e12
     peak = metrics.MFMA_PEAK_TFLOPS[w.dtype]
-    if w.bias:
+    ridge = peak * 1e12 / (metrics.HBM_PEAK_GBS * 1e9)   # flops per byte
+    if w.useful_flops() / w.io_bytes() < ridge:
         achieved = w.io_bytes() / (launch_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": metrics.HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / metrics.HBM_PEAK_GBS, 4)}
@@ -208,7 +221,7 @@ def main():
         "data": "synthetic: i.i.d. N(0,1) inputs from a seeded generator",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
                    "Nk": w.Nk, "D": w.D, "causal": w.causal, "bias": w.bias,
-                   "parallelism": "single GPU"},
+                   "path": w.path, "splits": splits, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * value / metrics.MFMA_PEAK_TFLOPS["bf16"], 2),
         "useful_tflops": round(w.useful_flops() / (ms_per_step / 1e3) / 1e12, 2),
         "launch_ms": {"mean": round(launch_ms, 5), "median": round(statistics.median(per), 5),

@@ -53,7 +53,7 @@ typedef enum fa_dtype {
   FA_DTYPE_FP32 = 2
 } fa_dtype;
 
-/* Status codes returned by fa_check_args and fa_forward. */
+/* Status codes returned by every entry point. */
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL_POINTER = 1, /* q, o or lse is NULL while the problem is not empty, or    */
@@ -70,7 +70,8 @@ typedef enum fa_status {
                            /* < 2^30; B*Hq*ceil(Nq/128) < 2^31; one head's Q and one     */
                            /* head's K (Nq*D or Nk*D elements) < 2^31 bytes; with a bias, */
                            /* 128*Nk elements < 2^31 bytes                               */
-  FA_ERR_HIP = 10          /* the HIP runtime rejected the launch                        */
+  FA_ERR_HIP = 10,         /* the HIP runtime rejected the launch                        */
+  FA_ERR_WORKSPACE = 11    /* key-split workspace is NULL, too small or misaligned       */
 } fa_status;
 
 /*
@@ -97,6 +98,86 @@ int fa_forward(const void* q, const void* k, const void* v, const void* bias,
                void* o, float* lse,
                int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
                float scale, int causal, int dtype, void* stream);
+
+/*
+ * Key-split ("flash-decode") forward.
+ *
+ * The same operation as fa_forward, for problems whose query-row blocks alone
+ * cannot fill the GPU (few heads, short Nq, decode steps with Nq = 1 against a
+ * long Nk).  Two launches on `stream`:
+ *  1. the keys of each KV head are cut into num_splits contiguous ranges of
+ *     64-key tiles; one workgroup per (b, hk, 128-row block, range) runs the
+ *     fused forward over its range and writes the range's normalised partial
+ *     output O_s (float32) and LSE_s into the workspace.  The Hq/Hkv query
+ *     heads that share a KV head are packed into one row space of
+ *     (Hq/Hkv)*Nq rows, so a decode step with Nq = 1 still fills row blocks;
+ *  2. fa_merge's kernel combines the num_splits partials of every row into o
+ *     (dtype) and lse with the merge of the kwkr.cn/news/592482 tutorial,
+ *     §2.2 (closing remarks there name flash decode as an extension of the
+ *     fused kernel).
+ * Results equal fa_forward's up to float32 rounding order.  All conventions of
+ * fa_forward apply; in addition:
+ *  - 1 <= num_splits <= 1024, else FA_ERR_BAD_SIZE.  Splits beyond the number
+ *    of visible 64-key tiles of a row block compute nothing and are merged
+ *    away;
+ *  - workspace: device memory owned by the caller, 16-byte aligned, at least
+ *    fa_split_workspace_bytes(B, Hq, Nq, D, num_splits) bytes
+ *    (workspace_bytes states its size), not overlapping any other argument;
+ *    else FA_ERR_WORKSPACE (FA_ERR_OVERLAP for an overlap).  Its contents on
+ *    entry are ignored and on return are unspecified.  Two calls that run at
+ *    the same time need two workspaces;
+ *  - (Hq/Hkv)*Nq*D elements must stay below 2^31 bytes, and
+ *    B*Hkv*ceil((Hq/Hkv)*Nq/128)*num_splits below 2^31, else FA_ERR_TOO_LARGE.
+ * Empty problems (B, Hq or Nq == 0) launch nothing and may pass a NULL
+ * workspace.
+ */
+int fa_forward_split(const void* q, const void* k, const void* v, const void* bias,
+                     void* o, float* lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                     float scale, int causal, int dtype,
+                     int64_t num_splits, void* workspace, int64_t workspace_bytes,
+                     void* stream);
+
+/*
+ * Workspace size of fa_forward_split, in bytes, through *bytes:
+ * partial O, float32 [num_splits][B*Hq*Nq][D], then partial LSE, float32
+ * [num_splits][B*Hq*Nq], from the next 256-byte boundary.  Pure host code.
+ * Returns FA_ERR_BAD_SIZE for negative sizes or num_splits outside
+ * [1, 1024], FA_ERR_HEAD_DIM for D not 64 or 128, FA_ERR_NULL_POINTER for a
+ * NULL bytes.
+ */
+int fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D,
+                             int64_t num_splits, int64_t* bytes);
+
+/*
+ * The split count the library suggests for a problem, through *num_splits
+ * (pure host code).  It aims for about 1024 workgroups (four per compute
+ * unit of the 256) while keeping at least four 64-key tiles per split; 1 when
+ * the row blocks alone reach that.  Same size errors as
+ * fa_split_workspace_bytes, plus FA_ERR_HEAD_GROUPS.
+ */
+int fa_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                   int64_t* num_splits);
+
+/*
+ * Merge of normalised partial attention results over disjoint key sets
+ * (kwkr.cn/news/592482 tutorial, §2.2, for several states at once): the
+ * combine step of a key-split or key-sharded forward.
+ *
+ *   part_o   float32 [num_parts][rows][D]   partial outputs, each normalised
+ *   part_lse float32 [num_parts][rows]      their natural-log LSEs (-inf: the
+ *                                           part saw no key of that row)
+ *   o        dtype   [rows][D]              out: sum_s w_s O_s / sum_s w_s,
+ *                                           w_s = exp(LSE_s - max_s LSE_s)
+ *   lse      float32 [rows]                 out: log(sum_s exp(LSE_s))
+ * A row with no finite LSE_s (or num_parts == 0) gets O = 0 and LSE = -inf;
+ * the O_s of a part with LSE_s = -inf is not read.  D: a multiple of 4 in
+ * [4, 65536] (FA_ERR_HEAD_DIM).  part_o and o 16-byte aligned, part_lse and
+ * lse 4-byte aligned; o and lse must not overlap each other or the partials.
+ * rows == 0 launches nothing.  Enqueued on stream; returns without waiting.
+ */
+int fa_merge(const float* part_o, const float* part_lse, int64_t num_parts, int64_t rows,
+             int64_t D, void* o, float* lse, int dtype, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);

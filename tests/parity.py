@@ -47,9 +47,20 @@ def run_gpu(q, k, v, bias, scale, causal):
     return o, lse
 
 
-def full_check(q, k, v, bias, scale, causal, dtype, what=""):
-    """Whole-tensor comparison with the oracle (small problems)."""
-    o, lse = run_gpu(q, k, v, bias, scale, causal)
+def run_split(num_splits=None):
+    """fa_forward_split with a given split count (None: the library's suggestion)."""
+    def run(q, k, v, bias, scale, causal):
+        o, lse = binding.forward_split(q, k, v, bias, causal=causal, scale=scale,
+                                       num_splits=num_splits)
+        torch.cuda.synchronize()
+        return o, lse
+    return run
+
+
+def full_check(q, k, v, bias, scale, causal, dtype, what="", run=None):
+    """Whole-tensor comparison with the oracle (small problems).  ``run`` is the
+    GPU entry point to test (default: fa_forward through ``run_gpu``)."""
+    o, lse = (run or run_gpu)(q, k, v, bias, scale, causal)
     o_ref, lse_ref = attention_forward(f64(q), f64(k), f64(v),
                                        None if bias is None else f64(bias),
                                        scale=scale, causal=causal)

@@ -46,7 +46,9 @@ def forward_status(**over):
 def test_library_loads_and_exports_every_declared_symbol():
     lib = binding.load_library()
     names = declared_functions()
-    assert set(names) == {"fa_check_args", "fa_forward", "fa_status_string", "fa_version"}
+    assert set(names) == {"fa_check_args", "fa_forward", "fa_forward_split", "fa_merge",
+                          "fa_split_count", "fa_split_workspace_bytes", "fa_status_string",
+                          "fa_version"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
@@ -57,7 +59,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert binding.fa_version().startswith("fa ") and "gfx950" in binding.fa_version()
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = binding.fa_status_string(code)
         assert s and s != "unknown status", code
     assert binding.fa_status_string(99) == "unknown status"
@@ -122,3 +124,82 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         binding.load_library()
     monkeypatch.setattr(binding, "_lib", None)
+
+
+# ---------------------------------------------------------------------------
+# key-split path and merge: validation only (no launch on the CPU)
+# ---------------------------------------------------------------------------
+
+WS = 0x100000000 * 8   # fake workspace address, far from the tensors above
+
+
+def split_status(num_splits=4, workspace=WS, workspace_bytes=1 << 40, **over):
+    a = dict(OK_ARGS, **over)
+    return binding.fa_forward_split(a["q"], a["k"], a["v"], a["bias"], a["o"], a["lse"], a["B"],
+                                    a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"],
+                                    a["causal"], a["dtype"], num_splits, workspace,
+                                    workspace_bytes, None)
+
+
+def test_split_workspace_bytes_layout():
+    # partial O fp32 [S][B*Hq*Nq][D], then partial LSE fp32 [S][B*Hq*Nq] from a 256-byte boundary
+    rows = 2 * 4 * 100
+    for s in (1, 3, 32):
+        o_bytes = s * rows * 64 * 4
+        o_pad = (o_bytes + 255) // 256 * 256
+        assert binding.fa_split_workspace_bytes(2, 4, 100, 64, s) == o_pad + s * rows * 4
+    assert binding.fa_split_workspace_bytes(1, 1, 1, 128, 1) == 512 + 4
+    assert binding.fa_split_workspace_bytes(0, 4, 100, 64, 2) == 0
+    for bad, code in ((dict(num_splits=0), 2), (dict(num_splits=1025), 2), (dict(D=96), 4),
+                      (dict(B=-1), 2)):
+        a = {**dict(B=2, Hq=4, Nq=100, D=64, num_splits=2), **bad}
+        with pytest.raises(binding.FaError) as e:
+            binding.fa_split_workspace_bytes(a["B"], a["Hq"], a["Nq"], a["D"], a["num_splits"])
+        assert e.value.status == code
+
+
+def test_split_count_heuristic():
+    # decode step: 8 batches x 4 KV heads, 5 query heads per group, Nq = 1, 32768 keys:
+    # 32 row blocks -> 32 splits of 16 tiles each
+    assert binding.fa_split_count(8, 20, 4, 1, 32768, 128) == 32
+    # enough row blocks already: 2 x 16 heads x 32 blocks of 128 rows
+    assert binding.fa_split_count(2, 16, 16, 4096, 4096, 64) == 1
+    # few keys: at least 4 tiles per split
+    assert binding.fa_split_count(1, 1, 1, 1, 64 * 8, 64) == 2
+    assert binding.fa_split_count(1, 1, 1, 1, 10, 64) == 1
+    assert binding.fa_split_count(1, 1, 1, 1, 1 << 24, 64) == 1024
+    assert binding.fa_split_count(0, 1, 1, 1, 100, 64) == 1
+    with pytest.raises(binding.FaError):
+        binding.fa_split_count(1, 5, 2, 1, 100, 64)
+
+
+def test_split_rejections_before_launch():
+    need = binding.fa_split_workspace_bytes(2, 4, 100, 64, 4)
+    assert split_status(num_splits=0) == 2
+    assert split_status(num_splits=1025) == 2
+    assert split_status(workspace=None) == 11
+    assert split_status(workspace=WS + 8) == 11
+    assert split_status(workspace_bytes=need - 1) == 11
+    assert split_status(workspace=O) == 8            # workspace over the output
+    assert split_status(workspace=Q - 256) == 8      # runs into q
+    assert split_status(D=96) == 4 and split_status(q=None) == 1   # the common checks first
+    # packed rows of one KV head: (Hq/Hkv) * Nq * D * 2 bytes must stay below 2^31
+    assert split_status(Hq=64, Hkv=1, Nq=1 << 18, B=1, workspace_bytes=1 << 62) == 9
+    # empty problem: nothing launched, no workspace needed
+    assert split_status(B=0, workspace=None, workspace_bytes=0) == 0
+
+
+def merge_status(part_o=WS, part_lse=WS + (1 << 30), num_parts=3, rows=10, D=64, o=O, lse=L,
+                 dtype=binding.FA_DTYPE_BF16):
+    return binding.fa_merge(part_o, part_lse, num_parts, rows, D, o, lse, dtype, None)
+
+
+def test_merge_rejections_before_launch():
+    assert merge_status(rows=0) == 0 and merge_status(rows=0, o=None, lse=None) == 0
+    assert merge_status(dtype=7) == 5
+    assert merge_status(num_parts=-1) == 2 and merge_status(rows=-1) == 2
+    assert merge_status(D=6) == 4 and merge_status(D=0) == 4 and merge_status(D=65540) == 4
+    assert merge_status(o=None) == 1 and merge_status(part_lse=None) == 1
+    assert merge_status(part_o=WS + 4) == 7 and merge_status(lse=L + 2) == 7
+    assert merge_status(o=WS + 64) == 8 and merge_status(lse=WS + (1 << 30) + 8) == 8
+    assert merge_status(num_parts=1 << 31) == 9

@@ -1,0 +1,179 @@
+"""GPU parity of the key-split path: fa_forward_split (partials + merge) and the
+public fa_merge, through the C ABI, against the fp64 oracle.
+
+fa_forward_split must give the attention of the definition (the oracle's
+attention_forward) for any split count; fa_merge must give the oracle's
+merge_partials of the same float32 partials.  Small problems are compared
+element by element, the two full-size key-split workloads on sampled rows in
+the configuration bench.py times (the library's suggested split count).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_partial, merge_partials
+from tests.parity import errors, f64, full_check, run_gpu, run_split, sampled_check
+from tiled_attention_forward_amd import binding
+from tiled_attention_forward_amd.workloads import WORKLOADS, custom, make_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+SPLIT_CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, causal, bias, splits (None: library's choice)
+    (2, 8, 2, 1, 1000, 128, "bf16", False, False, 3),     # decode step, ragged keys
+    (2, 8, 2, 1, 1000, 128, "bf16", False, False, None),
+    (1, 20, 4, 1, 4100, 128, "bf16", False, True, 16),    # decode with a logit term
+    (3, 4, 1, 3, 777, 64, "fp16", True, False, 5),        # 12 packed rows, causal
+    (1, 4, 1, 100, 300, 64, "bf16", True, True, 4),       # row blocks cross head boundaries
+    (1, 4, 2, 300, 300, 64, "fp16", True, True, 4),
+    (1, 2, 2, 5, 777, 64, "fp32", False, True, 5),
+    (1, 2, 1, 70, 130, 128, "fp32", True, False, 3),
+    (1, 2, 2, 1, 100, 64, "bf16", False, False, 8),       # more splits than key tiles
+    (2, 6, 3, 129, 1000, 128, "fp16", False, False, 7),
+    (1, 1, 1, 1, 1, 64, "bf16", True, False, 1),
+    (1, 4, 4, 1000, 1000, 64, "bf16", True, False, 2),
+    (1, 2, 2, 700, 1, 128, "bf16", True, False, 3),       # one key, splits mostly empty
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_split_matches_oracle(gpu_device, case):
+    B, Hq, Hkv, Nq, Nk, D, dt, causal, bias, splits = case
+    w = custom(B, Hq, Hkv, Nq, Nk, D, dt, causal, bias)
+    _log(f"split case {case}")
+    q, k, v, b = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=21))
+    st, _, _ = full_check(q, k, v, b, w.scale, causal, dt, str(case), run=run_split(splits))
+    _log(st)
+
+
+@pytest.mark.parametrize("case", [
+    (1, 4, 4, 300, 333, 64, "bf16", True, False),
+    (2, 8, 2, 1, 999, 128, "bf16", False, True),
+    (1, 6, 2, 77, 200, 128, "fp16", True, True),
+    (1, 2, 1, 50, 90, 64, "fp32", False, False),
+], ids=lambda c: "-".join(map(str, c)))
+def test_one_split_equals_fused_path(gpu_device, case):
+    """With one split, every row runs the fused kernel's arithmetic over the same
+    tiles in the same order, and the merge of one part multiplies by exactly 1:
+    the result must equal fa_forward's bit for bit."""
+    B, Hq, Hkv, Nq, Nk, D, dt, causal, bias = case
+    w = custom(B, Hq, Hkv, Nq, Nk, D, dt, causal, bias)
+    _log(f"one-split case {case}")
+    q, k, v, b = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=22))
+    o1, l1 = run_gpu(q, k, v, b, w.scale, causal)
+    o2, l2 = run_split(1)(q, k, v, b, w.scale, causal)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_split_no_keys(gpu_device):
+    q = torch.randn(2, 4, 3, 64, device=gpu_device).to(torch.bfloat16)
+    k = torch.empty(2, 2, 0, 64, device=gpu_device, dtype=torch.bfloat16)
+    for causal in (False, True):
+        o, lse = run_split(4)(q, k, k, None, 0.125, causal)
+        assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_split_workspace_reused(gpu_device):
+    """One caller-owned workspace for two problems in a row, the second smaller:
+    its earlier contents do not leak into the result."""
+    w1 = custom(2, 8, 2, 1, 3000, 128, "bf16", False, False)
+    w2 = custom(1, 4, 1, 2, 500, 128, "bf16", True, False)
+    need = binding.fa_split_workspace_bytes(w1.B, w1.Hq, w1.Nq, w1.D, 12)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=gpu_device)  # garbage floats
+    for w, s in ((w1, 12), (w2, 5)):
+        q, k, v, _ = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=23))
+
+        def run(q, k, v, bias, scale, causal, s=s):
+            o, lse = binding.forward_split(q, k, v, bias, causal=causal, scale=scale,
+                                           num_splits=s, workspace=ws)
+            torch.cuda.synchronize()
+            return o, lse
+        full_check(q, k, v, None, w.scale, w.causal, w.dtype, f"reuse {w}", run=run)
+
+
+def test_split_deterministic(gpu_device):
+    w = custom(2, 20, 4, 1, 5000, 128, "bf16", False, True)
+    q, k, v, b = (t.to(gpu_device) for t in make_inputs(w, seed=24))
+    o1, l1 = run_split(9)(q, k, v, b, w.scale, False)
+    o2, l2 = run_split(9)(q, k, v, b, w.scale, False)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# fa_merge on partials the oracle computed
+# ---------------------------------------------------------------------------
+
+MERGE_CASES = [
+    # parts (key ranges), Nk, D, out dtype
+    ([(0, 40), (40, 41), (41, 100)], 100, 128, "bf16"),
+    ([(0, 0), (0, 33), (33, 33), (33, 70)], 70, 64, "fp32"),   # empty parts: LSE = -inf
+    ([(10, 50)], 60, 12, "fp16"),                               # D not 64/128; keys 0-9 unused
+    ([(0, 5), (5, 9), (9, 17), (17, 30), (30, 31)], 31, 4, "fp32"),
+]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES, ids=lambda c: f"P{len(c[0])}-D{c[2]}-{c[3]}")
+def test_merge_matches_oracle(gpu_device, case):
+    ranges, nk, d, dt = case
+    r = np.random.default_rng(31)
+    q = r.standard_normal((2, 3, 9, d))
+    k = r.standard_normal((2, 3, nk, d))
+    v = r.standard_normal((2, 3, nk, d))
+    parts = [attention_partial(q, k, v, None, scale=0.5, causal=True, key_begin=a, key_end=b)
+             for a, b in ranges]
+    po = torch.tensor(np.stack([p[0] for p in parts]), dtype=torch.float32)
+    pl = torch.tensor(np.stack([p[1] for p in parts]), dtype=torch.float32)
+    o_ref, l_ref = merge_partials(po.double().numpy(), pl.double().numpy())
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dt]
+    o, lse = binding.merge(po.to(gpu_device), pl.to(gpu_device), tdt)
+    torch.cuda.synchronize()
+    st = errors(f64(o), lse.cpu().numpy(), o_ref, l_ref)
+    _log(case, st)
+    # The merge is float32 arithmetic on float32 partials, then one rounding to
+    # the output type: |O - O_ref| <= u * |O_ref| + 1e-5 elementwise (u the
+    # output type's unit roundoff; 1e-5 covers the float32 weights and sums).
+    # The fixed 1e-2 bar would not hold here: a partial's row can be one V row
+    # itself, and a bf16 value of magnitude >= 4 rounds by up to 0.0156.
+    u = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11, "fp32": 2.0 ** -24}[dt]
+    err = np.abs(f64(o) - o_ref)
+    bound = u * np.abs(o_ref) + 1e-5
+    assert np.all(err <= bound), f"merge {case}: worst err/bound {(err / bound).max()}"
+    assert st["lse_max"] <= 1e-5
+
+
+def test_merge_no_parts(gpu_device):
+    po = torch.empty(0, 5, 8, device=gpu_device)
+    pl = torch.empty(0, 5, device=gpu_device)
+    o, lse = binding.merge(po, pl, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+# ---------------------------------------------------------------------------
+# full-size key-split workloads, as bench.py runs them
+# ---------------------------------------------------------------------------
+
+SPLIT_FULL = [n for n, w in WORKLOADS.items() if w.path == "split"]
+
+
+@pytest.mark.parametrize("name", SPLIT_FULL)
+def test_split_full_size_sampled(gpu_device, name):
+    w = WORKLOADS[name]
+    splits = binding.fa_split_count(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D)
+    _log(f"full-size split {name}, {splits} splits")
+    q, k, v, bias = make_inputs(w, seed=0, device=gpu_device)
+    o, lse = run_split(splits)(q, k, v, bias, w.scale, w.causal)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    heads = sorted({(0, 0), (w.B - 1, w.Hq - 1), (0, w.Hq // 2), (w.B // 2, 1 % w.Hq),
+                    (w.B // 2, (w.Hq - 1) // 2)})
+    rows = sample_rows(w.Nq, 40, seed=2)
+    st = sampled_check(q, k, v, bias, w.scale, w.causal, w.dtype, heads, rows, o, lse, name)
+    _log(st)
+    del q, k, v, bias, o, lse
+    torch.cuda.empty_cache()

@@ -1,12 +1,15 @@
 """ctypes binding of libfa.so (argument marshalling only).
 
-``fa_forward``, ``fa_check_args``, ``fa_status_string`` and ``fa_version`` take
-the same arguments as the C functions of ``include/fa.h`` (device pointers as
-Python ints).  ``forward`` is the tensor-level convenience: it checks the torch
-tensors, allocates O and LSE with torch, and calls ``fa_forward`` on the
-current stream.  Every step of the attention runs in the library's kernels; if
-the library is missing or does not load, the call raises instead of computing
-anything some other way.
+``fa_forward``, ``fa_forward_split``, ``fa_merge``, ``fa_split_count``,
+``fa_split_workspace_bytes``, ``fa_check_args``, ``fa_status_string`` and
+``fa_version`` take the same arguments as the C functions of ``include/fa.h``
+(device pointers as Python ints; the two size queries return their value).
+``forward``, ``forward_split`` and ``merge`` are the tensor-level
+conveniences: they check the torch tensors, allocate outputs (and the
+key-split workspace) with torch, and call the library on the current stream.
+Every step of the attention runs in the library's kernels; if the library is
+missing or does not load, the call raises instead of computing anything some
+other way.
 """
 
 from __future__ import annotations
@@ -22,7 +25,7 @@ FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_BAD_SIZE", 3: "FA_ERR_HEAD_GROUPS",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_DTYPE", 6: "FA_ERR_SCALE", 7: "FA_ERR_ALIGNMENT",
-    8: "FA_ERR_OVERLAP", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP",
+    8: "FA_ERR_OVERLAP", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP", 11: "FA_ERR_WORKSPACE",
 }
 
 _lib = None
@@ -52,6 +55,15 @@ def load_library():
     lib.fa_check_args.restype = i32
     lib.fa_forward.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32, i32, i32, p]
     lib.fa_forward.restype = i32
+    lib.fa_forward_split.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32, i32,
+                                     i32, i64, p, i64, p]
+    lib.fa_forward_split.restype = i32
+    lib.fa_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(i64)]
+    lib.fa_split_workspace_bytes.restype = i32
+    lib.fa_split_count.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]
+    lib.fa_split_count.restype = i32
+    lib.fa_merge.argtypes = [p, p, i64, i64, i64, p, p, i32, p]
+    lib.fa_merge.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -71,6 +83,37 @@ def fa_forward(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtyp
                                      float(scale), int(causal), int(dtype), stream)
 
 
+def fa_forward_split(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype,
+                     num_splits, workspace, workspace_bytes, stream) -> int:
+    return load_library().fa_forward_split(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D,
+                                           float(scale), int(causal), int(dtype),
+                                           int(num_splits), workspace, int(workspace_bytes),
+                                           stream)
+
+
+def fa_merge(part_o, part_lse, num_parts, rows, D, o, lse, dtype, stream) -> int:
+    return load_library().fa_merge(part_o, part_lse, int(num_parts), int(rows), int(D), o, lse,
+                                   int(dtype), stream)
+
+
+def fa_split_workspace_bytes(B, Hq, Nq, D, num_splits) -> int:
+    """Workspace bytes of fa_forward_split; raises FaError on invalid sizes."""
+    out = ctypes.c_int64(0)
+    st = load_library().fa_split_workspace_bytes(B, Hq, Nq, D, num_splits, ctypes.byref(out))
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+    return out.value
+
+
+def fa_split_count(B, Hq, Hkv, Nq, Nk, D) -> int:
+    """The library's suggested key-split count; raises FaError on invalid sizes."""
+    out = ctypes.c_int64(0)
+    st = load_library().fa_split_count(B, Hq, Hkv, Nq, Nk, D, ctypes.byref(out))
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+    return out.value
+
+
 def fa_status_string(status: int) -> str:
     return load_library().fa_status_string(int(status)).decode()
 
@@ -88,17 +131,7 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def forward(q, k, v, bias=None, *, causal=False, scale=None, out=None, lse=None, stream=None):
-    """O, LSE = attention(q, k, v [, bias]) on the GPU through fa_forward.
-
-    q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D], bias [B,Hq,Nq,Nk] or None: contiguous
-    CUDA tensors of one dtype (bf16, fp16 or fp32).  ``scale=None`` means
-    1/sqrt(D).  ``out``/``lse`` may be preallocated ([B,Hq,Nq,D] dtype and
-    [B,Hq,Nq] float32).  Runs on ``stream`` (a torch.cuda.Stream) or the
-    current stream.
-    """
-    import torch
-    lib = load_library()
+def _check_inputs(q, k, v, bias):
     for name, t in (("q", q), ("k", k), ("v", v)) + ((("bias", bias),) if bias is not None else ()):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a CUDA tensor")
@@ -112,18 +145,103 @@ def forward(q, k, v, bias=None, *, causal=False, scale=None, out=None, lse=None,
         raise ValueError("k and v must be [B, Hkv, Nk, D] matching q")
     if bias is not None and tuple(bias.shape) != (B, Hq, Nq, Nk):
         raise ValueError("bias must be [B, Hq, Nq, Nk]")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
+    return B, Hq, Hkv, Nq, Nk, D
+
+
+def _outputs(q, out, lse):
+    import torch
+    B, Hq, Nq, _ = q.shape
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def forward(q, k, v, bias=None, *, causal=False, scale=None, out=None, lse=None, stream=None):
+    """O, LSE = attention(q, k, v [, bias]) on the GPU through fa_forward.
+
+    q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D], bias [B,Hq,Nq,Nk] or None: contiguous
+    CUDA tensors of one dtype (bf16, fp16 or fp32).  ``scale=None`` means
+    1/sqrt(D).  ``out``/``lse`` may be preallocated ([B,Hq,Nq,D] dtype and
+    [B,Hq,Nq] float32).  Runs on ``stream`` (a torch.cuda.Stream) or the
+    current stream.
+    """
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v, bias)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out, lse = _outputs(q, out, lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                         bias.data_ptr() if bias is not None else None,
                         out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, D, float(scale),
                         int(bool(causal)), _dtype_code(q), stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+    return out, lse
+
+
+def forward_split(q, k, v, bias=None, *, causal=False, scale=None, num_splits=None,
+                  workspace=None, out=None, lse=None, stream=None):
+    """The same result as ``forward`` through the key-split path (fa_forward_split).
+
+    ``num_splits=None`` takes the library's suggestion (fa_split_count).
+    ``workspace`` may be a preallocated CUDA uint8 tensor of at least
+    fa_split_workspace_bytes(...) bytes; otherwise one is allocated with torch.
+    """
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v, bias)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if num_splits is None:
+        num_splits = fa_split_count(B, Hq, Hkv, Nq, Nk, D)
+    need = fa_split_workspace_bytes(B, Hq, Nq, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    out, lse = _outputs(q, out, lse)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib.fa_forward_split(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              bias.data_ptr() if bias is not None else None,
+                              out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, D,
+                              float(scale), int(bool(causal)), _dtype_code(q), int(num_splits),
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+    return out, lse
+
+
+def merge(part_o, part_lse, dtype, *, out=None, lse=None, stream=None):
+    """O, LSE from normalised partials through fa_merge.
+
+    part_o float32 [P, ..., D], part_lse float32 [P, ...] (contiguous CUDA
+    tensors); the result has shape [..., D] in ``dtype`` and [...] float32.
+    """
+    import torch
+    lib = load_library()
+    if part_o.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    if not (part_o.is_cuda and part_lse.is_cuda and part_o.is_contiguous()
+            and part_lse.is_contiguous()):
+        raise ValueError("partials must be contiguous CUDA tensors")
+    if tuple(part_o.shape[:-1]) != tuple(part_lse.shape):
+        raise ValueError("part_o must be part_lse's shape plus a trailing D axis")
+    P, D = part_o.shape[0], part_o.shape[-1]
+    rows = part_lse[0].numel() if P > 0 else math.prod(part_lse.shape[1:])
+    if out is None:
+        out = torch.empty(tuple(part_o.shape[1:]), dtype=dtype, device=part_o.device)
+    if lse is None:
+        lse = torch.empty(tuple(part_lse.shape[1:]), dtype=torch.float32, device=part_o.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(part_o.device)
+    st = lib.fa_merge(part_o.data_ptr() if P > 0 else None,
+                      part_lse.data_ptr() if P > 0 else None, P, rows, D, out.data_ptr(),
+                      lse.data_ptr(), _dtype_code(out), stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, fa_status_string(st))
     return out, lse

@@ -99,6 +99,128 @@ extern "C" int fa_forward(const void* q, const void* k, const void* v, const voi
   return fa::launch_forward(a);
 }
 
+namespace {
+
+// Sizes of the key-split path, after the common checks: index limits of the
+// packed row space and of the grid.
+int check_split_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t D, int esz,
+                      int64_t num_splits) {
+  if (num_splits < 1 || num_splits > fa::kMaxSplits) return FA_ERR_BAD_SIZE;
+  const int64_t lim31 = int64_t(1) << 31;
+  const __int128 rows = __int128(Hq / Hkv) * Nq;  // packed rows of one KV head
+  if (rows * D * esz >= lim31) return FA_ERR_TOO_LARGE;
+  const int64_t tiles = (int64_t(rows) + fa::kRowsPerBlock - 1) / fa::kRowsPerBlock;
+  if (__int128(B) * Hkv * tiles * num_splits >= lim31) return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D,
+                                        int64_t num_splits, int64_t* bytes) {
+  if (bytes == nullptr) return FA_ERR_NULL_POINTER;
+  if (B < 0 || Hq < 0 || Nq < 0 || D < 0) return FA_ERR_BAD_SIZE;
+  if (num_splits < 1 || num_splits > fa::kMaxSplits) return FA_ERR_BAD_SIZE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  const __int128 rows = __int128(B) * Hq * Nq;
+  if (rows * D * 4 * num_splits >= (__int128(1) << 62)) return FA_ERR_TOO_LARGE;
+  *bytes = fa::split_workspace_bytes(int64_t(rows), D, num_splits);
+  return FA_OK;
+}
+
+extern "C" int fa_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                              int64_t D, int64_t* num_splits) {
+  if (num_splits == nullptr) return FA_ERR_NULL_POINTER;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_BAD_SIZE;
+  if (Hq > 0 && Hkv < 1) return FA_ERR_BAD_SIZE;
+  if (Hq > 0 && Hq % Hkv != 0) return FA_ERR_HEAD_GROUPS;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  *num_splits = 1;
+  if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
+  const int64_t lim = int64_t(1) << 30;
+  if (B >= lim || Hq >= lim || Nq >= lim || Nk >= lim) return FA_ERR_TOO_LARGE;
+  // About 1024 workgroups: four per compute unit, enough to keep every CU busy
+  // through the tail of the grid; each split keeps at least 4 key tiles so the
+  // partials stay a small fraction of the traffic.
+  constexpr int64_t kTargetBlocks = 1024;
+  const __int128 rows = __int128(Hq / Hkv) * Nq;
+  const __int128 units = __int128(B) * Hkv * ((rows + fa::kRowsPerBlock - 1) / fa::kRowsPerBlock);
+  if (units >= kTargetBlocks) return FA_OK;
+  int64_t s = (kTargetBlocks + int64_t(units) - 1) / int64_t(units);
+  const int64_t tiles = (Nk + 63) / 64;
+  const int64_t cap = tiles / 4 > 1 ? tiles / 4 : 1;
+  if (s > cap) s = cap;
+  if (s > fa::kMaxSplits) s = fa::kMaxSplits;
+  *num_splits = s;
+  return FA_OK;
+}
+
+extern "C" int fa_forward_split(const void* q, const void* k, const void* v, const void* bias,
+                                void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                                int64_t Nq, int64_t Nk, int64_t D, float scale, int causal,
+                                int dtype, int64_t num_splits, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+  int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
+  const int esz = elem_bytes(dtype);
+  st = check_split_sizes(B, Hq, Hkv, Nq, D, esz, num_splits);
+  if (st != FA_OK) return st;
+  const int64_t rows = B * Hq * Nq;
+  const int64_t need = fa::split_workspace_bytes(rows, D, num_splits);
+  if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)
+    return FA_ERR_WORKSPACE;
+  const uint64_t nq_b = uint64_t(rows) * D * esz;
+  const uint64_t nkv_b = uint64_t(B) * Hkv * Nk * D * esz;
+  const uint64_t nb_b = bias ? uint64_t(rows) * Nk * esz : 0;
+  const uint64_t nl_b = uint64_t(rows) * 4;
+  if (overlap(workspace, need, q, nq_b) || overlap(workspace, need, k, nkv_b) ||
+      overlap(workspace, need, v, nkv_b) || overlap(workspace, need, bias, nb_b) ||
+      overlap(workspace, need, o, nq_b) || overlap(workspace, need, lse, nl_b))
+    return FA_ERR_OVERLAP;
+  fa::LaunchArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.bias = bias;
+  a.o = o;
+  a.lse = lse;
+  a.B = int(B);
+  a.Hq = int(Hq);
+  a.Hkv = int(Hkv);
+  a.Nq = int(Nq);
+  a.Nk = int(Nk);
+  a.D = int(D);
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.stream = stream;
+  return fa::launch_forward_split(a, int(num_splits), workspace);
+}
+
+extern "C" int fa_merge(const float* part_o, const float* part_lse, int64_t num_parts,
+                        int64_t rows, int64_t D, void* o, float* lse, int dtype, void* stream) {
+  const int esz = elem_bytes(dtype);
+  if (esz == 0) return FA_ERR_DTYPE;
+  if (num_parts < 0 || rows < 0 || D < 0) return FA_ERR_BAD_SIZE;
+  if (D < 4 || D > 65536 || D % 4 != 0) return FA_ERR_HEAD_DIM;
+  if (rows == 0) return FA_OK;
+  if (o == nullptr || lse == nullptr) return FA_ERR_NULL_POINTER;
+  if (num_parts > 0 && (part_o == nullptr || part_lse == nullptr)) return FA_ERR_NULL_POINTER;
+  if (num_parts >= (int64_t(1) << 31) || __int128(num_parts) * rows * D >= (__int128(1) << 60) ||
+      __int128(rows) * D >= (__int128(1) << 60))
+    return FA_ERR_TOO_LARGE;
+  if (!aligned(part_o, 16) || !aligned(o, 16) || !aligned(part_lse, 4) || !aligned(lse, 4))
+    return FA_ERR_ALIGNMENT;
+  const uint64_t po_b = uint64_t(num_parts) * rows * D * 4, pl_b = uint64_t(num_parts) * rows * 4;
+  const uint64_t o_b = uint64_t(rows) * D * esz, l_b = uint64_t(rows) * 4;
+  if (overlap(o, o_b, part_o, po_b) || overlap(o, o_b, part_lse, pl_b) ||
+      overlap(o, o_b, lse, l_b) || overlap(lse, l_b, part_o, po_b) ||
+      overlap(lse, l_b, part_lse, pl_b))
+    return FA_ERR_OVERLAP;
+  return fa::launch_merge(part_o, part_lse, int(num_parts), rows, int(D), o, lse, dtype, stream);
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -112,8 +234,9 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_OVERLAP: return "o or lse overlaps another buffer";
     case FA_ERR_TOO_LARGE: return "a size exceeds the kernel's index range";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    case FA_ERR_WORKSPACE: return "the key-split workspace is NULL, too small or misaligned";
     default: return "unknown status";
   }
 }
 
-extern "C" const char* fa_version(void) { return "fa 0.1.0 gfx950"; }
+extern "C" const char* fa_version(void) { return "fa 0.2.0 gfx950"; }

@@ -153,6 +153,9 @@ struct Params {
   float c;       // |scale| * log2(e), never 0 (see the launcher)
   u32 q_sign;    // sign bits XORed into Q when scale < 0
   int bias_vec;  // bias rows allow 16-byte vector loads
+  // key-split path only: o and lse point at the fp32 partial outputs
+  int n_splits;       // key ranges per row block
+  int64_t part_rows;  // B * Hq * Nq, the row stride between splits
 };
 
 // Key position inside a V^T tile row.  Within each group of 16 keys the 4-key
@@ -195,11 +198,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS>
+// SPLIT = false: one workgroup per (batch, query head, 128-row block); O and
+// LSE are final.
+// SPLIT = true (key-split path): the query heads that share a KV head are
+// taken as one row space of group * Nq rows (rows r = (hq - hk*group)*Nq + i,
+// contiguous in Q, O, LSE and bias), one workgroup per (batch, KV head,
+// 128-row block, key range); it writes the normalised partial O (fp32) and
+// partial LSE of its key range, to be combined by fa_merge_kernel.
+template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT>
 __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_kernel(Params p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
   constexpr bool F32 = std::is_same<T, float>::value;
+  using OutT = typename std::conditional<SPLIT, float, T>::type;
+  constexpr bool OUT_F32 = F32 || SPLIT;
   constexpr int KP = E::KP;
   constexpr int KS = 2 * KP;         // contraction length of one MFMA
   constexpr int NS = D / KS;         // MFMAs per 32x32 score block
@@ -240,43 +252,91 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   //  * non-causal (all blocks equal): the ids one XCD receives are renumbered
   //    to be consecutive in head-major order, so the query blocks of a head
   //    run at the same time on one XCD and re-read K and V from its L2.
-  int bh, tile;
-  if (CAUSAL) {
-    bh = int(blockIdx.x % unsigned(p.BH));
-    const int rank = int(blockIdx.x / unsigned(p.BH));
-    const int half = (p.n_qtiles + 1) / 2;
-    tile = rank < half ? p.n_qtiles - 1 - rank : rank - half;
-  } else {
+  //  * key-split: the same head-major renumbering over (batch, KV head,
+  //    split, row block), so the row blocks that read one key range of a KV
+  //    head run together on one XCD.
+  int b, hk, tile, split = 0;
+  int64_t row_base;  // global index (over B*Hq*Nq) of row 0 of this row space
+  int n_rows;        // rows of this row space
+  if constexpr (SPLIT) {
     const unsigned nblk = gridDim.x, full = nblk & ~7u;
     unsigned logical = blockIdx.x;
     if (logical < full) logical = (logical & 7u) * (full >> 3) + (logical >> 3);
-    bh = int(logical / unsigned(p.n_qtiles));
     tile = int(logical % unsigned(p.n_qtiles));
+    const unsigned rest = logical / unsigned(p.n_qtiles);
+    split = int(rest % unsigned(p.n_splits));
+    const int bhk = int(rest / unsigned(p.n_splits));
+    b = bhk / p.Hkv;
+    hk = bhk - b * p.Hkv;
+    row_base = (int64_t(b) * p.Hq + int64_t(hk) * p.group) * p.Nq;
+    n_rows = p.group * p.Nq;
+  } else {
+    int bh;
+    if (CAUSAL) {
+      bh = int(blockIdx.x % unsigned(p.BH));
+      const int rank = int(blockIdx.x / unsigned(p.BH));
+      const int half = (p.n_qtiles + 1) / 2;
+      tile = rank < half ? p.n_qtiles - 1 - rank : rank - half;
+    } else {
+      const unsigned nblk = gridDim.x, full = nblk & ~7u;
+      unsigned logical = blockIdx.x;
+      if (logical < full) logical = (logical & 7u) * (full >> 3) + (logical >> 3);
+      bh = int(logical / unsigned(p.n_qtiles));
+      tile = int(logical % unsigned(p.n_qtiles));
+    }
+    b = bh / p.Hq;
+    hk = (bh - b * p.Hq) / p.group;
+    row_base = int64_t(bh) * p.Nq;
+    n_rows = p.Nq;
   }
-  const int b = bh / p.Hq, hq = bh - b * p.Hq, hk = hq / p.group;
   const int64_t kv_head = int64_t(b) * p.Hkv + hk;
+  const int64_t out_base = SPLIT ? row_base + int64_t(split) * p.part_rows : row_base;
 
-  const T* Qh = static_cast<const T*>(p.q) + int64_t(bh) * p.Nq * D;
+  const T* Qh = static_cast<const T*>(p.q) + row_base * D;
   const T* Kh = static_cast<const T*>(p.k) + kv_head * p.Nk * D;
   const T* Vh = static_cast<const T*>(p.v) + kv_head * p.Nk * D;
-  T* Oh = static_cast<T*>(p.o) + int64_t(bh) * p.Nq * D;
-  float* Lh = p.lse + int64_t(bh) * p.Nq;
-  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(Qh, uint32_t(p.Nq) * D * ESZ);
+  OutT* Oh = static_cast<OutT*>(p.o) + out_base * D;
+  float* Lh = p.lse + out_base;
+  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(Qh, uint32_t(n_rows) * D * ESZ);
   const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh, uint32_t(p.Nk) * D * ESZ);
   const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh, uint32_t(p.Nk) * D * ESZ);
   const float c = p.c;
 
   const int q_blk = tile * BM;
   const int wq0 = q_blk + wave * QW;      // first row of this wave
-  const bool wave_has_rows = wq0 < p.Nq;
-  const int wq_last = min(wq0 + QW, p.Nq) - 1;
-  const int blk_last = min(q_blk + BM, p.Nq) - 1;
+  const bool wave_has_rows = wq0 < n_rows;
+  const int wq_last = min(wq0 + QW, n_rows) - 1;
+  const int blk_last = min(q_blk + BM, n_rows) - 1;
   int qi[QB];                             // the row this lane owns in block qb
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) qi[qb] = wq0 + 32 * qb + ln;
 
+  // Causal query positions.  Without the key split a row is its position.
+  // With it, row r sits at position r % Nq; a run of rows [r0, r1] inside one
+  // head covers positions r0 % Nq .. r1 % Nq, and a run that crosses a head
+  // boundary is taken to cover 0 .. Nq-1 (a safe over-estimate).
+  auto pos_max = [&](int r0, int r1) {
+    if constexpr (!SPLIT) return r1;
+    return (r0 / p.Nq == r1 / p.Nq) ? r1 % p.Nq : p.Nq - 1;
+  };
+  auto pos_min = [&](int r0, int r1) {
+    if constexpr (!SPLIT) return r0;
+    return (r0 / p.Nq == r1 / p.Nq) ? r0 % p.Nq : 0;
+  };
+  int qpos[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) qpos[qb] = SPLIT ? qi[qb] % p.Nq : qi[qb];
+  const int wave_pos_max = pos_max(wq0, wq_last);
+
   int n_kv = (p.Nk + BN - 1) / BN;
-  if (CAUSAL) n_kv = min(n_kv, blk_last / BN + 1);
+  if (CAUSAL) n_kv = min(n_kv, pos_max(q_blk, blk_last) / BN + 1);
+  // Key tiles [j_begin, j_end) of this workgroup: all visible tiles, or the
+  // split's share of them (balanced, empty only when splits outnumber tiles).
+  int j_begin = 0, j_end = n_kv;
+  if constexpr (SPLIT) {
+    j_begin = int(int64_t(split) * n_kv / p.n_splits);
+    j_end = int(int64_t(split + 1) * n_kv / p.n_splits);
+  }
 
   // ---- Q fragments: B operand of S^T = K Q^T, loaded once ---------------------
   Frag qf[QB][NS];
@@ -302,7 +362,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   using BiasVec = typename std::conditional<F32, u32x4, u32x2>::type;
   BiasVec bcur[QB][NKB][4], bnext[QB][NKB][4];
   // (without a bias the resource is built over an empty range and never read)
-  const T* bblk = BIAS ? static_cast<const T*>(p.bias) + (int64_t(bh) * p.Nq + q_blk) * p.Nk
+  const T* bblk = BIAS ? static_cast<const T*>(p.bias) + (row_base + q_blk) * p.Nk
                        : static_cast<const T*>(p.q);
   const __amdgpu_buffer_rsrc_t b_rs =
       make_rsrc(bblk, BIAS ? uint32_t(blk_last - q_blk + 1) * uint32_t(p.Nk) * ESZ : 0u);
@@ -514,14 +574,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
             s[qb][kb][r] = fmaf(s[qb][kb][r], c, bias_at(qb, kb, r) * kLog2e);
       }
       const bool need_mask =
-          (key0 + BN > p.Nk) || (CAUSAL && key0 + BN - 1 > wq0 + 32 * qb);
+          (key0 + BN > p.Nk) ||
+          (CAUSAL && key0 + BN - 1 > pos_min(wq0 + 32 * qb, wq0 + 32 * qb + 31));
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool dead = key >= p.Nk || (CAUSAL && key > qi[qb]);
+            const bool dead = key >= p.Nk || (CAUSAL && key > qpos[qb]);
             if (dead) s[qb][kb][r] = -INFINITY;
           }
       }
@@ -606,19 +667,20 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   };
 
   // ---- main loop: double-buffered K/V tiles -------------------------------------
-  if (n_kv > 0) {
-    gload(0);
-    if constexpr (BIAS) load_bias(bcur, 0);
+  if (j_end > j_begin) {
+    gload(j_begin);
+    if constexpr (BIAS) load_bias(bcur, j_begin);
     sstore(0);
     __syncthreads();
   }
-  for (int j = 0; j < n_kv; ++j) {
-    const int cur = j & 1;
-    const bool has_next = j + 1 < n_kv;
+  for (int j = j_begin; j < j_end; ++j) {
+    const int cur = (j - j_begin) & 1;
+    const bool has_next = j + 1 < j_end;
     if (has_next) gload(j + 1);
-    const bool active = wave_has_rows && (!CAUSAL || j * BN <= wq_last);
+    const bool active = wave_has_rows && (!CAUSAL || j * BN <= wave_pos_max);
     if constexpr (BIAS) {
-      const bool next_active = has_next && wave_has_rows && (!CAUSAL || (j + 1) * BN <= wq_last);
+      const bool next_active =
+          has_next && wave_has_rows && (!CAUSAL || (j + 1) * BN <= wave_pos_max);
       if (next_active) load_bias(bnext, j + 1);
     }
     if (active) compute(j, cur);
@@ -635,9 +697,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 -----------------------------
+  // (key split: the same over the split's keys, O kept in fp32)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const bool row_ok = qi[qb] < p.Nq;
+    const bool row_ok = qi[qb] < n_rows;
     const float l_tot = partner_sum(l_run[qb]);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
     // Lane half g holds d = 8*q4 + 4*g + 0..3 of each 32-wide block.  One swap
@@ -654,8 +717,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
           a4[e] = acc[qb][db][8 * pr + e] * inv;
           b4[e] = acc[qb][db][8 * pr + 4 + e] * inv;
         }
-        T* dst = Oh + int64_t(qi[qb]) * D + db * 32 + 16 * pr + 8 * g;
-        if constexpr (F32) {
+        OutT* dst = Oh + int64_t(qi[qb]) * D + db * 32 + 16 * pr + 8 * g;
+        if constexpr (OUT_F32) {
           const u32x4 aw = __builtin_bit_cast(u32x4, a4), bw = __builtin_bit_cast(u32x4, b4);
           u32x4 ao, bo;
 #pragma unroll
@@ -687,48 +750,98 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   }
 }
 
-template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS>
+// ---------------------------------------------------------------------------
+// Merge of normalised partial results (key-split path, and fa_merge).
+// Row r of the result combines part_o[s][r][:] and part_lse[s][r] over the
+// parts s: with M = max_s LSE_s and w_s = e^(LSE_s - M), O = sum_s w_s O_s /
+// sum_s w_s and LSE = M + ln(sum_s w_s) -- the merge of the kwkr.cn tutorial,
+// §2.2, for normalised states (state (m, l, o) = (LSE_s, 1, O_s)).  A part
+// with LSE = -inf has weight 0 and its O is not read; with no finite part the
+// row gets O = 0 and LSE = -inf.
+// One thread per 4 output columns of a row; grid-stride over rows * D/4.
+// The partials are read once (HBM-bound); the LSE reads of a row hit the
+// same cache line from its D/4 threads.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ part_o,
+                                                       const float* __restrict__ part_lse,
+                                                       int n_parts, int64_t rows, int d4,
+                                                       T* __restrict__ o, float* __restrict__ lse) {
+  constexpr bool F32 = std::is_same<T, float>::value;
+  const int64_t total = rows * d4;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int64_t row = t / d4;
+    const int c4 = int(t - row * d4);
+    float m = -INFINITY;
+    for (int sp = 0; sp < n_parts; ++sp) m = fmaxf(m, part_lse[sp * rows + row]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+      for (int sp = 0; sp < n_parts; ++sp) {
+        const float ls = part_lse[sp * rows + row];
+        if (ls == -INFINITY) continue;
+        const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
+        const f32x4 x =
+            *reinterpret_cast<const f32x4*>(part_o + (sp * rows + row) * int64_t(4 * d4) + 4 * c4);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= inv;
+    T* dst = o + row * int64_t(4 * d4) + 4 * c4;
+    if constexpr (F32) {
+      *reinterpret_cast<f32x4*>(dst) = acc;
+    } else {
+      *reinterpret_cast<u32x2*>(dst) = Elem<T>::narrow4(acc);
+    }
+    if (c4 == 0) lse[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+  }
+}
+
+template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT>
 hipError_t launch_one(const Params& p, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&p)};
   return hipLaunchKernel(
-      reinterpret_cast<const void*>(&fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS>), dim3(grid),
-      dim3(kThreads), args, 0, stream);
+      reinterpret_cast<const void*>(&fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT>),
+      dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
-template <typename T, int D, int BN, int QB>
+template <typename T, int D, int BN, int QB, bool SPLIT>
 hipError_t launch_d(const Params& p, unsigned grid, hipStream_t s, bool causal, bool bias) {
   if (causal) {
-    return bias ? launch_one<T, D, BN, QB, true, true>(p, grid, s)
-                : launch_one<T, D, BN, QB, true, false>(p, grid, s);
+    return bias ? launch_one<T, D, BN, QB, true, true, SPLIT>(p, grid, s)
+                : launch_one<T, D, BN, QB, true, false, SPLIT>(p, grid, s);
   }
-  return bias ? launch_one<T, D, BN, QB, false, true>(p, grid, s)
-              : launch_one<T, D, BN, QB, false, false>(p, grid, s);
+  return bias ? launch_one<T, D, BN, QB, false, true, SPLIT>(p, grid, s)
+              : launch_one<T, D, BN, QB, false, false, SPLIT>(p, grid, s);
 }
 
 // 32-row query blocks per wave.  Two blocks (64 rows) halve the K/V operand
 // reads per MFMA, but only fit in registers for 16-bit inputs with D = 64 and
-// no bias tile; every other instance keeps one.
-constexpr int query_blocks(int dtype, int D, bool bias) {
-  return (dtype != FA_DTYPE_FP32 && D == 64 && !bias) ? kQB64 : (D == 64 ? 1 : kQB128);
+// no bias tile; every other instance keeps one.  The key-split path keeps one.
+constexpr int query_blocks(int dtype, int D, bool bias, bool split) {
+  return split ? 1 : (dtype != FA_DTYPE_FP32 && D == 64 && !bias) ? kQB64 : (D == 64 ? 1 : kQB128);
 }
 
-template <typename T>
+template <typename T, bool SPLIT>
 hipError_t launch_t(const Params& p, unsigned grid, hipStream_t s, int D, bool causal, bool bias) {
   if (D == 64) {
-    if constexpr (!std::is_same<T, float>::value) {
+    if constexpr (!std::is_same<T, float>::value && !SPLIT) {
       if (!bias) {
-        return causal ? launch_one<T, 64, kBN64, kQB64, true, false>(p, grid, s)
-                      : launch_one<T, 64, kBN64, kQB64, false, false>(p, grid, s);
+        return causal ? launch_one<T, 64, kBN64, kQB64, true, false, false>(p, grid, s)
+                      : launch_one<T, 64, kBN64, kQB64, false, false, false>(p, grid, s);
       }
     }
-    return launch_d<T, 64, kBN64, 1>(p, grid, s, causal, bias);
+    return launch_d<T, 64, kBN64, 1, SPLIT>(p, grid, s, causal, bias);
   }
-  return launch_d<T, 128, kBN128, kQB128>(p, grid, s, causal, bias);
+  return launch_d<T, 128, kBN128, SPLIT ? 1 : kQB128, SPLIT>(p, grid, s, causal, bias);
 }
 
-}  // namespace
-
-int launch_forward(const LaunchArgs& a) {
+Params make_params(const LaunchArgs& a, int rows_per_block, int n_rows) {
   Params p;
   p.q = a.q;
   p.k = a.k;
@@ -742,8 +855,7 @@ int launch_forward(const LaunchArgs& a) {
   p.Nk = a.Nk;
   p.BH = a.B * a.Hq;
   p.group = a.Hq / a.Hkv;
-  const int bm = kWaves * 32 * query_blocks(a.dtype, a.D, a.bias != nullptr);
-  p.n_qtiles = (a.Nq + bm - 1) / bm;
+  p.n_qtiles = (n_rows + rows_per_block - 1) / rows_per_block;
   // The kernel folds the scale into base-2 exponents and needs a positive
   // factor: a negative scale is realised by flipping the sign of Q (exact), and
   // a zero (or vanishing) one by a factor so small that every finite logit
@@ -754,16 +866,81 @@ int launch_forward(const LaunchArgs& a) {
   const bool neg = a.scale < 0.f;
   p.q_sign = !neg ? 0u : (a.dtype == FA_DTYPE_FP32 ? 0x80000000u : 0x80008000u);
   p.bias_vec = (a.dtype == FA_DTYPE_FP32) ? (a.Nk % 4) == 0 : (a.Nk % 8) == 0;
-  const unsigned grid = unsigned(p.n_qtiles) * unsigned(p.BH);
+  p.n_splits = 1;
+  p.part_rows = 0;
+  return p;
+}
+
+template <bool SPLIT>
+hipError_t dispatch(const Params& p, unsigned grid, const LaunchArgs& a) {
   hipStream_t s = static_cast<hipStream_t>(a.stream);
   const bool bias = a.bias != nullptr;
-  hipError_t err;
   switch (a.dtype) {
-    case FA_DTYPE_BF16: err = launch_t<__bf16>(p, grid, s, a.D, a.causal, bias); break;
-    case FA_DTYPE_FP16: err = launch_t<_Float16>(p, grid, s, a.D, a.causal, bias); break;
-    default: err = launch_t<float>(p, grid, s, a.D, a.causal, bias); break;
+    case FA_DTYPE_BF16: return launch_t<__bf16, SPLIT>(p, grid, s, a.D, a.causal, bias);
+    case FA_DTYPE_FP16: return launch_t<_Float16, SPLIT>(p, grid, s, a.D, a.causal, bias);
+    default: return launch_t<float, SPLIT>(p, grid, s, a.D, a.causal, bias);
   }
-  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+hipError_t merge(const float* part_o, const float* part_lse, int n_parts, int64_t rows, int D,
+                 void* o, float* lse, int dtype, hipStream_t s) {
+  const int d4 = D / 4;
+  const int64_t total = rows * d4;
+  // enough waves to keep HBM busy; the kernel strides over the rest
+  const int64_t want = (total + 255) / 256;
+  const unsigned grid = unsigned(want < 8192 ? want : 8192);
+  switch (dtype) {
+    case FA_DTYPE_BF16:
+      fa_merge_kernel<__bf16><<<grid, 256, 0, s>>>(part_o, part_lse, n_parts, rows, d4,
+                                                   static_cast<__bf16*>(o), lse);
+      break;
+    case FA_DTYPE_FP16:
+      fa_merge_kernel<_Float16><<<grid, 256, 0, s>>>(part_o, part_lse, n_parts, rows, d4,
+                                                     static_cast<_Float16*>(o), lse);
+      break;
+    default:
+      fa_merge_kernel<float><<<grid, 256, 0, s>>>(part_o, part_lse, n_parts, rows, d4,
+                                                  static_cast<float*>(o), lse);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_forward(const LaunchArgs& a) {
+  const int bm = kWaves * 32 * query_blocks(a.dtype, a.D, a.bias != nullptr, false);
+  const Params p = make_params(a, bm, a.Nq);
+  const unsigned grid = unsigned(p.n_qtiles) * unsigned(p.BH);
+  return dispatch<false>(p, grid, a) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int launch_forward_split(const LaunchArgs& a, int n_splits, void* workspace) {
+  const int group = a.Hq / a.Hkv;
+  const int64_t part_rows = int64_t(a.B) * a.Hq * a.Nq;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             split_partial_o_bytes(part_rows, a.D, n_splits));
+  LaunchArgs pa = a;
+  pa.o = part_o;
+  pa.lse = part_lse;
+  Params p = make_params(pa, kWaves * 32, group * a.Nq);
+  p.n_splits = n_splits;
+  p.part_rows = part_rows;
+  const unsigned grid = unsigned(p.n_qtiles) * unsigned(n_splits) * unsigned(a.B * a.Hkv);
+  if (dispatch<true>(p, grid, pa) != hipSuccess) return FA_ERR_HIP;
+  return merge(part_o, part_lse, n_splits, part_rows, a.D, a.o, a.lse, a.dtype,
+               static_cast<hipStream_t>(a.stream)) == hipSuccess
+             ? FA_OK
+             : FA_ERR_HIP;
+}
+
+int launch_merge(const float* part_o, const float* part_lse, int n_parts, int64_t rows, int D,
+                 void* o, float* lse, int dtype, void* stream) {
+  return merge(part_o, part_lse, n_parts, rows, D, o, lse, dtype,
+               static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FA_OK
+             : FA_ERR_HIP;
 }
 
 }  // namespace fa

@@ -23,6 +23,27 @@ struct LaunchArgs {
 // Arguments are already validated.  Returns FA_OK or FA_ERR_HIP.
 int launch_forward(const LaunchArgs& a);
 
+// Key-split forward: partials into `workspace` (layout below), then the merge
+// into a.o / a.lse, both on a.stream.  Arguments are already validated.
+int launch_forward_split(const LaunchArgs& a, int n_splits, void* workspace);
+
+// Merge of n_parts normalised partials: part_o [n_parts][rows][D] fp32,
+// part_lse [n_parts][rows] -> o [rows][D] (dtype), lse [rows].  Validated.
+int launch_merge(const float* part_o, const float* part_lse, int n_parts, int64_t rows, int D,
+                 void* o, float* lse, int dtype, void* stream);
+
+// Workspace of the key-split forward: partial O, fp32 [splits][rows][D], then
+// partial LSE, fp32 [splits][rows], starting at the next 256-byte boundary.
+inline int64_t split_partial_o_bytes(int64_t rows, int64_t D, int64_t splits) {
+  return (splits * rows * D * 4 + 255) / 256 * 256;
+}
+inline int64_t split_workspace_bytes(int64_t rows, int64_t D, int64_t splits) {
+  return split_partial_o_bytes(rows, D, splits) + splits * rows * 4;
+}
+
+// Largest key-split count accepted.
+constexpr int kMaxSplits = 1024;
+
 // Query rows per workgroup of the forward kernel (the grid-size limit depends on it).
 constexpr int kRowsPerBlock = 128;
 

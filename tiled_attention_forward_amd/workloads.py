@@ -16,6 +16,12 @@ Day 26 post (B=2, H=16, S=512, D=64 fp16), its benchmark report shape (B=2,
 H=16, S=4096, D=64 bf16 causal), the S/P size example of the kwkr.cn tutorial
 (B=8, H=32, N=2048, D=128), and the GQA 20 query / 4 KV head setup of the Block
 Attention Residual post with a dense pre-softmax logit term.
+
+Two more shapes exercise the key-split path, where row blocks alone leave most
+of the 256 compute units idle; the pages give no such benchmark, so they are
+synthetic choices: one decode step (Nq = 1) of the same 20/4-head, D = 128
+setup for 8 sequences over a 32768-entry KV cache, and a long sequence with
+only two heads (B = 1, H = 2, S = 16384, D = 64, 256 row blocks).
 """
 
 from __future__ import annotations
@@ -40,6 +46,7 @@ class Workload:
     dtype: str
     causal: bool
     bias: bool
+    path: str = "fused"   # "fused": fa_forward; "split": fa_forward_split
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -88,6 +95,10 @@ WORKLOADS = {
         Workload("b8_h32_s2048_d128_bf16", 8, 32, 32, 2048, 2048, 128, "bf16", False, False),
         Workload("b1_hq20_hkv4_s8192_d128_bf16_causal_bias", 1, 20, 4, 8192, 8192, 128, "bf16",
                  True, True),
+        Workload("decode_b8_hq20_hkv4_nq1_nk32768_d128_bf16", 8, 20, 4, 1, 32768, 128, "bf16",
+                 False, False, "split"),
+        Workload("b1_h2_s16384_d64_bf16", 1, 2, 2, 16384, 16384, 64, "bf16", False, False,
+                 "split"),
     ]
 }
 
