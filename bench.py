@@ -26,6 +26,7 @@ cpu_baseline = the fp64 oracle, timed on the host on a bounded sample of the
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -54,6 +55,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--path", choices=["fused", "split"], default=None,
+                    help="entry point to time (default: the workload's own)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="key splits for the split path (default: the library's suggestion)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time for the oracle sample")
@@ -135,6 +140,8 @@ def main():
     from tiled_attention_forward_amd.workloads import HEADLINE, WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload or HEADLINE]
+    if args.path is not None and args.path != w.path:
+        w = dataclasses.replace(w, path=args.path)
     dev = torch.device("cuda:0")
     lib = binding.load_library()
     q, k, v, bias = make_inputs(w, seed=args.seed, device=dev)
@@ -147,7 +154,7 @@ def main():
                  w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal), dtype_code)
     splits = None
     if w.path == "split":
-        splits = binding.fa_split_count(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D)
+        splits = args.splits or binding.fa_split_count(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D)
         ws_bytes = binding.fa_split_workspace_bytes(w.B, w.Hq, w.Nq, w.D, splits)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         entry = lib.fa_forward_split

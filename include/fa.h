@@ -151,9 +151,9 @@ int fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D,
 
 /*
  * The split count the library suggests for a problem, through *num_splits
- * (pure host code).  It aims for about 1024 workgroups (four per compute
- * unit of the 256) while keeping at least four 64-key tiles per split; 1 when
- * the row blocks alone reach that.  Same size errors as
+ * (pure host code).  It aims for about 512 workgroups (two per compute unit
+ * of the 256, the number resident at once) while keeping at least four
+ * 64-key tiles per split; 1 when the row blocks alone reach that.  Same size errors as
  * fa_split_workspace_bytes, plus FA_ERR_HEAD_GROUPS.
  */
 int fa_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,

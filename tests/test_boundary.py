@@ -160,14 +160,16 @@ def test_split_workspace_bytes_layout():
 
 def test_split_count_heuristic():
     # decode step: 8 batches x 4 KV heads, 5 query heads per group, Nq = 1, 32768 keys:
-    # 32 row blocks -> 32 splits of 16 tiles each
-    assert binding.fa_split_count(8, 20, 4, 1, 32768, 128) == 32
+    # 32 row blocks -> 16 splits of 32 tiles each (512 workgroups)
+    assert binding.fa_split_count(8, 20, 4, 1, 32768, 128) == 16
+    # two heads of 16384 rows: 256 row blocks -> 2 splits
+    assert binding.fa_split_count(1, 2, 2, 16384, 16384, 64) == 2
     # enough row blocks already: 2 x 16 heads x 32 blocks of 128 rows
     assert binding.fa_split_count(2, 16, 16, 4096, 4096, 64) == 1
     # few keys: at least 4 tiles per split
     assert binding.fa_split_count(1, 1, 1, 1, 64 * 8, 64) == 2
     assert binding.fa_split_count(1, 1, 1, 1, 10, 64) == 1
-    assert binding.fa_split_count(1, 1, 1, 1, 1 << 24, 64) == 1024
+    assert binding.fa_split_count(1, 1, 1, 1, 1 << 24, 64) == 512
     assert binding.fa_split_count(0, 1, 1, 1, 100, 64) == 1
     with pytest.raises(binding.FaError):
         binding.fa_split_count(1, 5, 2, 1, 100, 64)

@@ -139,10 +139,11 @@ extern "C" int fa_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, in
   if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
   const int64_t lim = int64_t(1) << 30;
   if (B >= lim || Hq >= lim || Nq >= lim || Nk >= lim) return FA_ERR_TOO_LARGE;
-  // About 1024 workgroups: four per compute unit, enough to keep every CU busy
-  // through the tail of the grid; each split keeps at least 4 key tiles so the
-  // partials stay a small fraction of the traffic.
-  constexpr int64_t kTargetBlocks = 1024;
+  // About 512 workgroups: two per compute unit, as many as are resident at
+  // once (register and LDS limits of the forward kernel), so the grid runs in
+  // one round; each split keeps at least 4 key tiles so the partials stay a
+  // small fraction of the traffic.
+  constexpr int64_t kTargetBlocks = 512;
   const __int128 rows = __int128(Hq / Hkv) * Nq;
   const __int128 units = __int128(B) * Hkv * ((rows + fa::kRowsPerBlock - 1) / fa::kRowsPerBlock);
   if (units >= kTargetBlocks) return FA_OK;

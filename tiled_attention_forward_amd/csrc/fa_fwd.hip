@@ -758,47 +758,88 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
 // §2.2, for normalised states (state (m, l, o) = (LSE_s, 1, O_s)).  A part
 // with LSE = -inf has weight 0 and its O is not read; with no finite part the
 // row gets O = 0 and LSE = -inf.
-// One thread per 4 output columns of a row; grid-stride over rows * D/4.
-// The partials are read once (HBM-bound); the LSE reads of a row hit the
-// same cache line from its D/4 threads.
+//
+// Layout: the output is a flat list of rows * D/4 items (a row and 4 of its
+// columns).  A workgroup takes 64 consecutive items, one per lane, and its 4
+// waves split the parts between them (wave w folds parts w, w+4, ...), so the
+// loads of different parts are independent and many are in flight at once.
+// Each wave's state (M_w, sum of weights, weighted sum) goes through LDS and
+// wave 0 merges the four the same way.  HBM-bound: every partial is read once.
 // ---------------------------------------------------------------------------
+constexpr int kMergeWaves = 4;
+
 template <typename T>
-__global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ part_o,
-                                                       const float* __restrict__ part_lse,
-                                                       int n_parts, int64_t rows, int d4,
-                                                       T* __restrict__ o, float* __restrict__ lse) {
+__global__ __launch_bounds__(kMergeWaves * 64) void fa_merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, int n_parts,
+    int64_t rows, int d4, T* __restrict__ o, float* __restrict__ lse) {
   constexpr bool F32 = std::is_same<T, float>::value;
+  __shared__ float s_m[kMergeWaves][64];
+  __shared__ float s_w[kMergeWaves][64];
+  __shared__ f32x4 s_a[kMergeWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t total = rows * d4;
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < total; t += stride) {
-    const int64_t row = t / d4;
-    const int c4 = int(t - row * d4);
+  const int64_t D = int64_t(4) * d4;
+  for (int64_t base = int64_t(blockIdx.x) * 64; base < total; base += int64_t(gridDim.x) * 64) {
+    const int64_t t = base + lane;
+    const bool ok = t < total;
+    const int64_t row = ok ? t / d4 : 0;
+    const int c4 = ok ? int(t - row * d4) : 0;
+    // this wave's parts: max LSE, then weights and the weighted sum
     float m = -INFINITY;
-    for (int sp = 0; sp < n_parts; ++sp) m = fmaxf(m, part_lse[sp * rows + row]);
+    if (ok) {
+#pragma unroll 8
+      for (int sp = wave; sp < n_parts; sp += kMergeWaves)
+        m = fmaxf(m, part_lse[sp * rows + row]);
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    if (m != -INFINITY) {
-      for (int sp = 0; sp < n_parts; ++sp) {
+    if (ok && m != -INFINITY) {
+#pragma unroll 4
+      for (int sp = wave; sp < n_parts; sp += kMergeWaves) {
         const float ls = part_lse[sp * rows + row];
-        if (ls == -INFINITY) continue;
-        const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
-        const f32x4 x =
-            *reinterpret_cast<const f32x4*>(part_o + (sp * rows + row) * int64_t(4 * d4) + 4 * c4);
-        wsum += w;
+        if (ls != -INFINITY) {
+          const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
+          const f32x4 x = *reinterpret_cast<const f32x4*>(part_o + (sp * rows + row) * D + 4 * c4);
+          wsum += w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+          for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+        }
       }
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    s_m[wave][lane] = m;
+    s_w[wave][lane] = wsum;
+    s_a[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && ok) {
+      float mt = s_m[0][lane];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] *= inv;
-    T* dst = o + row * int64_t(4 * d4) + 4 * c4;
-    if constexpr (F32) {
-      *reinterpret_cast<f32x4*>(dst) = acc;
-    } else {
-      *reinterpret_cast<u32x2*>(dst) = Elem<T>::narrow4(acc);
+      for (int g = 1; g < kMergeWaves; ++g) mt = fmaxf(mt, s_m[g][lane]);
+      f32x4 at = {0.f, 0.f, 0.f, 0.f};
+      float wt = 0.f;
+      if (mt != -INFINITY) {
+#pragma unroll
+        for (int g = 0; g < kMergeWaves; ++g) {
+          const float mg = s_m[g][lane];
+          if (mg == -INFINITY) continue;
+          const float f = __builtin_amdgcn_exp2f((mg - mt) * kLog2e);
+          const f32x4 ag = s_a[g][lane];
+          wt = fmaf(f, s_w[g][lane], wt);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) at[e] = fmaf(f, ag[e], at[e]);
+        }
+      }
+      const float inv = wt > 0.f ? 1.f / wt : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) at[e] *= inv;
+      T* dst = o + row * D + 4 * c4;
+      if constexpr (F32) {
+        *reinterpret_cast<f32x4*>(dst) = at;
+      } else {
+        *reinterpret_cast<u32x2*>(dst) = Elem<T>::narrow4(at);
+      }
+      if (c4 == 0) lse[row] = wt > 0.f ? mt + logf(wt) : -INFINITY;
     }
-    if (c4 == 0) lse[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+    __syncthreads();
   }
 }
 
@@ -886,21 +927,22 @@ hipError_t merge(const float* part_o, const float* part_lse, int n_parts, int64_
                  void* o, float* lse, int dtype, hipStream_t s) {
   const int d4 = D / 4;
   const int64_t total = rows * d4;
-  // enough waves to keep HBM busy; the kernel strides over the rest
-  const int64_t want = (total + 255) / 256;
-  const unsigned grid = unsigned(want < 8192 ? want : 8192);
+  // one workgroup per 64 items, up to 64 per CU; the kernel strides over the rest
+  const int64_t want = (total + 63) / 64;
+  const unsigned grid = unsigned(want < 16384 ? want : 16384);
+  const dim3 block(kMergeWaves * 64);
   switch (dtype) {
     case FA_DTYPE_BF16:
-      fa_merge_kernel<__bf16><<<grid, 256, 0, s>>>(part_o, part_lse, n_parts, rows, d4,
-                                                   static_cast<__bf16*>(o), lse);
+      fa_merge_kernel<__bf16><<<grid, block, 0, s>>>(part_o, part_lse, n_parts, rows, d4,
+                                                     static_cast<__bf16*>(o), lse);
       break;
     case FA_DTYPE_FP16:
-      fa_merge_kernel<_Float16><<<grid, 256, 0, s>>>(part_o, part_lse, n_parts, rows, d4,
-                                                     static_cast<_Float16*>(o), lse);
+      fa_merge_kernel<_Float16><<<grid, block, 0, s>>>(part_o, part_lse, n_parts, rows, d4,
+                                                       static_cast<_Float16*>(o), lse);
       break;
     default:
-      fa_merge_kernel<float><<<grid, 256, 0, s>>>(part_o, part_lse, n_parts, rows, d4,
-                                                  static_cast<float*>(o), lse);
+      fa_merge_kernel<float><<<grid, block, 0, s>>>(part_o, part_lse, n_parts, rows, d4,
+                                                    static_cast<float*>(o), lse);
       break;
   }
   return hipGetLastError();
