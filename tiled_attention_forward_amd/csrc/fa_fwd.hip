@@ -58,6 +58,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 4;              // waves per workgroup
 constexpr int kThreads = kWaves * 64;
@@ -217,10 +219,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   constexpr int NS = D / KS;         // MFMAs per 32x32 score block
   constexpr int ESZ = sizeof(T);
   constexpr int VEC = 16 / ESZ;      // elements per 16-byte vector
+  // 16-bit types keep V row-major in LDS, like K, and read the MFMA operand
+  // transposed with ds_read_b64_tr_b16; fp32 stores V transposed (V^T).
+  constexpr bool VTR = !F32;
   constexpr int KSTR = D + VEC;      // K tile row stride, elements
-  constexpr int VSTR = BN + VEC;     // V^T tile row stride, elements
+  constexpr int VSTR = BN + VEC;     // V^T tile row stride, elements (fp32)
+  constexpr int VRSTR = D + 2 * VEC; // V tile row stride, elements (16-bit types)
   constexpr int KT = BN * KSTR;      // elements per K buffer
-  constexpr int VT = D * VSTR;       // elements per V^T buffer
+  constexpr int VT = VTR ? BN * VRSTR : D * VSTR;  // elements per V buffer
   constexpr int NKB = BN / 32;       // 32-key blocks per tile
   constexpr int NDB = D / 32;        // 32-wide column blocks of the output
   constexpr int QW = 32 * QB;        // query rows per wave
@@ -235,6 +241,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, ln = lane & 31;
+  // Transposed V reads (ds_read_b64_tr_b16): within each 16-lane group, lane
+  // 4a+b receives element b of the 8-byte chunks read by lanes a, a+4, a+8,
+  // a+12.  So lane s of the group reads row (4g + s/4) of the key group, at
+  // column 16*(lane/16 % 2) + 4*(s % 4); lane s then holds 4 consecutive keys
+  // of column lane % 32.
+  const int tr_off = (4 * g + ((lane >> 2) & 3)) * VRSTR + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // Workgroup -> (head, query block).  Consecutive ids walk the heads, so
   // with B*Hq a multiple of 8 all blocks of a head share one XCD (ids are
@@ -456,7 +468,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
 
   // ---- K/V staging through registers -------------------------------------------
   u32x4 kreg[KCH];
-  u32x4 vreg[VTPT][4];
+  u32x4 vreg[VTR ? 1 : VTPT][4];   // V^T path: 4 keys x VEC columns per task
+  u32x4 vrow[VTR ? KCH : 1];       // row-major path: same split as K
 
   auto gload = [&](int j) {
     const int key0 = j * BN;
@@ -466,15 +479,24 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
       const int row = cidx / (D / VEC), col = (cidx % (D / VEC)) * VEC;
       kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(k_rs, ((key0 + row) * D + col) * ESZ, 0, 0);
     }
+    if constexpr (VTR) {
 #pragma unroll
-    for (int i = 0; i < VTPT; ++i) {
-      const int t = tid + i * kThreads;
-      const int kg = t % (BN / 4), dc = t / (BN / 4);
-      if (VTASKS % kThreads == 0 || t < VTASKS) {
+      for (int i = 0; i < KCH; ++i) {
+        const int cidx = tid + i * kThreads;
+        const int row = cidx / (D / VEC), col = (cidx % (D / VEC)) * VEC;
+        vrow[i] = __builtin_amdgcn_raw_buffer_load_b128(v_rs, ((key0 + row) * D + col) * ESZ, 0, 0);
+      }
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          vreg[i][r] = __builtin_amdgcn_raw_buffer_load_b128(
-              v_rs, ((key0 + kg * 4 + r) * D + dc * VEC) * ESZ, 0, 0);
+      for (int i = 0; i < VTPT; ++i) {
+        const int t = tid + i * kThreads;
+        const int kg = t % (BN / 4), dc = t / (BN / 4);
+        if (VTASKS % kThreads == 0 || t < VTASKS) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            vreg[i][r] = __builtin_amdgcn_raw_buffer_load_b128(
+                v_rs, ((key0 + kg * 4 + r) * D + dc * VEC) * ESZ, 0, 0);
+          }
         }
       }
     }
@@ -488,6 +510,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
       const int cidx = tid + i * kThreads;
       const int row = cidx / (D / VEC), col = (cidx % (D / VEC)) * VEC;
       *reinterpret_cast<u32x4*>(sK + row * KSTR + col) = kreg[i];
+    }
+    if constexpr (VTR) {
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) {
+        const int cidx = tid + i * kThreads;
+        const int row = cidx / (D / VEC), col = (cidx % (D / VEC)) * VEC;
+        *reinterpret_cast<u32x4*>(sV + row * VRSTR + col) = vrow[i];
+      }
+      return;
     }
 #pragma unroll
     for (int i = 0; i < VTPT; ++i) {
@@ -656,8 +687,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
           }
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const T* src = sV + (db * 32 + ln) * VSTR + kb * 32 + 16 * h + 8 * g;
-            const Frag vf = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(src));
+            // The 8 keys lane half g feeds this MFMA are k16+4g+0..3, then
+            // k16+4g+8..11 (k16 = first key of the 16-key group), the order
+            // the S^T registers hold P in.  Each transposed read gives every
+            // lane 4 consecutive keys of its column d = 32*db + lane%32.
+            const T* src = sV + (kb * 32 + 16 * h) * VRSTR + db * 32 + tr_off;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 8 * VRSTR));
+            const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
+            const Frag vf = __builtin_bit_cast(Frag, u32x4{lw[0], lw[1], hw[0], hw[1]});
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) acc[qb][db] = E::mma(vf, pf[qb], acc[qb][db]);
           }
