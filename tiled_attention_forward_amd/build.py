@@ -65,8 +65,24 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
+        check_no_undefined_kernels(tmp_lib)
         os.replace(tmp_lib, LIB)
     return LIB
+
+
+def check_no_undefined_kernels(path: str) -> None:
+    """Refuse a library that references a kernel it does not define.
+
+    The host pass of hipcc can drop a kernel template instance without any
+    diagnostic (seen with a non-constant signed offset passed to an LDS-load
+    builtin); the library then links but fails to load.
+    """
+    res = subprocess.run(["nm", "-D", "--undefined-only", path], capture_output=True, text=True)
+    if res.returncode != 0:
+        return  # nm unavailable: the load in the tests still catches it
+    missing = [l.split()[-1] for l in res.stdout.splitlines() if "_ZN2fa" in l]
+    if missing:
+        raise RuntimeError("libfa.so references undefined kernels:\n  " + "\n  ".join(missing))
 
 
 if __name__ == "__main__":

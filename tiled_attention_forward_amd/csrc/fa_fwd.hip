@@ -60,6 +60,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;              // waves per workgroup
 constexpr int kThreads = kWaves * 64;
@@ -87,6 +88,10 @@ static_assert(kWaves * 32 >= kRowsPerBlock,
               "grid-size validation assumes at least this block height");
 
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt = 0 only: vector
+// memory counter bits [3:0] and [15:14] zero, expcnt [6:4] and lgkmcnt [11:8]
+// at their maxima (no wait).
+constexpr int kWaitVmem0 = 0x0F70;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
@@ -219,14 +224,20 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   constexpr int NS = D / KS;         // MFMAs per 32x32 score block
   constexpr int ESZ = sizeof(T);
   constexpr int VEC = 16 / ESZ;      // elements per 16-byte vector
-  // 16-bit types keep V row-major in LDS, like K, and read the MFMA operand
-  // transposed with ds_read_b64_tr_b16; fp32 stores V transposed (V^T).
+  // 16-bit types: K and V tiles go from HBM straight into LDS (buffer loads
+  // with the LDS flag), row-major and unpadded, 16-byte chunks XOR-swizzled
+  // per row against bank conflicts; the P.V operand is read from V with
+  // ds_read_b64_tr_b16.  fp32: staged through registers, K padded, V stored
+  // transposed (V^T).
   constexpr bool VTR = !F32;
-  constexpr int KSTR = D + VEC;      // K tile row stride, elements
-  constexpr int VSTR = BN + VEC;     // V^T tile row stride, elements (fp32)
-  constexpr int VRSTR = D + 2 * VEC; // V tile row stride, elements (16-bit types)
-  constexpr int KT = BN * KSTR;      // elements per K buffer
-  constexpr int VT = VTR ? BN * VRSTR : D * VSTR;  // elements per V buffer
+  constexpr int KSTR = D + VEC;      // fp32: K tile row stride, elements
+  constexpr int VSTR = BN + VEC;     // fp32: V^T tile row stride, elements
+  constexpr int RB = D * ESZ;        // 16-bit: bytes per K/V tile row
+  constexpr int CPR = D / VEC;       // 16-byte chunks per row
+  constexpr int KT = VTR ? BN * D : BN * KSTR;   // elements per K buffer
+  constexpr int VT = VTR ? BN * D : D * VSTR;    // elements per V buffer
+  constexpr int DNI = VTR ? BN * CPR / (64 * kWaves) : 1;  // LDS loads per wave per matrix
+  static_assert(!VTR || DNI * 64 * kWaves == BN * CPR, "tile must split into whole wave loads");
   constexpr int NKB = BN / 32;       // 32-key blocks per tile
   constexpr int NDB = D / 32;        // 32-wide column blocks of the output
   constexpr int QW = 32 * QB;        // query rows per wave
@@ -241,12 +252,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, ln = lane & 31;
-  // Transposed V reads (ds_read_b64_tr_b16): within each 16-lane group, lane
-  // 4a+b receives element b of the 8-byte chunks read by lanes a, a+4, a+8,
-  // a+12.  So lane s of the group reads row (4g + s/4) of the key group, at
-  // column 16*(lane/16 % 2) + 4*(s % 4); lane s then holds 4 consecutive keys
-  // of column lane % 32.
-  const int tr_off = (4 * g + ((lane >> 2) & 3)) * VRSTR + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // Workgroup -> (head, query block).  Consecutive ids walk the heads, so
   // with B*Hq a multiple of 8 all blocks of a head share one XCD (ids are
@@ -467,11 +472,61 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   };
 
   // ---- K/V staging through registers -------------------------------------------
-  u32x4 kreg[KCH];
-  u32x4 vreg[VTR ? 1 : VTPT][4];   // V^T path: 4 keys x VEC columns per task
-  u32x4 vrow[VTR ? KCH : 1];       // row-major path: same split as K
+  u32x4 kreg[VTR ? 1 : KCH];
+  u32x4 vreg[VTR ? 1 : VTPT][4];   // fp32 V^T path: 4 keys x VEC columns per task
 
+  // 16-bit layout.  Chunk c (16 bytes) of tile row r sits at chunk
+  // c ^ (r & 7) of the row in K and at chunk c ^ 2*(r & 3) in V, so that the
+  // 8 rows one ds_read_b128 of K serves per cycle, and the 4 rows of each
+  // 16-lane group of a transposed V read, fall in distinct banks.
+  // Direct loads: load i of wave w fills LDS bytes [1 KB * (w*DNI + i), +1 KB)
+  // of each buffer, lane l the 16 bytes at l*16; the lane's source offset
+  // (without the tile's first key) is precomputed.
+  int dma_k[DNI], dma_v[DNI];
+#pragma unroll
+  for (int i = 0; i < DNI; ++i) {
+    const int q = (wave * DNI + i) * 64 + lane;   // physical chunk index in the tile
+    const int row = q / CPR, pc = q % CPR;
+    dma_k[i] = (row * D + (pc ^ (row & 7)) * VEC) * ESZ;
+    dma_v[i] = (row * D + (pc ^ ((row & 3) << 1)) * VEC) * ESZ;
+  }
+  // K operand reads: lane (row ln of a 32-key block, lane half g) reads
+  // logical chunk 2*st + g.
+  int k_off[VTR ? NS : 1];
+#pragma unroll
+  for (int st = 0; st < (VTR ? NS : 1); ++st)
+    k_off[st] = ln * RB + (((2 * st + g) ^ (ln & 7)) * 16);
+  // Transposed V reads (ds_read_b64_tr_b16): within each 16-lane group, lane
+  // 4a+b receives element b of the 8-byte chunks read by lanes a, a+4, a+8,
+  // a+12.  So lane s of the group reads row 4g + s/4 of the key group, at
+  // column 32*db + 16*(lane/16 % 2) + 4*(s % 4); it then holds 4 consecutive
+  // keys of column 32*db + lane % 32.
+  int v_off[VTR ? NDB : 1];
+#pragma unroll
+  for (int db = 0; db < (VTR ? NDB : 1); ++db) {
+    const int r4 = (lane >> 2) & 3;
+    const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    v_off[db] = (4 * g + r4) * RB + ((c ^ (r4 << 1)) * 16) + 8 * (lane & 1);
+  }
+
+  // Issue the direct LDS loads of tile j into buffer buf (16-bit types).
+  auto dma_tile = [&](int j, int buf) {
+    if constexpr (VTR) {
+      char* base = reinterpret_cast<char*>(smem + buf * (KT + VT));
+      const int soff = j * BN * D * ESZ;
+#pragma unroll
+      for (int i = 0; i < DNI; ++i) {
+        char* dst = base + (wave * DNI + i) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rs, (lds_void*)dst, 16, unsigned(dma_k[i]), unsigned(soff), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rs, (lds_void*)(dst + KT * ESZ), 16,
+                                                 unsigned(dma_v[i]), unsigned(soff), 0, 0);
+      }
+    }
+  };
+
+  // fp32: global -> registers (the LDS store follows the compute of the tile)
   auto gload = [&](int j) {
+    if constexpr (!VTR) {
     const int key0 = j * BN;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
@@ -479,14 +534,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
       const int row = cidx / (D / VEC), col = (cidx % (D / VEC)) * VEC;
       kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(k_rs, ((key0 + row) * D + col) * ESZ, 0, 0);
     }
-    if constexpr (VTR) {
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int cidx = tid + i * kThreads;
-        const int row = cidx / (D / VEC), col = (cidx % (D / VEC)) * VEC;
-        vrow[i] = __builtin_amdgcn_raw_buffer_load_b128(v_rs, ((key0 + row) * D + col) * ESZ, 0, 0);
-      }
-    } else {
 #pragma unroll
       for (int i = 0; i < VTPT; ++i) {
         const int t = tid + i * kThreads;
@@ -503,6 +550,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   };
 
   auto sstore = [&](int buf) {
+    if constexpr (VTR) return;  // the direct loads already wrote the tile
     T* sK = smem + buf * (KT + VT);
     T* sV = sK + KT;
 #pragma unroll
@@ -510,15 +558,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
       const int cidx = tid + i * kThreads;
       const int row = cidx / (D / VEC), col = (cidx % (D / VEC)) * VEC;
       *reinterpret_cast<u32x4*>(sK + row * KSTR + col) = kreg[i];
-    }
-    if constexpr (VTR) {
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int cidx = tid + i * kThreads;
-        const int row = cidx / (D / VEC), col = (cidx % (D / VEC)) * VEC;
-        *reinterpret_cast<u32x4*>(sV + row * VRSTR + col) = vrow[i];
-      }
-      return;
     }
 #pragma unroll
     for (int i = 0; i < VTPT; ++i) {
@@ -578,11 +617,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
     for (int st = 0; st < NS; ++st) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const T* src = sK + (kb * 32 + ln) * KSTR + st * KS + g * KP;
         Frag kf;
         if constexpr (F32) {
-          kf = *src;
+          kf = sK[(kb * 32 + ln) * KSTR + st * KS + g * KP];
         } else {
+          const char* src = reinterpret_cast<const char*>(sK) + kb * 32 * RB + k_off[st];
           kf = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(src));
         }
 #pragma unroll
@@ -691,9 +730,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
             // k16+4g+8..11 (k16 = first key of the 16-key group), the order
             // the S^T registers hold P in.  Each transposed read gives every
             // lane 4 consecutive keys of its column d = 32*db + lane%32.
-            const T* src = sV + (kb * 32 + 16 * h) * VRSTR + db * 32 + tr_off;
+            const char* src = reinterpret_cast<const char*>(sV) + (kb * 32 + 16 * h) * RB + v_off[db];
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 8 * VRSTR));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 8 * RB));
             const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
             const Frag vf = __builtin_bit_cast(Frag, u32x4{lw[0], lw[1], hw[0], hw[1]});
 #pragma unroll
@@ -705,16 +744,24 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   };
 
   // ---- main loop: double-buffered K/V tiles -------------------------------------
+  // Tile j+1 is requested (into the other LDS buffer, or into registers for
+  // fp32) before tile j is computed; one barrier per tile.  The buffer being
+  // filled was last read in the previous iteration, before its barrier.
   if (j_end > j_begin) {
+    dma_tile(j_begin, 0);
     gload(j_begin);
     if constexpr (BIAS) load_bias(bcur, j_begin);
     sstore(0);
+    if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
     __syncthreads();
   }
   for (int j = j_begin; j < j_end; ++j) {
     const int cur = (j - j_begin) & 1;
     const bool has_next = j + 1 < j_end;
-    if (has_next) gload(j + 1);
+    if (has_next) {
+      dma_tile(j + 1, cur ^ 1);
+      gload(j + 1);
+    }
     const bool active = wave_has_rows && (!CAUSAL || j * BN <= wave_pos_max);
     if constexpr (BIAS) {
       const bool next_active =
@@ -731,6 +778,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
           for (int q4 = 0; q4 < 4; ++q4) bcur[qb][kb][q4] = bnext[qb][kb][q4];
     }
     if (has_next) sstore(cur ^ 1);
+    // the direct LDS loads of this wave are done before the barrier publishes them
+    if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
     __syncthreads();
   }
 
