@@ -8,9 +8,9 @@ inputs already resident in HBM; for the key-split workloads it is one
 fa_forward_split call (the split kernel and the merge kernel, workspace
 allocated beforehand).  The default workload is B=2, H=16, S=4096,
 D=64, bf16, causal.  Timing follows the CUDA-event method of the Day 26 post
-(blog.ans20xx.com/posts/ai/day26): W untimed warm-up steps, then K steps, each
-bracketed by its own pair of events on the stream the kernel runs on, plus one
-pair around all K.  Prints one JSON line.
+(blog.ans20xx.com/posts/ai/day26): W untimed warm-up steps, then K steps with
+one event recorded before each step and one after the last, on the stream the
+kernels run on.  Prints one JSON line.
 
 value     = 4*B*H*S^2*D / t_step in TFLOP/s (the post's formula, not halved
             for causal), t_step = wall time of the K steps / K;
@@ -181,20 +181,19 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # One event before each step and one after the last, all on the launch
+    # stream: step i lasts from event i to event i+1 (its kernels and the
+    # dispatch gap to the next step), and the K steps from event 0 to event K.
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
-    t_start.record(stream)
-    for a, b in ev:
-        a.record(stream)
+    for i in range(K):
+        ev[i].record(stream)
         step()
-        b.record(stream)
-    t_end.record(stream)
+    ev[K].record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    per = sorted(a.elapsed_time(b) for a, b in ev)
+    total_ms = ev[0].elapsed_time(ev[K])
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(K))
     ms_per_step = total_ms / K
     launch_ms = statistics.fmean(per)
     assert torch.isfinite(lse).all(), "non-finite LSE in the benchmark output"
