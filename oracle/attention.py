@@ -57,6 +57,7 @@ __all__ = [
     "merge_states",
     "attention_partial",
     "merge_partials",
+    "attention_backward",
 ]
 
 
@@ -279,3 +280,55 @@ def merge_partials(o_parts, lse_parts):
     o_out = np.where(ok[..., None], o / np.where(ok, l, 1.0)[..., None], 0.0)
     lse_out = np.where(ok, m + np.log(np.where(ok, l, 1.0)), -np.inf)
     return o_out, lse_out
+
+
+def attention_backward(q, k, v, dout, bias=None, *, scale=None, causal=False):
+    """Gradients of the forward definition above with respect to q, k and v.
+
+    The forward keeps only O and the per-row statistic and recomputes S and P
+    in the backward ("FlashAttention principles and Triton practice", §2.3 and
+    §4.3; kwkr.cn tutorial, §2.4).  What that recomputation must reproduce is
+    the chain rule through the definition, per (b, hq) with hk = hq // group:
+
+        P   = softmax(S)            (S as in the forward, masked entries -inf)
+        dV  = P^T dO                (summed over the query heads of a group)
+        dP  = dO V^T
+        D_i = sum_j P_ij dP_ij  =  sum_d dO_id O_id     (the row sum to subtract)
+        dS  = P o (dP - D)          (elementwise; masked entries have P = 0)
+        dQ  = scale * dS K
+        dK  = scale * dS^T Q        (summed over the query heads of a group)
+
+    The bias term receives dS itself and is treated as a constant here (its
+    gradient is not returned); LSE is an auxiliary output with no incoming
+    gradient.  Rows that see no key have P = 0 and contribute nothing.
+    Returns ``(dQ, dK, dV)`` in float64 with the shapes of q, k, v.
+    """
+    b_, hq_, hkv, nq, nk, d = _check_shapes(q, k, v, bias)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    group = hq_ // hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(b_):
+        for h in range(hq_):
+            hk = h // group
+            s = (q[b, h] @ k[b, hk].T) * float(scale)
+            if bias is not None:
+                s = s + _f64(bias[b, h])
+            if causal:
+                i = np.arange(nq)[:, None]
+                j = np.arange(nk)[None, :]
+                s = np.where(j > i, -np.inf, s)
+            p, _, _ = softmax_two_pass(s)
+            do = dout[b, h]
+            dv[b, hk] += p.T @ do
+            dp = do @ v[b, hk].T
+            dsum = (p * dp).sum(axis=1, keepdims=True)
+            ds = p * (dp - dsum)
+            dq[b, h] = float(scale) * (ds @ k[b, hk])
+            dk[b, hk] += float(scale) * (ds.T @ q[b, h])
+    return dq, dk, dv
