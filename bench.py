@@ -42,7 +42,8 @@ sys.path.insert(0, ROOT)
 PAGE_FLASH_ATTN_V2_TFLOPS = 11.57
 METRIC = ("attention TFLOPS (4·B·H·S²·D/t) and % MFMA bf16 peak at "
           "B2 H16 S4096 D64 causal")
-KERNEL_SOURCE = os.path.join(ROOT, "tiled_attention_forward_amd", "csrc", "fa_fwd.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_forward_amd", "csrc", f)
+                  for f in ("fa_fwd.hip", "fa_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -69,8 +70,13 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the forward kernels' sources (the counters in traffic.json
+    were taken on the build of exactly these bytes)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_for(workload: str):

@@ -42,25 +42,11 @@
 #include <type_traits>
 
 #include "../../include/fa.h"
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
-
-typedef uint32_t u32;
-typedef uint16_t u16;
-typedef u32 u32x4 __attribute__((ext_vector_type(4)));
-typedef u32 u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;              // waves per workgroup
 constexpr int kThreads = kWaves * 64;
@@ -86,65 +72,6 @@ constexpr int kQB128 = FA_QB128;       // 32-row query blocks per wave, D = 128
 constexpr float kTau = 8.f;            // lazy-rescale threshold (log2 units)
 static_assert(kWaves * 32 >= kRowsPerBlock,
               "grid-size validation assumes at least this block height");
-
-constexpr float kLog2e = 1.4426950408889634f;
-// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt = 0 only: vector
-// memory counter bits [3:0] and [15:14] zero, expcnt [6:4] and lgkmcnt [11:8]
-// at their maxima (no wait).
-constexpr int kWaitVmem0 = 0x0F70;
-constexpr float kLn2 = 0.6931471805599453f;
-
-// ---------------------------------------------------------------------------
-// Element traits: MFMA shape, operand fragment type and conversions.
-// KP = contraction values one lane supplies to one MFMA.
-// ---------------------------------------------------------------------------
-template <typename T>
-struct Elem;
-
-template <>
-struct Elem<__bf16> {
-  static constexpr int KP = 8;
-  using Frag = bf16x8;
-  static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ Frag pack8(f32x8 x) {
-    return __builtin_convertvector(x, bf16x8);
-  }
-  static __device__ __forceinline__ float widen(u32 bits16) {
-    return __builtin_bit_cast(float, bits16 << 16);
-  }
-  static __device__ __forceinline__ u32x2 narrow4(f32x4 x) {
-    return __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
-  }
-};
-
-template <>
-struct Elem<_Float16> {
-  static constexpr int KP = 8;
-  using Frag = f16x8;
-  static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ Frag pack8(f32x8 x) {
-    return __builtin_convertvector(x, f16x8);
-  }
-  static __device__ __forceinline__ float widen(u32 bits16) {
-    return float(__builtin_bit_cast(_Float16, u16(bits16)));
-  }
-  static __device__ __forceinline__ u32x2 narrow4(f32x4 x) {
-    return __builtin_bit_cast(u32x2, __builtin_convertvector(x, f16x4));
-  }
-};
-
-template <>
-struct Elem<float> {
-  static constexpr int KP = 1;
-  using Frag = float;
-  static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-  }
-};
 
 struct Params {
   const void* q;
@@ -172,37 +99,6 @@ __device__ __forceinline__ int vt_pos_of_group(int kg) {  // kg = key / 4
   const int r = kg & 3;
   const int sigma = (r == 1) ? 2 : (r == 2) ? 1 : r;
   return (kg >> 2) * 16 + sigma * 4;
-}
-
-// {own value, value of lane l^32} in some order, via v_permlane32_swap.  The
-// two results are copied out of the returned vector as values before being
-// reinterpreted: applying __builtin_bit_cast to the element lvalue r[1] reads
-// the vector's first element instead (seen with this ROCm clang).
-__device__ __forceinline__ void own_and_partner(float x, float& a, float& b) {
-  const u32 xi = __builtin_bit_cast(u32, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
-  const u32 r0 = r[0], r1 = r[1];
-  a = __builtin_bit_cast(float, r0);
-  b = __builtin_bit_cast(float, r1);
-}
-
-__device__ __forceinline__ float partner_max(float x) {
-  float a, b;
-  own_and_partner(x, a, b);
-  return fmaxf(a, b);
-}
-
-__device__ __forceinline__ float partner_sum(float x) {
-  float a, b;
-  own_and_partner(x, a, b);
-  return a + b;
-}
-
-// Raw buffer resource over [base, base + bytes): loads past the end return 0
-// (the hardware range check), so tails need no branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
-                                           0x00020000);
 }
 
 // SPLIT = false: one workgroup per (batch, query head, 128-row block); O and
