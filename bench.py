@@ -42,8 +42,12 @@ sys.path.insert(0, ROOT)
 PAGE_FLASH_ATTN_V2_TFLOPS = 11.57
 METRIC = ("attention TFLOPS (4·B·H·S²·D/t) and % MFMA bf16 peak at "
           "B2 H16 S4096 D64 causal")
-KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_forward_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_device.h")]
+KERNEL_SOURCES = {
+    p: [os.path.join(ROOT, "tiled_attention_forward_amd", "csrc", f)
+        for f in (("fa_fwd.hip", "fa_device.h") if p == "forward" else ("fa_bwd.hip", "fa_device.h"))]
+    for p in ("forward", "backward")
+}
+BACKWARD_FLOP_FACTOR = 2.5  # five products against the forward's two
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -56,6 +60,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--pass", dest="pass_", choices=["forward", "backward"], default="forward",
+                    help="time the forward (default) or the backward (dQ, dK, dV)")
     ap.add_argument("--path", choices=["fused", "split"], default=None,
                     help="entry point to time (default: the workload's own)")
     ap.add_argument("--splits", type=int, default=0,
@@ -69,25 +75,26 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the forward kernels' sources (the counters in traffic.json
-    were taken on the build of exactly these bytes)."""
+def kernel_source_hash(pass_: str = "forward") -> str:
+    """sha256 over the kernels' sources of one pass (the counters in
+    traffic.json were taken on the build of exactly these bytes)."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in KERNEL_SOURCES[pass_]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def traffic_for(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+def traffic_for(workload: str, pass_: str = "forward"):
+    """HBM bytes per step from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
+    key = workload if pass_ == "forward" else f"{workload}:{pass_}"
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(workload)
+            rec = json.load(f).get(key)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash(pass_):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -101,6 +108,35 @@ def blas_threads() -> int:
     except Exception:
         pass
     return os.cpu_count() or 1
+
+
+def cpu_baseline_backward(w, q, k, v, dout, target_s: float):
+    """Time the oracle's backward on whole (batch, KV head) groups until about target_s."""
+    import numpy as np
+
+    from oracle import attention_backward
+
+    grp = w.Hq // w.Hkv
+    done, t_used = 0, 0.0
+    for b in range(w.B):
+        for hk in range(w.Hkv):
+            hs = slice(hk * grp, (hk + 1) * grp)
+            f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+            qs, gs = f(q[b:b + 1, hs]), f(dout[b:b + 1, hs])
+            ks, vs = f(k[b:b + 1, hk:hk + 1]), f(v[b:b + 1, hk:hk + 1])
+            t0 = time.perf_counter()
+            attention_backward(qs, ks, vs, gs, None, scale=w.scale, causal=w.causal)
+            t_used += time.perf_counter() - t0
+            done += grp
+            if t_used >= target_s:
+                break
+        if t_used >= target_s:
+            break
+    per_head = BACKWARD_FLOP_FACTOR * w.metric_flops() / (w.B * w.Hq)
+    return {"value": round(per_head * done / t_used / 1e12, 6), "unit": "TFLOPS",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"backward of {done} of {w.B * w.Hq} (batch, head) slices of {w.name}, "
+                      f"fp64 NumPy, {t_used:.1f} s"}
 
 
 def cpu_baseline(w, q, k, v, bias, target_s: float):
@@ -159,7 +195,23 @@ def main():
                  bias.data_ptr() if bias is not None else None, o.data_ptr(), lse.data_ptr(),
                  w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal), dtype_code)
     splits = None
-    if w.path == "split":
+    backward = args.pass_ == "backward"
+    if backward:
+        if w.bias or w.dtype == "fp32":
+            print("the backward is timed on bias-free 16-bit workloads", file=sys.stderr)
+            sys.exit(2)
+        g = torch.Generator(device=dev).manual_seed(args.seed + 1000)
+        dout = torch.randn(q.shape, generator=g, device=dev).to(q.dtype)
+        binding.forward(q, k, v, None, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_bytes = binding.fa_backward_workspace_bytes(w.B, w.Hq, w.Nq)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        entry = lib.fa_backward
+        call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), None, o.data_ptr(), lse.data_ptr(),
+                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.Hq,
+                     w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal), dtype_code,
+                     workspace.data_ptr(), ws_bytes, stream.cuda_stream)
+    elif w.path == "split":
         splits = args.splits or binding.fa_split_count(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D)
         ws_bytes = binding.fa_split_workspace_bytes(w.B, w.Hq, w.Nq, w.D, splits)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -204,22 +256,28 @@ def main():
     launch_ms = statistics.fmean(per)
     assert torch.isfinite(lse).all(), "non-finite LSE in the benchmark output"
 
-    value = w.metric_flops() / (ms_per_step / 1e3) / 1e12
+    fl = BACKWARD_FLOP_FACTOR if backward else 1.0
+    value = fl * w.metric_flops() / (ms_per_step / 1e3) / 1e12
     peak = metrics.MFMA_PEAK_TFLOPS[w.dtype]
     ridge = peak * 1e12 / (metrics.HBM_PEAK_GBS * 1e9)   # flops per byte
-    if w.useful_flops() / w.io_bytes() < ridge:
+    if not backward and w.useful_flops() / w.io_bytes() < ridge:
         achieved = w.io_bytes() / (launch_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": metrics.HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / metrics.HBM_PEAK_GBS, 4)}
     else:
-        achieved = w.useful_flops() / (launch_ms / 1e3) / 1e12
+        achieved = fl * w.useful_flops() / (launch_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
-    roof["traffic"] = traffic_for(w.name)
+    roof["traffic"] = traffic_for(w.name, args.pass_)
 
+    if backward:
+        metric = f"attention backward TFLOPS (2.5·4·B·H·Nq·Nk·D/t) at {w.name}"
+    elif w.name == HEADLINE:
+        metric = METRIC
+    else:
+        metric = f"attention TFLOPS (4·B·H·Nq·Nk·D/t) at {w.name}"
     out = {
-        "metric": METRIC if w.name == HEADLINE else
-        f"attention TFLOPS (4·B·H·Nq·Nk·D/t) at {w.name}",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -228,20 +286,23 @@ def main():
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGE_FLASH_ATTN_V2_TFLOPS, 2) if w.name == HEADLINE else None,
+        "vs_baseline": (round(value / PAGE_FLASH_ATTN_V2_TFLOPS, 2)
+                        if w.name == HEADLINE and not backward else None),
         "dtype": w.dtype,
         "data": "synthetic: i.i.d. N(0,1) inputs from a seeded generator",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
                    "Nk": w.Nk, "D": w.D, "causal": w.causal, "bias": w.bias,
-                   "path": w.path, "splits": splits, "parallelism": "single GPU"},
+                   "path": w.path, "splits": splits, "pass": args.pass_,
+                   "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * value / metrics.MFMA_PEAK_TFLOPS["bf16"], 2),
-        "useful_tflops": round(w.useful_flops() / (ms_per_step / 1e3) / 1e12, 2),
+        "useful_tflops": round(fl * w.useful_flops() / (ms_per_step / 1e3) / 1e12, 2),
         "launch_ms": {"mean": round(launch_ms, 5), "median": round(statistics.median(per), 5),
                       "p90": round(per[int(len(per) * 0.9)], 5), "min": round(per[0], 5)},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, bias, args.cpu_seconds)
+        out["cpu_baseline"] = (cpu_baseline_backward(w, q, k, v, dout, args.cpu_seconds) if backward
+                               else cpu_baseline(w, q, k, v, bias, args.cpu_seconds))
     print(json.dumps(out), flush=True)
 
 

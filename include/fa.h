@@ -179,6 +179,49 @@ int fa_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, i
 int fa_merge(const float* part_o, const float* part_lse, int64_t num_parts, int64_t rows,
              int64_t D, void* o, float* lse, int dtype, void* stream);
 
+/*
+ * Backward of fa_forward: gradients of a loss with respect to q, k and v,
+ * given its gradient dout with respect to o.
+ *
+ * The forward keeps neither S nor P; they are recomputed from q, k (and bias)
+ * and the saved per-row lse ("FlashAttention principles and Triton practice",
+ * xnwp.cn/news/15505, §2.3 and §4.3; kwkr.cn/news/592482 tutorial, §2.4).  With
+ * P = exp(S - LSE) per row:
+ *     dV = P^T dO,  dP = dO V^T,  D_i = sum_d dO_id O_id,  dS = P o (dP - D),
+ *     dQ = scale dS K,  dK = scale dS^T Q,
+ * with dK and dV summed over the query heads that share a KV head.  The bias
+ * is taken as a constant (its gradient, dS itself, is not produced) and lse as
+ * an auxiliary output with no incoming gradient.
+ *
+ *   q, k, v, bias, scale, causal: exactly as passed to fa_forward;
+ *   o, lse:  that call's outputs (o in dtype, lse float32);
+ *   dout:    gradient of the loss w.r.t. o, [B, Hq, Nq, D], dtype;
+ *   dq:      out, [B, Hq, Nq, D], dtype;
+ *   dk, dv:  out, [B, Hkv, Nk, D], dtype;
+ *   workspace: device scratch owned by the caller, 16-byte aligned, at least
+ *     fa_backward_workspace_bytes(B, Hq, Nq) bytes; holds D_i and LSE_i*log2(e)
+ *     (float32) on return.  NULL is allowed when B*Hq*Nq == 0.
+ * bf16 and fp16 only (FA_ERR_DTYPE for fp32).  Products run on the matrix
+ * cores with float32 accumulation; P and dS are rounded to the input type
+ * before their products, as P is in the forward.  Results are deterministic
+ * (no atomics: dQ has its own kernel).  Errors as for fa_forward, plus
+ * FA_ERR_NULL_POINTER for a missing dout/dq (rows present) or dk/dv/k/v (keys
+ * present), FA_ERR_WORKSPACE, and FA_ERR_OVERLAP if dq, dk, dv or the
+ * workspace overlap an input or each other.  With no query rows (B, Hq or
+ * Nq == 0) but keys present, dk and dv are set to zero.  Three kernels are
+ * enqueued on stream (row sums, dQ, dK/dV); the call returns without waiting.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* bias,
+                const void* o, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv,
+                int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                float scale, int causal, int dtype,
+                void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes of fa_backward through *bytes: float32 [B*Hq*Nq] twice,
+ * the second part from the next 256-byte boundary.  Pure host code. */
+int fa_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t* bytes);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_string(int status);
 

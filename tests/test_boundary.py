@@ -47,8 +47,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = binding.load_library()
     names = declared_functions()
     assert set(names) == {"fa_check_args", "fa_forward", "fa_forward_split", "fa_merge",
-                          "fa_split_count", "fa_split_workspace_bytes", "fa_status_string",
-                          "fa_version"}
+                          "fa_split_count", "fa_split_workspace_bytes", "fa_backward",
+                          "fa_backward_workspace_bytes", "fa_status_string", "fa_version"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
@@ -205,3 +205,44 @@ def test_merge_rejections_before_launch():
     assert merge_status(part_o=WS + 4) == 7 and merge_status(lse=L + 2) == 7
     assert merge_status(o=WS + 64) == 8 and merge_status(lse=WS + (1 << 30) + 8) == 8
     assert merge_status(num_parts=1 << 31) == 9
+
+
+# ---------------------------------------------------------------------------
+# backward: validation only (no launch on the CPU)
+# ---------------------------------------------------------------------------
+
+GO, DQ, DK, DV = (0x100000000 * (i + 10) for i in range(4))
+
+
+def bwd_status(workspace=WS, workspace_bytes=1 << 40, dout=GO, dq=DQ, dk=DK, dv=DV, **over):
+    a = dict(OK_ARGS, **over)
+    return binding.fa_backward(a["q"], a["k"], a["v"], a["bias"], a["o"], a["lse"], dout, dq, dk,
+                               dv, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"],
+                               a["scale"], a["causal"], a["dtype"], workspace, workspace_bytes,
+                               None)
+
+
+def test_backward_workspace_bytes():
+    rows = 2 * 4 * 100
+    assert binding.fa_backward_workspace_bytes(2, 4, 100) == ((rows + 63) // 64 * 64 + rows) * 4
+    assert binding.fa_backward_workspace_bytes(0, 4, 100) == 0
+    with pytest.raises(binding.FaError):
+        binding.fa_backward_workspace_bytes(-1, 4, 100)
+
+
+def test_backward_rejections_before_launch():
+    assert bwd_status(dtype=binding.FA_DTYPE_FP32) == 5       # 16-bit types only
+    assert bwd_status(D=96) == 4 and bwd_status(q=None) == 1   # the forward's checks first
+    assert bwd_status(dout=None) == 1 and bwd_status(dq=None) == 1
+    assert bwd_status(dk=None) == 1 and bwd_status(dv=None) == 1
+    assert bwd_status(dq=DQ + 8) == 7 and bwd_status(dout=GO + 4) == 7
+    need = binding.fa_backward_workspace_bytes(2, 4, 100)
+    assert bwd_status(workspace=None) == 11 and bwd_status(workspace_bytes=need - 4) == 11
+    assert bwd_status(workspace=WS + 8) == 11
+    assert bwd_status(dq=Q) == 8 and bwd_status(dk=V + 64) == 8 and bwd_status(dv=DK) == 8
+    assert bwd_status(workspace=GO) == 8
+    # no rows and no keys: nothing to do, nothing needed
+    assert bwd_status(B=0, q=None, k=None, v=None, o=None, lse=None, dout=None, dq=None, dk=None,
+                      dv=None, workspace=None) == 0
+    # no query rows but keys present: dk and dv are still written (zeros), so needed
+    assert bwd_status(Nq=0, dk=None) == 1

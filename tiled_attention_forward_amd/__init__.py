@@ -8,9 +8,10 @@ is missing or does not load.
 
 from . import metrics, workloads  # noqa: F401
 
-_BINDING_NAMES = ("fa_forward", "fa_forward_split", "fa_merge", "fa_split_count",
-                  "fa_split_workspace_bytes", "fa_check_args", "fa_status_string", "fa_version",
-                  "forward", "forward_split", "merge", "FaError", "library_path", "load_library")
+_BINDING_NAMES = ("fa_forward", "fa_forward_split", "fa_merge", "fa_backward", "fa_split_count",
+                  "fa_split_workspace_bytes", "fa_backward_workspace_bytes", "fa_check_args",
+                  "fa_status_string", "fa_version", "forward", "forward_split", "merge",
+                  "backward", "FaError", "library_path", "load_library")
 
 
 def __getattr__(name):

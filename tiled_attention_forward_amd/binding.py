@@ -1,11 +1,11 @@
 """ctypes binding of libfa.so (argument marshalling only).
 
-``fa_forward``, ``fa_forward_split``, ``fa_merge``, ``fa_split_count``,
-``fa_split_workspace_bytes``, ``fa_check_args``, ``fa_status_string`` and
-``fa_version`` take the same arguments as the C functions of ``include/fa.h``
-(device pointers as Python ints; the two size queries return their value).
-``forward``, ``forward_split`` and ``merge`` are the tensor-level
-conveniences: they check the torch tensors, allocate outputs (and the
+``fa_forward``, ``fa_forward_split``, ``fa_merge``, ``fa_backward``,
+``fa_split_count``, ``fa_split_workspace_bytes``, ``fa_backward_workspace_bytes``,
+``fa_check_args``, ``fa_status_string`` and ``fa_version`` take the same
+arguments as the C functions of ``include/fa.h`` (device pointers as Python
+ints; the size queries return their value).  ``forward``, ``forward_split``,
+``merge`` and ``backward`` are the tensor-level conveniences: they check the torch tensors, allocate outputs (and the
 key-split workspace) with torch, and call the library on the current stream.
 Every step of the attention runs in the library's kernels; if the library is
 missing or does not load, the call raises instead of computing anything some
@@ -64,6 +64,11 @@ def load_library():
     lib.fa_split_count.restype = i32
     lib.fa_merge.argtypes = [p, p, i64, i64, i64, p, p, i32, p]
     lib.fa_merge.restype = i32
+    lib.fa_backward.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32,
+                                i32, i32, p, i64, p]
+    lib.fa_backward.restype = i32
+    lib.fa_backward_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
+    lib.fa_backward_workspace_bytes.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -109,6 +114,22 @@ def fa_split_count(B, Hq, Hkv, Nq, Nk, D) -> int:
     """The library's suggested key-split count; raises FaError on invalid sizes."""
     out = ctypes.c_int64(0)
     st = load_library().fa_split_count(B, Hq, Hkv, Nq, Nk, D, ctypes.byref(out))
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+    return out.value
+
+
+def fa_backward(q, k, v, bias, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, D, scale, causal,
+                dtype, workspace, workspace_bytes, stream) -> int:
+    return load_library().fa_backward(q, k, v, bias, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk,
+                                      D, float(scale), int(causal), int(dtype), workspace,
+                                      int(workspace_bytes), stream)
+
+
+def fa_backward_workspace_bytes(B, Hq, Nq) -> int:
+    """Workspace bytes of fa_backward; raises FaError on invalid sizes."""
+    out = ctypes.c_int64(0)
+    st = load_library().fa_backward_workspace_bytes(B, Hq, Nq, ctypes.byref(out))
     if st != FA_OK:
         raise FaError(st, fa_status_string(st))
     return out.value
@@ -245,3 +266,38 @@ def merge(part_o, part_lse, dtype, *, out=None, lse=None, stream=None):
     if st != FA_OK:
         raise FaError(st, fa_status_string(st))
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, bias=None, *, causal=False, scale=None, dq=None, dk=None,
+             dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of attention(q, k, v [, bias]) through fa_backward.
+
+    ``o`` and ``lse`` are the outputs of ``forward`` on the same arguments and
+    ``dout`` the gradient with respect to ``o``.  bf16/fp16 tensors; outputs
+    and the workspace are allocated with torch unless given.
+    """
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v, bias)
+    for name, t in (("o", o), ("dout", dout)):
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fa_backward_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                         bias.data_ptr() if bias is not None else None, o.data_ptr(),
+                         lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                         dv.data_ptr(), B, Hq, Hkv, Nq, Nk, D, float(scale), int(bool(causal)),
+                         _dtype_code(q), workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+    return dq, dk, dv

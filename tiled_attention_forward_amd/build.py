@@ -2,7 +2,7 @@
 
     python -m tiled_attention_forward_amd.build
 
-compiles ``csrc/fa_api.cpp`` and ``csrc/fa_fwd.hip`` into
+compiles ``csrc/fa_api.cpp``, ``csrc/fa_fwd.hip`` and ``csrc/fa_bwd.hip`` into
 ``tiled_attention_forward_amd/libfa.so``.  Packed-fp32 code generation is
 switched off for all device code.
 """
@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

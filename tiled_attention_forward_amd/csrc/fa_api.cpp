@@ -222,6 +222,86 @@ extern "C" int fa_merge(const float* part_o, const float* part_lse, int64_t num_
   return fa::launch_merge(part_o, part_lse, int(num_parts), rows, int(D), o, lse, dtype, stream);
 }
 
+extern "C" int fa_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t* bytes) {
+  if (bytes == nullptr) return FA_ERR_NULL_POINTER;
+  if (B < 0 || Hq < 0 || Nq < 0) return FA_ERR_BAD_SIZE;
+  const __int128 rows = __int128(B) * Hq * Nq;
+  if (rows >= (__int128(1) << 60)) return FA_ERR_TOO_LARGE;
+  *bytes = fa::backward_workspace_bytes(int64_t(rows));
+  return FA_OK;
+}
+
+extern "C" int fa_backward(const void* q, const void* k, const void* v, const void* bias,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                           void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                           int64_t D, float scale, int causal, int dtype, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+  if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;  // 16-bit types only
+  int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  const int esz = elem_bytes(dtype);
+  const bool no_rows = (B == 0 || Hq == 0 || Nq == 0);
+  const bool no_keys = (B == 0 || Hkv == 0 || Nk == 0);
+  if (no_rows && no_keys) return FA_OK;
+  // pointers fa_check_args does not cover, or skipped for an empty row space
+  if (!no_rows && (dout == nullptr || dq == nullptr)) return FA_ERR_NULL_POINTER;
+  if (!no_keys && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return FA_ERR_NULL_POINTER;
+  if (no_rows && (!aligned(k, 16) || !aligned(v, 16))) return FA_ERR_ALIGNMENT;
+  const int64_t lim = int64_t(1) << 30;
+  if (B >= lim || Hq >= lim || Hkv >= lim || Nq >= lim || Nk >= lim) return FA_ERR_TOO_LARGE;
+  const int64_t lim31 = int64_t(1) << 31;
+  // dK/dV kernel: the packed query rows of one KV head, and its grid
+  if (Hkv > 0 && __int128(Hq / Hkv) * Nq * D * esz >= lim31) return FA_ERR_TOO_LARGE;
+  if (Nk * D * esz >= lim31) return FA_ERR_TOO_LARGE;
+  if (__int128(B) * Hkv * ((Nk + 127) / 128) >= lim31) return FA_ERR_TOO_LARGE;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return FA_ERR_ALIGNMENT;
+  const int64_t rows = B * Hq * Nq;
+  const int64_t need = fa::backward_workspace_bytes(rows);
+  if (rows > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need))
+    return FA_ERR_WORKSPACE;
+  // outputs and workspace must not overlap the inputs or each other
+  const uint64_t nq_b = uint64_t(rows) * D * esz;
+  const uint64_t nkv_b = uint64_t(B) * Hkv * Nk * D * esz;
+  const uint64_t nb_b = bias ? uint64_t(rows) * Nk * esz : 0;
+  const uint64_t nl_b = uint64_t(rows) * 4;
+  const uint64_t ws_b = rows > 0 ? uint64_t(need) : 0;
+  struct Buf { const void* p; uint64_t n; };
+  const Buf ins[] = {{q, nq_b}, {k, nkv_b}, {v, nkv_b}, {bias, nb_b}, {o, nq_b}, {lse, nl_b},
+                     {dout, nq_b}};
+  const Buf outs[] = {{dq, nq_b}, {dk, nkv_b}, {dv, nkv_b}, {workspace, ws_b}};
+  for (const Buf& a : outs) {
+    for (const Buf& b : ins)
+      if (overlap(a.p, a.n, b.p, b.n)) return FA_ERR_OVERLAP;
+    for (const Buf& b : outs)
+      if (&a != &b && overlap(a.p, a.n, b.p, b.n)) return FA_ERR_OVERLAP;
+  }
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.bias = bias;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.workspace = workspace;
+  a.B = int(B);
+  a.Hq = int(Hq);
+  a.Hkv = int(Hkv);
+  a.Nq = int(Nq);
+  a.Nk = int(Nk);
+  a.D = int(D);
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.dtype = dtype;
+  a.stream = stream;
+  return fa::launch_backward(a);
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

@@ -1,0 +1,682 @@
+// Attention backward for gfx950 (MI355X): gradients dQ, dK, dV of the fused
+// forward from its saved output O and per-row LSE.
+//
+// Method: the forward keeps no S or P; the backward recomputes them from Q, K
+// and the saved statistic and applies the chain rule ("FlashAttention
+// principles and Triton practice", xnwp.cn/news/15505, §2.3 and §4.3; the
+// kwkr.cn/news/592482 tutorial, §2.4).  With P = exp(S - LSE):
+//     dV = P^T dO,  dP = dO V^T,  D = rowsum(dO o O),  dS = P o (dP - D),
+//     dQ = scale dS K,  dK = scale dS^T Q.
+// The pages note that dQ collects contributions from every key block; here it
+// gets a kernel of its own (one workgroup per query block, looping over key
+// tiles), so no atomics are needed and the results are deterministic, at the
+// price of computing S and dP twice.
+//
+// Kernels (16-bit types, D in {64, 128}):
+//  * fa_bwd_prep_kernel: delta_i = sum_d dO_id O_id and lse2_i = LSE_i log2(e)
+//    (+inf for rows with LSE = -inf, so that their P is exactly 0), fp32;
+//  * fa_bwd_dq_kernel: the forward's layout -- each wave owns 32 query rows,
+//    one per lane; S^T = K Q^T and dP^T = V dO^T on 32x32x16 MFMAs with Q and
+//    dO rows held in registers and K/V tiles streamed through LDS; then
+//    dQ^T += K^T dS^T with K read transposed from LDS;
+//  * fa_bwd_dkdv_kernel: the roles swapped -- each wave owns 32 keys, one per
+//    lane, and the query rows of the KV head's group (packed as the key-split
+//    forward packs them) stream through LDS in 64-row tiles: S = Q K^T and
+//    dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS with Q and dO read
+//    transposed from LDS.
+// P and dS are rounded to the input type for the MFMAs (as P is in the
+// forward); all sums are fp32.
+//
+// LDS tiles are row-major and unpadded, filled straight from HBM by buffer
+// loads with the LDS flag; the 16-byte chunk c of tile row r is stored at
+// chunk c ^ sw(r), sw(r) = 2*(r & 3) | ((r >> 2) & 1).  That one swizzle keeps
+// both access patterns free of bank conflicts: 16-byte row reads (8 rows per
+// cycle, sw takes 8 distinct values over r = 0..7) and transposed reads (in a
+// 16-lane group, 4 rows r with sw(r) differing in bits 1-2, each reading 2
+// adjacent chunks).
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "../../include/fa.h"
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdThreads = 256;  // 4 waves
+constexpr int kQTile = 64;        // query rows per tile in the dK/dV kernel
+constexpr int kKTile = 64;        // keys per tile in the dQ kernel
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* bias;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;  // [B*Hq*Nq]
+  float* lse2;   // [B*Hq*Nq]
+  void* dq;
+  void* dk;
+  void* dv;
+  int Hq, Hkv, Nq, Nk;
+  int BH, BHkv;
+  int group;
+  int n_qblk;    // 128-row query blocks per (b, hq)
+  int n_kblk;    // 128-key blocks per (b, hk)
+  float c;       // scale * log2(e)
+  float scale;
+  int bias_vec;  // bias rows allow 8-byte loads (Nk % 4 == 0)
+  int64_t rows;  // B * Hq * Nq
+};
+
+__device__ __forceinline__ int sw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Direct LDS loads of an R x D tile (16-bit, row-major in HBM at a buffer
+// resource, first row at byte soff) into the swizzled LDS layout.  Load i of
+// wave w fills LDS bytes [1 KB * (w*NI + i), +1 KB) of the tile, lane l the
+// 16 bytes at l*16; off[i] is the lane's source offset within the tile.
+template <int R, int D>
+struct TileLoad {
+  static constexpr int RB = D * 2;
+  static constexpr int CPR = RB / 16;
+  static constexpr int NI = R * CPR / kBwdThreads;
+  static_assert(NI * kBwdThreads == R * CPR, "tile must split into whole wave loads");
+  int off[NI];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q = (wave * NI + i) * 64 + lane;
+      const int row = q / CPR, pc = q % CPR;
+      off[i] = row * RB + ((pc ^ sw(row)) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* lds, int wave,
+                                        uint32_t soff) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (wave * NI + i) * 1024), 16,
+                                               unsigned(off[i]), soff, 0, 0);
+  }
+};
+
+// Per-lane LDS offsets for reading MFMA operands out of a swizzled tile with
+// RB bytes per row.
+//  row_off[st]: the lane's 16-byte chunk 2*st + g of row ln (A/B operand with
+//    the contraction along the row: lane = row, 8 consecutive columns);
+//  tr_off[db]: the lane's 8-byte piece for ds_read_b64_tr_b16 over the 16-row
+//    group at rows (4g + (lane>>2 & 3)) and (that + 8), column block db: the
+//    lane receives 4 consecutive rows of column 32*db + lane % 32 (within a
+//    16-lane group, lane 4a+b receives element b of the chunks read by lanes
+//    a, a+4, a+8, a+12).
+template <int D>
+struct Offsets {
+  static constexpr int RB = D * 2;
+  static constexpr int NS = D / 16;
+  static constexpr int NDB = D / 32;
+  int row_off[NS];
+  int tr_off[NDB];
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 5, ln = lane & 31;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) row_off[st] = ln * RB + (((2 * st + g) ^ sw(ln)) * 16);
+    const int r = 4 * g + ((lane >> 2) & 3);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+      tr_off[db] = r * RB + ((c ^ sw(r)) * 16) + 8 * (lane & 1);
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::Frag lds_frag(const char* p) {
+  return __builtin_bit_cast(typename Elem<T>::Frag, *reinterpret_cast<const u32x4*>(p));
+}
+
+// Two transposed reads (rows +0 and +8 of a 16-row group) -> one MFMA fragment.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::Frag lds_frag_tr(const char* p, int rb8) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + rb8));
+  const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(typename Elem<T>::Frag, u32x4{lw[0], lw[1], hw[0], hw[1]});
+}
+
+// Registers 8h..8h+7 of a 32x32 accumulator, rounded to T as one fragment.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::Frag pack_half(const f32x16& x, int h) {
+  f32x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = x[8 * h + i];
+  return Elem<T>::pack8(v);
+}
+
+// Store a transposed 32 x (32*NDB) accumulator (lane = output row, register r
+// of block db = column 32*db + 8*(r/4) + 4*g + r%4) times `mul` as row `row`
+// of a row-major [.., D] tensor: one v_permlane32_swap per word pair gives each
+// lane 8 consecutive columns, written as one 16-byte store.
+template <typename T, int NDB>
+__device__ __forceinline__ void store_rows(T* dst_row, const f32x16 (&acc)[NDB], float mul,
+                                           int g, bool ok) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      f32x4 a4, b4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a4[e] = acc[db][8 * pr + e] * mul;
+        b4[e] = acc[db][8 * pr + 4 + e] * mul;
+      }
+      const u32x2 aw = Elem<T>::narrow4(a4), bw = Elem<T>::narrow4(b4);
+      u32x4 out;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const auto r = __builtin_amdgcn_permlane32_swap(u32(aw[e]), u32(bw[e]), false, false);
+        const u32 r0 = r[0], r1 = r[1];
+        out[e] = r0;
+        out[2 + e] = r1;
+      }
+      if (ok) *reinterpret_cast<u32x4*>(dst_row + db * 32 + 16 * pr + 8 * g) = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// delta = rowsum(dO o O) and lse2 = LSE * log2(e), one row per D/8 lanes.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;  // lanes per row (8 elements, 16 bytes each)
+  constexpr int RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR;
+  const T* o = static_cast<const T*>(p.o);
+  const T* dout = static_cast<const T*>(p.dout);
+  for (int64_t row = int64_t(blockIdx.x) * RPB + tid / LPR; row < p.rows;
+       row += int64_t(gridDim.x) * RPB) {
+    const u32x4 ow = *reinterpret_cast<const u32x4*>(o + row * D + sub * 8);
+    const u32x4 gw = *reinterpret_cast<const u32x4*>(dout + row * D + sub * 8);
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(Elem<T>::widen(ow[w] & 0xffffu), Elem<T>::widen(gw[w] & 0xffffu), acc);
+      acc = fmaf(Elem<T>::widen(ow[w] >> 16), Elem<T>::widen(gw[w] >> 16), acc);
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if (sub == 0) {
+      p.delta[row] = acc;
+      const float l = p.lse[row];
+      p.lse2[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (b, hq, 128-row query block), 64-key tiles.
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL, bool BIAS>
+__global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) {
+  using E = Elem<T>;
+  using Frag = typename E::Frag;
+  constexpr int BN = kKTile;
+  constexpr int NS = D / 16, NDB = D / 32, NKB = BN / 32;
+  constexpr int RB = D * 2;
+  constexpr int TILE = BN * RB;  // bytes per K (or V) tile
+  __shared__ __attribute__((aligned(16))) char smem[2][2 * TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, ln = lane & 31;
+
+  // heaviest causal blocks first (as in the forward); non-causal: head-major
+  int bh, tile;
+  if (CAUSAL) {
+    bh = int(blockIdx.x % unsigned(p.BH));
+    const int rank = int(blockIdx.x / unsigned(p.BH));
+    const int half = (p.n_qblk + 1) / 2;
+    tile = rank < half ? p.n_qblk - 1 - rank : rank - half;
+  } else {
+    bh = int(blockIdx.x / unsigned(p.n_qblk));
+    tile = int(blockIdx.x % unsigned(p.n_qblk));
+  }
+  const int b = bh / p.Hq, hk = (bh - b * p.Hq) / p.group;
+  const int64_t kv_head = int64_t(b) * p.Hkv + hk;
+  const int64_t row_base = int64_t(bh) * p.Nq;
+  const T* Qh = static_cast<const T*>(p.q) + row_base * D;
+  const T* Gh = static_cast<const T*>(p.dout) + row_base * D;
+  const T* Kh = static_cast<const T*>(p.k) + kv_head * p.Nk * D;
+  const T* Vh = static_cast<const T*>(p.v) + kv_head * p.Nk * D;
+  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(Qh, uint32_t(p.Nq) * RB);
+  const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(Gh, uint32_t(p.Nq) * RB);
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh, uint32_t(p.Nk) * RB);
+  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh, uint32_t(p.Nk) * RB);
+
+  const int q_blk = tile * 128;
+  const int wq0 = q_blk + wave * 32;
+  const int qi = wq0 + ln;
+  const bool wave_has_rows = wq0 < p.Nq;
+  const int wq_last = min(wq0 + 31, p.Nq - 1);
+  const int blk_last = min(q_blk + 127, p.Nq - 1);
+
+  // Q and dO rows of this lane: B operands of S^T = K Q^T and dP^T = V dO^T
+  Frag qf[NS], gf[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const int off = qi * RB + (16 * st + 8 * g) * 2;
+    qf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(q_rs, off, 0, 0));
+    gf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(g_rs, off, 0, 0));
+  }
+  const bool row_ok = qi < p.Nq;
+  const float lse2 = row_ok ? p.lse2[row_base + qi] : INFINITY;
+  const float dlt = row_ok ? p.delta[row_base + qi] : 0.f;
+
+  // bias rows of this block (resource over the block's rows)
+  const T* bblk = BIAS ? static_cast<const T*>(p.bias) + (row_base + q_blk) * p.Nk
+                       : static_cast<const T*>(p.q);
+  const __amdgpu_buffer_rsrc_t b_rs =
+      make_rsrc(bblk, BIAS ? uint32_t(blk_last - q_blk + 1) * uint32_t(p.Nk) * 2 : 0u);
+
+  TileLoad<BN, D> tl;
+  tl.init(wave, lane);
+  Offsets<D> of;
+  of.init(lane);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  int n_kv = (p.Nk + BN - 1) / BN;
+  if (CAUSAL) n_kv = min(n_kv, blk_last / BN + 1);
+
+  auto issue = [&](int j, int buf) {
+    tl.issue(k_rs, smem[buf], wave, uint32_t(j) * BN * RB);
+    tl.issue(v_rs, smem[buf] + TILE, wave, uint32_t(j) * BN * RB);
+  };
+
+  auto compute = [&](int j, int buf) {
+    const char* sK = smem[buf];
+    const char* sV = smem[buf] + TILE;
+    const int key0 = j * BN;
+    f32x16 s[NKB], dp[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const Frag kf = lds_frag<T>(sK + kb * 32 * RB + of.row_off[st]);
+        s[kb] = E::mma(kf, qf[st], st == 0 ? f32x16{} : s[kb]);
+      }
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const Frag vf = lds_frag<T>(sV + kb * 32 * RB + of.row_off[st]);
+        dp[kb] = E::mma(vf, gf[st], st == 0 ? f32x16{} : dp[kb]);
+      }
+    }
+    // register r of block kb: key key0 + kb*32 + 8*(r/4) + 4*g + r%4 of row qi
+    const bool need_mask = (key0 + BN > p.Nk) || (CAUSAL && key0 + BN - 1 > wq0);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float bvals[16];
+      if constexpr (BIAS) {
+        const int row_off = (qi - q_blk) * p.Nk + key0 + kb * 32 + 4 * g;
+        if (p.bias_vec) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(b_rs, (row_off + 8 * q4) * 2, 0, 0);
+            bvals[4 * q4 + 0] = E::widen(w[0] & 0xffffu);
+            bvals[4 * q4 + 1] = E::widen(w[0] >> 16);
+            bvals[4 * q4 + 2] = E::widen(w[1] & 0xffffu);
+            bvals[4 * q4 + 3] = E::widen(w[1] >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            bvals[r] = E::widen(__builtin_amdgcn_raw_buffer_load_b16(
+                b_rs, (row_off + 8 * (r >> 2) + (r & 3)) * 2, 0, 0));
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float t = BIAS ? fmaf(s[kb][r], p.c, fmaf(bvals[r], kLog2e, -lse2))
+                       : fmaf(s[kb][r], p.c, -lse2);
+        if (need_mask) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= p.Nk || (CAUSAL && key > qi)) t = -INFINITY;
+        }
+        const float pr = __builtin_amdgcn_exp2f(t);
+        s[kb][r] = pr * (dp[kb][r] - dlt);  // dS^T
+      }
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const Frag dsf = pack_half<T>(s[kb], h);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const Frag kt = lds_frag_tr<T>(sK + (kb * 32 + 16 * h) * RB + of.tr_off[db], 8 * RB);
+          acc[db] = E::mma(kt, dsf, acc[db]);
+        }
+      }
+  };
+
+  if (n_kv > 0) {
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    __syncthreads();
+  }
+  for (int j = 0; j < n_kv; ++j) {
+    const int cur = j & 1;
+    if (j + 1 < n_kv) issue(j + 1, cur ^ 1);
+    const bool active = wave_has_rows && (!CAUSAL || j * BN <= wq_last);
+    if (active) compute(j, cur);
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    __syncthreads();
+  }
+
+  T* dst = static_cast<T*>(p.dq) + (row_base + qi) * D;
+  store_rows<T, NDB>(dst, acc, p.scale, g, row_ok);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (b, hk, 128-key block), 64-row query tiles over
+// the group's packed rows r = (hq - hk*group)*Nq + i (query position r % Nq).
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL, bool BIAS>
+__global__ __launch_bounds__(kBwdThreads, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(BwdParams p) {
+  using E = Elem<T>;
+  using Frag = typename E::Frag;
+  constexpr int BQ = kQTile;
+  constexpr int NS = D / 16, NDB = D / 32, NQB = BQ / 32;
+  constexpr int RB = D * 2;
+  constexpr int TILE = BQ * RB;               // bytes per Q (or dO) tile
+  constexpr bool KV_LDS = (D == 128);         // K/V of the block in LDS, else registers
+  constexpr int KVB = KV_LDS ? 128 * RB : 16; // bytes per K (or V) block in LDS
+  // per stage: Q tile, dO tile, lse2[BQ], delta[BQ]
+  constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + 2 * KVB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, ln = lane & 31;
+
+  // causal: low key blocks see the most query rows; heavy blocks first
+  const int bhk = int(blockIdx.x % unsigned(p.BHkv));
+  const int rank = int(blockIdx.x / unsigned(p.BHkv));
+  int kt;
+  if (CAUSAL) {
+    const int half = (p.n_kblk + 1) / 2;
+    kt = rank < half ? rank : p.n_kblk - 1 - (rank - half);
+  } else {
+    kt = rank;
+  }
+  const int b = bhk / p.Hkv, hk = bhk - b * p.Hkv;
+  const int64_t kv_head = int64_t(b) * p.Hkv + hk;
+  const int64_t row_base = (int64_t(b) * p.Hq + int64_t(hk) * p.group) * p.Nq;
+  const int R = p.group * p.Nq;  // packed query rows of this KV head
+  const T* Kh = static_cast<const T*>(p.k) + kv_head * p.Nk * D;
+  const T* Vh = static_cast<const T*>(p.v) + kv_head * p.Nk * D;
+  const T* Qg = static_cast<const T*>(p.q) + row_base * D;
+  const T* Gg = static_cast<const T*>(p.dout) + row_base * D;
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh, uint32_t(p.Nk) * RB);
+  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh, uint32_t(p.Nk) * RB);
+  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(Qg, uint32_t(R) * RB);
+  const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(Gg, uint32_t(R) * RB);
+  const __amdgpu_buffer_rsrc_t l_rs = make_rsrc(p.lse2 + row_base, uint32_t(R) * 4);
+  const __amdgpu_buffer_rsrc_t d_rs = make_rsrc(p.delta + row_base, uint32_t(R) * 4);
+
+  const int k_blk = kt * 128;
+  const int kw0 = k_blk + wave * 32;  // first key of this wave
+  const int kj = kw0 + ln;            // the key this lane owns
+
+  TileLoad<BQ, D> tl;
+  tl.init(wave, lane);
+  Offsets<D> of;
+  of.init(lane);
+
+  // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T
+  Frag kf[KV_LDS ? 1 : NS], vf[KV_LDS ? 1 : NS];
+  char* sKV = smem + 2 * STAGE;
+  if constexpr (KV_LDS) {
+    TileLoad<128, D> kl;
+    kl.init(wave, lane);
+    kl.issue(k_rs, sKV, wave, uint32_t(k_blk) * RB);
+    kl.issue(v_rs, sKV + KVB, wave, uint32_t(k_blk) * RB);
+  } else {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int off = kj * RB + (16 * st + 8 * g) * 2;
+      kf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(k_rs, off, 0, 0));
+      vf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(v_rs, off, 0, 0));
+    }
+  }
+
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+
+  // Query positions covered by packed rows [r0, r1]: a run inside one head
+  // covers r0 % Nq .. r1 % Nq; a run across a head boundary is taken to cover
+  // 0 .. Nq-1 (a safe over-estimate).
+  auto pos_max = [&](int r0, int r1) {
+    return (r0 / p.Nq == r1 / p.Nq) ? r1 % p.Nq : p.Nq - 1;
+  };
+  auto pos_min = [&](int r0, int r1) { return (r0 / p.Nq == r1 / p.Nq) ? r0 % p.Nq : 0; };
+  const int n_t = (R + BQ - 1) / BQ;
+  // a query tile matters to this workgroup unless every one of its queries
+  // precedes every key of the block (causal)
+  auto tile_visible = [&](int t) {
+    if (!CAUSAL) return true;
+    const int r0 = t * BQ, r1 = min(r0 + BQ, R) - 1;
+    return pos_max(r0, r1) >= k_blk;
+  };
+  auto next_visible = [&](int t) {
+    while (t < n_t && !tile_visible(t)) ++t;
+    return t;
+  };
+
+  auto issue = [&](int t, int buf) {
+    char* st = smem + buf * STAGE;
+    const uint32_t soff = uint32_t(t) * BQ * RB;
+    tl.issue(q_rs, st, wave, soff);
+    tl.issue(g_rs, st + TILE, wave, soff);
+    // lse2 and delta: 64 floats each, by 16 lanes of waves 0 and 1
+    if (wave == 0) {
+      if (lane < 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(l_rs, (lds_void*)(st + 2 * TILE), 16,
+                                                 unsigned(lane * 16), uint32_t(t) * BQ * 4, 0, 0);
+    } else if (wave == 1) {
+      if (lane < 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d_rs, (lds_void*)(st + 2 * TILE + BQ * 4), 16,
+                                                 unsigned(lane * 16), uint32_t(t) * BQ * 4, 0, 0);
+    }
+  };
+
+  auto compute = [&](int t, int buf) {
+    const char* sQ = smem + buf * STAGE;
+    const char* sG = sQ + TILE;
+    const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
+    const float* sD = sL + BQ;
+    const int r0 = t * BQ;
+    const bool straddle = (r0 / p.Nq) != ((r0 + BQ - 1) / p.Nq);
+    const int pos0 = r0 % p.Nq;
+    // bias rows of this tile (reads past the group's rows or keys return 0)
+    const T* btile = BIAS ? static_cast<const T*>(p.bias) + (row_base + r0) * p.Nk
+                          : static_cast<const T*>(p.q);
+    const __amdgpu_buffer_rsrc_t b_rs =
+        make_rsrc(btile, BIAS ? uint32_t(min(BQ, R - r0)) * uint32_t(p.Nk) * 2 : 0u);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int rb0 = r0 + qb * 32;  // first packed row of this 32-row block
+      if (rb0 >= R) break;
+      if (CAUSAL && pos_max(rb0, min(rb0 + 31, R - 1)) < kw0) continue;  // all masked
+      f32x16 s, dp;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const Frag qa = lds_frag<T>(sQ + qb * 32 * RB + of.row_off[st]);
+        const Frag kb = KV_LDS ? lds_frag<T>(sKV + wave * 32 * RB + of.row_off[st]) : kf[st];
+        s = E::mma(qa, kb, st == 0 ? f32x16{} : s);
+      }
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const Frag ga = lds_frag<T>(sG + qb * 32 * RB + of.row_off[st]);
+        const Frag vb =
+            KV_LDS ? lds_frag<T>(sKV + KVB + wave * 32 * RB + of.row_off[st]) : vf[st];
+        dp = E::mma(ga, vb, st == 0 ? f32x16{} : dp);
+      }
+      // register r: query row qb*32 + 8*(r/4) + 4*g + r%4 of the tile, key kj
+      const bool tail = rb0 + 32 > R;
+      const bool need_mask =
+          tail || (CAUSAL && pos_min(rb0, min(rb0 + 31, R - 1)) < kw0 + 31);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int qr = qb * 32 + 8 * q4 + 4 * g;  // tile row of register 4*q4
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + qr);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + qr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          float tv = fmaf(s[r], p.c, -l4[e]);
+          if constexpr (BIAS) {
+            // key kj's column of tile row qr + e (2-byte loads: the lanes of a
+            // wave read 32 adjacent keys of one row)
+            const u32 bw = __builtin_amdgcn_raw_buffer_load_b16(
+                b_rs, ((qr + e) * p.Nk + min(kj, p.Nk)) * 2, 0, 0);
+            tv = fmaf(E::widen(bw), kLog2e, tv);
+          }
+          if (need_mask) {
+            const int row = r0 + qr + e;
+            const int pos = straddle ? row % p.Nq : pos0 + qr + e;
+            if (row >= R || (CAUSAL && kj > pos)) tv = -INFINITY;
+          }
+          const float pr = __builtin_amdgcn_exp2f(tv);
+          s[r] = pr;
+          dp[r] = pr * (dp[r] - d4[e]);  // dS
+        }
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const Frag pf = pack_half<T>(s, h);
+        const Frag dsf = pack_half<T>(dp, h);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const Frag gt = lds_frag_tr<T>(sG + (qb * 32 + 16 * h) * RB + of.tr_off[db], 8 * RB);
+          dva[db] = E::mma(gt, pf, dva[db]);
+          const Frag qt = lds_frag_tr<T>(sQ + (qb * 32 + 16 * h) * RB + of.tr_off[db], 8 * RB);
+          dka[db] = E::mma(qt, dsf, dka[db]);
+        }
+      }
+    }
+  };
+
+  int t = next_visible(0);
+  if (t < n_t) issue(t, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+  __syncthreads();
+  int buf = 0;
+  while (t < n_t) {
+    const int tn = next_visible(t + 1);
+    if (tn < n_t) issue(tn, buf ^ 1);
+    compute(t, buf);
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    __syncthreads();
+    t = tn;
+    buf ^= 1;
+  }
+
+  const bool key_ok = kj < p.Nk;
+  T* dk_row = static_cast<T*>(p.dk) + (kv_head * p.Nk + kj) * D;
+  T* dv_row = static_cast<T*>(p.dv) + (kv_head * p.Nk + kj) * D;
+  store_rows<T, NDB>(dk_row, dka, p.scale, g, key_ok);
+  store_rows<T, NDB>(dv_row, dva, 1.f, g, key_ok);
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool bias, hipStream_t s, unsigned g_prep,
+                        unsigned g_dq, unsigned g_kv) {
+  void* args[] = {const_cast<BwdParams*>(&p)};
+  hipError_t e = hipSuccess;
+  if (g_prep) {
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_prep_kernel<T, D>), dim3(g_prep),
+                        dim3(256), args, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  const void* dq;
+  const void* kv;
+  if (causal) {
+    dq = bias ? reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, true>)
+              : reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, false>);
+    kv = bias ? reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, true>)
+              : reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, false>);
+  } else {
+    dq = bias ? reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, false, true>)
+              : reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, false, false>);
+    kv = bias ? reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, false, true>)
+              : reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, false, false>);
+  }
+  if (g_dq) {
+    e = hipLaunchKernel(dq, dim3(g_dq), dim3(kBwdThreads), args, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  if (g_kv) e = hipLaunchKernel(kv, dim3(g_kv), dim3(kBwdThreads), args, 0, s);
+  return e;
+}
+
+}  // namespace
+
+int launch_backward(const BwdArgs& a) {
+  BwdParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.bias = a.bias;
+  p.o = a.o;
+  p.dout = a.dout;
+  p.lse = a.lse;
+  p.delta = static_cast<float*>(a.workspace);
+  p.rows = int64_t(a.B) * a.Hq * a.Nq;
+  p.lse2 = p.delta + backward_lse2_offset(p.rows);
+  p.dq = a.dq;
+  p.dk = a.dk;
+  p.dv = a.dv;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.Nq = a.Nq;
+  p.Nk = a.Nk;
+  p.BH = a.B * a.Hq;
+  p.BHkv = a.B * a.Hkv;
+  p.group = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
+  p.n_qblk = (a.Nq + 127) / 128;
+  p.n_kblk = (a.Nk + 127) / 128;
+  p.c = a.scale * kLog2e;
+  p.scale = a.scale;
+  p.bias_vec = (a.Nk % 4) == 0;
+  const int64_t lpr = a.D / 8;
+  const int64_t rows_per_block = 256 / lpr;
+  const int64_t want = (p.rows + rows_per_block - 1) / rows_per_block;
+  const unsigned g_prep = unsigned(want < 16384 ? want : 16384);
+  const unsigned g_dq = unsigned(p.n_qblk) * unsigned(p.BH);
+  const unsigned g_kv = unsigned(p.n_kblk) * unsigned(p.BHkv);
+  hipStream_t s = static_cast<hipStream_t>(a.stream);
+  hipError_t e;
+  if (a.dtype == FA_DTYPE_BF16) {
+    e = a.D == 64 ? launch_bwd_d<__bf16, 64>(p, a.causal, a.bias, s, g_prep, g_dq, g_kv)
+                  : launch_bwd_d<__bf16, 128>(p, a.causal, a.bias, s, g_prep, g_dq, g_kv);
+  } else {
+    e = a.D == 64 ? launch_bwd_d<_Float16, 64>(p, a.causal, a.bias, s, g_prep, g_dq, g_kv)
+                  : launch_bwd_d<_Float16, 128>(p, a.causal, a.bias, s, g_prep, g_dq, g_kv);
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace fa

@@ -41,6 +41,36 @@ inline int64_t split_workspace_bytes(int64_t rows, int64_t D, int64_t splits) {
   return split_partial_o_bytes(rows, D, splits) + splits * rows * 4;
 }
 
+// Backward: gradients dq [B,Hq,Nq,D], dk and dv [B,Hkv,Nk,D] (16-bit types).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* bias;  // may be null
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* workspace;   // backward_workspace_bytes(B*Hq*Nq) bytes, 16-byte aligned
+  int B, Hq, Hkv, Nq, Nk, D;
+  float scale;
+  int causal;
+  int dtype;
+  void* stream;
+};
+
+// Arguments are already validated.  Returns FA_OK or FA_ERR_HIP.
+int launch_backward(const BwdArgs& a);
+
+// Backward workspace: delta fp32 [rows], then lse2 fp32 [rows] from the next
+// 256-byte boundary (rows = B*Hq*Nq).
+inline int64_t backward_lse2_offset(int64_t rows) { return (rows + 63) / 64 * 64; }  // floats
+inline int64_t backward_workspace_bytes(int64_t rows) {
+  return (backward_lse2_offset(rows) + rows) * 4;
+}
+
 // Largest key-split count accepted.
 constexpr int kMaxSplits = 1024;
 
