@@ -29,11 +29,8 @@
 //
 // LDS tiles are row-major and unpadded, filled straight from HBM by buffer
 // loads with the LDS flag; the 16-byte chunk c of tile row r is stored at
-// chunk c ^ sw(r), sw(r) = 2*(r & 3) | ((r >> 2) & 1).  That one swizzle keeps
-// both access patterns free of bank conflicts: 16-byte row reads (8 rows per
-// cycle, sw takes 8 distinct values over r = 0..7) and transposed reads (in a
-// 16-lane group, 4 rows r with sw(r) differing in bits 1-2, each reading 2
-// adjacent chunks).
+// chunk c ^ lds_swizzle<D>(r), which keeps both access patterns (16-byte row
+// reads and transposed reads) free of bank conflicts.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -76,8 +73,6 @@ struct BwdParams {
   int64_t rows;  // B * Hq * Nq
 };
 
-__device__ __forceinline__ int sw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
 // Direct LDS loads of an R x D tile (16-bit, row-major in HBM at a buffer
 // resource, first row at byte soff) into the swizzled LDS layout.  Load i of
 // wave w fills LDS bytes [1 KB * (w*NI + i), +1 KB) of the tile, lane l the
@@ -94,7 +89,7 @@ struct TileLoad {
     for (int i = 0; i < NI; ++i) {
       const int q = (wave * NI + i) * 64 + lane;
       const int row = q / CPR, pc = q % CPR;
-      off[i] = row * RB + ((pc ^ sw(row)) * 16);
+      off[i] = row * RB + ((pc ^ lds_swizzle<D>(row)) * 16);
     }
   }
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* lds, int wave,
@@ -110,28 +105,31 @@ struct TileLoad {
 // RB bytes per row.
 //  row_off[st]: the lane's 16-byte chunk 2*st + g of row ln (A/B operand with
 //    the contraction along the row: lane = row, 8 consecutive columns);
-//  tr_off[db]: the lane's 8-byte piece for ds_read_b64_tr_b16 over the 16-row
-//    group at rows (4g + (lane>>2 & 3)) and (that + 8), column block db: the
-//    lane receives 4 consecutive rows of column 32*db + lane % 32 (within a
-//    16-lane group, lane 4a+b receives element b of the chunks read by lanes
-//    a, a+4, a+8, a+12).
+//  tr_off[t][db]: the lane's 8-byte piece for ds_read_b64_tr_b16 over the
+//    16-row group at row 8*t + 4g + (lane>>2 & 3), column block db: the lane
+//    receives 4 consecutive rows of column 32*db + lane % 32 (within a 16-lane
+//    group, lane 4a+b receives element b of the chunks read by lanes a, a+4,
+//    a+8, a+12); t = 0 and t = 1 give the two halves of one MFMA fragment.
 template <int D>
 struct Offsets {
   static constexpr int RB = D * 2;
   static constexpr int NS = D / 16;
   static constexpr int NDB = D / 32;
   int row_off[NS];
-  int tr_off[NDB];
+  int tr_off[2][NDB];
   __device__ __forceinline__ void init(int lane) {
     const int g = lane >> 5, ln = lane & 31;
 #pragma unroll
-    for (int st = 0; st < NS; ++st) row_off[st] = ln * RB + (((2 * st + g) ^ sw(ln)) * 16);
-    const int r = 4 * g + ((lane >> 2) & 3);
+    for (int st = 0; st < NS; ++st)
+      row_off[st] = ln * RB + (((2 * st + g) ^ lds_swizzle<D>(ln)) * 16);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-      tr_off[db] = r * RB + ((c ^ sw(r)) * 16) + 8 * (lane & 1);
-    }
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int r = 8 * t + 4 * g + ((lane >> 2) & 3);
+        const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        tr_off[t][db] = r * RB + ((c ^ lds_swizzle<D>(r)) * 16) + 8 * (lane & 1);
+      }
   }
 };
 
@@ -140,11 +138,12 @@ __device__ __forceinline__ typename Elem<T>::Frag lds_frag(const char* p) {
   return __builtin_bit_cast(typename Elem<T>::Frag, *reinterpret_cast<const u32x4*>(p));
 }
 
-// Two transposed reads (rows +0 and +8 of a 16-row group) -> one MFMA fragment.
+// Two transposed reads (rows +0..3 and +8..11 of a 16-row group, this lane's
+// pieces at grp + off0 and grp + off1) -> one MFMA fragment.
 template <typename T>
-__device__ __forceinline__ typename Elem<T>::Frag lds_frag_tr(const char* p, int rb8) {
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + rb8));
+__device__ __forceinline__ typename Elem<T>::Frag lds_frag_tr(const char* grp, int off0, int off1) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(grp + off0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(grp + off1));
   const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
   return __builtin_bit_cast(typename Elem<T>::Frag, u32x4{lw[0], lw[1], hw[0], hw[1]});
 }
@@ -361,7 +360,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
         const Frag dsf = pack_half<T>(s[kb], h);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const Frag kt = lds_frag_tr<T>(sK + (kb * 32 + 16 * h) * RB + of.tr_off[db], 8 * RB);
+          const Frag kt = lds_frag_tr<T>(sK + (kb * 32 + 16 * h) * RB, of.tr_off[0][db], of.tr_off[1][db]);
           acc[db] = E::mma(kt, dsf, acc[db]);
         }
       }
@@ -570,9 +569,9 @@ __global__ __launch_bounds__(kBwdThreads, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_ke
         const Frag dsf = pack_half<T>(dp, h);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const Frag gt = lds_frag_tr<T>(sG + (qb * 32 + 16 * h) * RB + of.tr_off[db], 8 * RB);
+          const Frag gt = lds_frag_tr<T>(sG + (qb * 32 + 16 * h) * RB, of.tr_off[0][db], of.tr_off[1][db]);
           dva[db] = E::mma(gt, pf, dva[db]);
-          const Frag qt = lds_frag_tr<T>(sQ + (qb * 32 + 16 * h) * RB + of.tr_off[db], 8 * RB);
+          const Frag qt = lds_frag_tr<T>(sQ + (qb * 32 + 16 * h) * RB, of.tr_off[0][db], of.tr_off[1][db]);
           dka[db] = E::mma(qt, dsf, dka[db]);
         }
       }

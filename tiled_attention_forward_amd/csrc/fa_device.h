@@ -106,6 +106,38 @@ __device__ __forceinline__ float partner_sum(float x) {
   return a + b;
 }
 
+// LDS tiles of 16-bit K, V, Q or dO rows are stored unpadded, the 16-byte
+// chunk c of tile row r at chunk c ^ lds_swizzle<D>(r).  The LDS serves 256
+// bytes per cycle (64 banks of 4 bytes): a ds_read_b128 serves 16 lanes per
+// cycle, a ds_read_b64_tr_b16 32 lanes.  The swizzle keeps both patterns the
+// kernels use free of bank conflicts:
+//  * row reads: 16 lanes read the same logical chunk of 16 consecutive rows;
+//  * transposed reads: 32 lanes read 4 consecutive rows, 4 adjacent chunks each.
+// With D = 64 a row is 128 bytes, so even and odd rows sit in different bank
+// halves and the swizzle needs only bits 1-3 of r; with D = 128 a row covers
+// all 64 banks and it uses bits 0-3.  Only r mod 16 matters.
+template <int D>
+__device__ __forceinline__ int lds_swizzle(int r) {
+  if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
+// Tiles read one way only can use a swizzle for that pattern alone:
+// lds_swizzle_rows<D> for row reads (16 distinct bank groups over 16 rows),
+// lds_swizzle_tr<D> for transposed reads.  The latter ignores bit 3 of r, so
+// the second transposed read of a 16-row group (rows +8) sits at a fixed
+// 8-row byte offset from the first.
+template <int D>
+__device__ __forceinline__ int lds_swizzle_rows(int r) {
+  if constexpr (D == 64) return (r >> 1) & 7;
+  return r & 15;
+}
+template <int D>
+__device__ __forceinline__ int lds_swizzle_tr(int r) {
+  if constexpr (D == 64) return ((r >> 1) & 1) << 2;
+  return (r & 3) << 2;
+}
+
 // Raw buffer resource over [base, base + bytes): loads past the end return 0
 // (the hardware range check), so tails need no branches.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

@@ -371,10 +371,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   u32x4 kreg[VTR ? 1 : KCH];
   u32x4 vreg[VTR ? 1 : VTPT][4];   // fp32 V^T path: 4 keys x VEC columns per task
 
-  // 16-bit layout.  Chunk c (16 bytes) of tile row r sits at chunk
-  // c ^ (r & 7) of the row in K and at chunk c ^ 2*(r & 3) in V, so that the
-  // 8 rows one ds_read_b128 of K serves per cycle, and the 4 rows of each
-  // 16-lane group of a transposed V read, fall in distinct banks.
+  // 16-bit layout: chunk c (16 bytes) of tile row r sits at chunk
+  // c ^ lds_swizzle_rows<D>(r) in K (read by rows) and c ^ lds_swizzle_tr<D>(r)
+  // in V (read transposed); both bank-conflict free.
   // Direct loads: load i of wave w fills LDS bytes [1 KB * (w*DNI + i), +1 KB)
   // of each buffer, lane l the 16 bytes at l*16; the lane's source offset
   // (without the tile's first key) is precomputed.
@@ -383,26 +382,26 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   for (int i = 0; i < DNI; ++i) {
     const int q = (wave * DNI + i) * 64 + lane;   // physical chunk index in the tile
     const int row = q / CPR, pc = q % CPR;
-    dma_k[i] = (row * D + (pc ^ (row & 7)) * VEC) * ESZ;
-    dma_v[i] = (row * D + (pc ^ ((row & 3) << 1)) * VEC) * ESZ;
+    dma_k[i] = (row * D + (pc ^ lds_swizzle_rows<D>(row)) * VEC) * ESZ;
+    dma_v[i] = (row * D + (pc ^ lds_swizzle_tr<D>(row)) * VEC) * ESZ;
   }
   // K operand reads: lane (row ln of a 32-key block, lane half g) reads
   // logical chunk 2*st + g.
   int k_off[VTR ? NS : 1];
 #pragma unroll
   for (int st = 0; st < (VTR ? NS : 1); ++st)
-    k_off[st] = ln * RB + (((2 * st + g) ^ (ln & 7)) * 16);
+    k_off[st] = ln * RB + (((2 * st + g) ^ lds_swizzle_rows<D>(ln)) * 16);
   // Transposed V reads (ds_read_b64_tr_b16): within each 16-lane group, lane
   // 4a+b receives element b of the 8-byte chunks read by lanes a, a+4, a+8,
-  // a+12.  So lane s of the group reads row 4g + s/4 of the key group, at
-  // column 32*db + 16*(lane/16 % 2) + 4*(s % 4); it then holds 4 consecutive
-  // keys of column 32*db + lane % 32.
+  // a+12.  So lane s of the group reads row 4g + s/4 (and 8 rows further for
+  // the second read) of the 16-key group, at column 32*db + 16*(lane/16 % 2) +
+  // 4*(s % 4); it then holds 4 consecutive keys of column 32*db + lane % 32.
   int v_off[VTR ? NDB : 1];
 #pragma unroll
   for (int db = 0; db < (VTR ? NDB : 1); ++db) {
-    const int r4 = (lane >> 2) & 3;
+    const int r = 4 * g + ((lane >> 2) & 3);
     const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    v_off[db] = (4 * g + r4) * RB + ((c ^ (r4 << 1)) * 16) + 8 * (lane & 1);
+    v_off[db] = r * RB + ((c ^ lds_swizzle_tr<D>(r)) * 16) + 8 * (lane & 1);
   }
 
   // Issue the direct LDS loads of tile j into buffer buf (16-bit types).
