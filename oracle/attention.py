@@ -84,13 +84,15 @@ def softmax_two_pass(s):
     return p, m, l
 
 
-def attention_head_rows(q_rows, k, v, *, rows, scale, causal, bias_rows=None):
+def attention_head_rows(q_rows, k, v, *, rows, scale, causal, bias_rows=None, window=None):
     """O and LSE for selected query rows of one (batch, query head).
 
     q_rows    [n, D]  the query rows
     rows      [n]     their absolute query indices (used by the causal mask)
     k, v      [Nk, D] the key/value rows of the KV head these queries read
     bias_rows [n, Nk] additive logit term for those rows, or None
+    window    None, or W >= 1 with causal: key j is visible to row i only if
+              i - W < j <= i (a sliding window of the W most recent keys)
 
     Row i of the output depends only on q_i, on K, V and on bias row i, so a
     subset of rows is the same definition evaluated on fewer rows.
@@ -104,6 +106,8 @@ def attention_head_rows(q_rows, k, v, *, rows, scale, causal, bias_rows=None):
     if causal:
         j = np.arange(nk, dtype=np.int64)
         s = np.where(j[None, :] > rows[:, None], -np.inf, s)
+        if window is not None:
+            s = np.where(j[None, :] <= rows[:, None] - int(window), -np.inf, s)
     p, m, l = softmax_two_pass(s)
     o = p @ v
     lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
@@ -124,13 +128,18 @@ def _check_shapes(q, k, v, bias):
     return b, hq, hkv, nq, nk, d
 
 
-def attention_forward(q, k, v, bias=None, *, scale=None, causal=False):
+def attention_forward(q, k, v, bias=None, *, scale=None, causal=False, window=None):
     """Full attention forward, one (b, hq) at a time.
 
     q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D], bias [B,Hq,Nq,Nk] or None.
-    ``scale=None`` means 1/sqrt(D).  Returns ``(O [B,Hq,Nq,D], LSE [B,Hq,Nq])``
-    in float64.
+    ``scale=None`` means 1/sqrt(D).  ``window`` (with ``causal``) limits each
+    row i to the keys i - window < j <= i: the sliding-window attention that
+    "FlashAttention principles and Triton practice", §3.1, and the kwkr.cn
+    tutorial's closing remarks name as a mask variant of the same kernel.
+    Returns ``(O [B,Hq,Nq,D], LSE [B,Hq,Nq])`` in float64.
     """
+    if window is not None and (not causal or int(window) < 1):
+        raise ValueError("window needs causal=True and window >= 1")
     b_, hq_, hkv, nq, nk, d = _check_shapes(q, k, v, bias)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -143,7 +152,7 @@ def attention_forward(q, k, v, bias=None, *, scale=None, causal=False):
             hk = h // group
             o[b, h], lse[b, h] = attention_head_rows(
                 q[b, h], k[b, hk], v[b, hk], rows=rows, scale=scale, causal=causal,
-                bias_rows=None if bias is None else bias[b, h])
+                bias_rows=None if bias is None else bias[b, h], window=window)
     return o, lse
 
 
@@ -282,7 +291,7 @@ def merge_partials(o_parts, lse_parts):
     return o_out, lse_out
 
 
-def attention_backward(q, k, v, dout, bias=None, *, scale=None, causal=False):
+def attention_backward(q, k, v, dout, bias=None, *, scale=None, causal=False, window=None):
     """Gradients of the forward definition above with respect to q, k and v.
 
     The forward keeps only O and the per-row statistic and recomputes S and P
@@ -301,8 +310,11 @@ def attention_backward(q, k, v, dout, bias=None, *, scale=None, causal=False):
     The bias term receives dS itself and is treated as a constant here (its
     gradient is not returned); LSE is an auxiliary output with no incoming
     gradient.  Rows that see no key have P = 0 and contribute nothing.
+    ``window`` masks as in ``attention_forward``.
     Returns ``(dQ, dK, dV)`` in float64 with the shapes of q, k, v.
     """
+    if window is not None and (not causal or int(window) < 1):
+        raise ValueError("window needs causal=True and window >= 1")
     b_, hq_, hkv, nq, nk, d = _check_shapes(q, k, v, bias)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -323,6 +335,8 @@ def attention_backward(q, k, v, dout, bias=None, *, scale=None, causal=False):
                 i = np.arange(nq)[:, None]
                 j = np.arange(nk)[None, :]
                 s = np.where(j > i, -np.inf, s)
+                if window is not None:
+                    s = np.where(j <= i - int(window), -np.inf, s)
             p, _, _ = softmax_two_pass(s)
             do = dout[b, h]
             dv[b, hk] += p.T @ do
