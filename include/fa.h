@@ -100,6 +100,21 @@ int fa_forward(const void* q, const void* k, const void* v, const void* bias,
                float scale, int causal, int dtype, void* stream);
 
 /*
+ * Causal sliding-window attention: fa_forward with causal = 1 and each query
+ * row i limited to its window most recent keys, i - window < j <= i (the
+ * window mask that "FlashAttention principles and Triton practice",
+ * xnwp.cn/news/15505, §3.1, and the kwkr.cn/news/592482 tutorial's closing
+ * remarks name as a variant of the same kernel).  Key tiles wholly outside a
+ * row block's windows are skipped, so the work grows with Nq * window rather
+ * than Nq * Nk.  window >= 1 (FA_ERR_BAD_SIZE otherwise; window >= Nk is the
+ * plain causal result); everything else as fa_forward.
+ */
+int fa_forward_window(const void* q, const void* k, const void* v, const void* bias,
+                      void* o, float* lse,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                      float scale, int64_t window, int dtype, void* stream);
+
+/*
  * Key-split ("flash-decode") forward.
  *
  * The same operation as fa_forward, for problems whose query-row blocks alone
@@ -217,6 +232,17 @@ int fa_backward(const void* q, const void* k, const void* v, const void* bias,
                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
                 float scale, int causal, int dtype,
                 void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Backward of fa_forward_window: as fa_backward, with causal = 1 and the same
+ * window (window >= 1, FA_ERR_BAD_SIZE otherwise).
+ */
+int fa_backward_window(const void* q, const void* k, const void* v, const void* bias,
+                       const void* o, const float* lse, const void* dout,
+                       void* dq, void* dk, void* dv,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                       float scale, int64_t window, int dtype,
+                       void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Workspace bytes of fa_backward through *bytes: float32 [B*Hq*Nq] twice,
  * the second part from the next 256-byte boundary.  Pure host code. */

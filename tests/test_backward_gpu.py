@@ -137,3 +137,27 @@ def test_backward_full_size_heads(gpu_device, name):
         _log(compare((dq[sl], dk[sl], dv[sl]), ref, w.dtype, f"{name} b{bb} h{h}"))
     del q, k, v, dout, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+WINDOW_CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, bias, window
+    (1, 2, 2, 300, 300, 64, "bf16", False, 37),
+    (1, 4, 1, 200, 260, 128, "bf16", True, 100),     # GQA, bias, Nk > Nq
+    (2, 2, 2, 513, 513, 64, "fp16", False, 129),
+    (1, 5, 1, 64, 64, 64, "bf16", False, 5),          # group 5: row tiles cross heads
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_window_backward(gpu_device, case):
+    B, Hq, Hkv, Nq, Nk, D, dt, bias, win = case
+    w = custom(B, Hq, Hkv, Nq, Nk, D, dt, True, bias)
+    _log(f"window backward case {case}")
+    q, k, v, b = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=42))
+    dout = _dout(q.shape, 42, q.dtype, gpu_device)
+    o, lse = binding.forward(q, k, v, b, causal=True, scale=w.scale, window=win)
+    got = binding.backward(q, k, v, o, lse, dout, b, causal=True, scale=w.scale, window=win)
+    torch.cuda.synchronize()
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(dout), None if b is None else f64(b),
+                             scale=w.scale, causal=True, window=win)
+    _log(compare(got, ref, dt, str(case)))

@@ -48,7 +48,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"fa_check_args", "fa_forward", "fa_forward_split", "fa_merge",
                           "fa_split_count", "fa_split_workspace_bytes", "fa_backward",
-                          "fa_backward_workspace_bytes", "fa_status_string", "fa_version"}
+                          "fa_backward_workspace_bytes", "fa_forward_window",
+                          "fa_backward_window", "fa_status_string", "fa_version"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
@@ -246,3 +247,18 @@ def test_backward_rejections_before_launch():
                       dv=None, workspace=None) == 0
     # no query rows but keys present: dk and dv are still written (zeros), so needed
     assert bwd_status(Nq=0, dk=None) == 1
+
+
+def test_window_rejections_before_launch():
+    lib = binding.load_library()
+    a = dict(OK_ARGS)
+    args = (a["q"], a["k"], a["v"], a["bias"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+            a["Nq"], a["Nk"], a["D"], a["scale"])
+    assert lib.fa_forward_window(*args, 0, a["dtype"], None) == 2
+    assert lib.fa_forward_window(*args, -3, a["dtype"], None) == 2
+    assert lib.fa_forward_window(*args, 1 << 30, a["dtype"], None) == 9
+    assert lib.fa_forward_window(*args[:11], 96, a["scale"], 16, a["dtype"], None) == 4
+    bargs = (a["q"], a["k"], a["v"], None, a["o"], a["lse"], GO, DQ, DK, DV, a["B"], a["Hq"],
+             a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"])
+    assert lib.fa_backward_window(*bargs, 0, a["dtype"], WS, 1 << 40, None) == 2
+    assert lib.fa_backward_window(*bargs, 8, binding.FA_DTYPE_FP32, WS, 1 << 40, None) == 5

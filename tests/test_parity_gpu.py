@@ -163,3 +163,56 @@ def test_full_size_sampled(gpu_device, name):
         assert torch.equal(o[:, :, 0, :], v0)
     del q, k, v, bias, o, lse
     torch.cuda.empty_cache()
+
+
+WINDOW_CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, bias, window
+    (1, 2, 2, 300, 300, 64, "bf16", False, 1),
+    (1, 2, 2, 300, 300, 64, "bf16", False, 37),      # inside one key tile
+    (1, 2, 1, 513, 513, 64, "fp16", True, 100),      # across tiles, GQA, bias
+    (2, 4, 2, 1000, 1000, 128, "bf16", False, 256),
+    (1, 2, 2, 700, 900, 128, "bf16", True, 129),     # Nk > Nq
+    (1, 2, 2, 200, 200, 64, "fp32", False, 64),
+    (1, 2, 2, 200, 200, 64, "bf16", False, 200),     # window = Nk: plain causal
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_window_forward(gpu_device, case):
+    """Causal sliding window (fa_forward_window) against the oracle's window mask."""
+    from oracle import attention_forward
+    B, Hq, Hkv, Nq, Nk, D, dt, bias, win = case
+    w = custom(B, Hq, Hkv, Nq, Nk, D, dt, True, bias)
+    _log(f"window case {case}")
+    q, k, v, b = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=41))
+    o, lse = binding.forward(q, k, v, b, causal=True, scale=w.scale, window=win)
+    torch.cuda.synchronize()
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v), None if b is None else f64(b),
+                                     scale=w.scale, causal=True, window=win)
+    from tests.parity import assert_within, errors
+    st = errors(f64(o), lse.cpu().numpy(), o_ref, l_ref)
+    _log(st)
+    assert_within(st, dt, str(case))
+    if win >= Nk:
+        o2, l2 = run_gpu(q, k, v, b, w.scale, True)
+        assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+def test_window_full_size_sampled(gpu_device):
+    """The headline shape with a 1024-key window, sampled rows against the oracle."""
+    from oracle import attention_head_rows
+    w = WORKLOADS["b2_h16_s4096_d64_bf16_causal"]
+    q, k, v, _ = make_inputs(w, seed=0, device=gpu_device)
+    o, lse = binding.forward(q, k, v, None, causal=True, scale=w.scale, window=1024)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.Nq, 40, seed=3)
+    rt = torch.as_tensor(rows, device=gpu_device)
+    from tests.parity import assert_within, errors
+    for bb, h in ((0, 0), (1, 15)):
+        o_ref, l_ref = attention_head_rows(f64(q[bb, h].index_select(0, rt)), f64(k[bb, h]),
+                                           f64(v[bb, h]), rows=rows, scale=w.scale, causal=True,
+                                           window=1024)
+        st = errors(f64(o[bb, h].index_select(0, rt)), lse[bb, h].index_select(0, rt).cpu().numpy(),
+                    o_ref, l_ref)
+        _log(st)
+        assert_within(st, "bf16", f"window 1024 b{bb} h{h}")

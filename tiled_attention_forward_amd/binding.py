@@ -55,6 +55,12 @@ def load_library():
     lib.fa_check_args.restype = i32
     lib.fa_forward.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32, i32, i32, p]
     lib.fa_forward.restype = i32
+    lib.fa_forward_window.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32, i64,
+                                      i32, p]
+    lib.fa_forward_window.restype = i32
+    lib.fa_backward_window.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64,
+                                       f32, i64, i32, p, i64, p]
+    lib.fa_backward_window.restype = i32
     lib.fa_forward_split.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32, i32,
                                      i32, i64, p, i64, p]
     lib.fa_forward_split.restype = i32
@@ -179,14 +185,16 @@ def _outputs(q, out, lse):
     return out, lse
 
 
-def forward(q, k, v, bias=None, *, causal=False, scale=None, out=None, lse=None, stream=None):
+def forward(q, k, v, bias=None, *, causal=False, scale=None, out=None, lse=None, stream=None,
+            window=None):
     """O, LSE = attention(q, k, v [, bias]) on the GPU through fa_forward.
 
     q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D], bias [B,Hq,Nq,Nk] or None: contiguous
     CUDA tensors of one dtype (bf16, fp16 or fp32).  ``scale=None`` means
     1/sqrt(D).  ``out``/``lse`` may be preallocated ([B,Hq,Nq,D] dtype and
     [B,Hq,Nq] float32).  Runs on ``stream`` (a torch.cuda.Stream) or the
-    current stream.
+    current stream.  ``window`` (requires ``causal``) calls
+    fa_forward_window: row i sees keys i - window < j <= i.
     """
     import torch
     lib = load_library()
@@ -196,10 +204,18 @@ def forward(q, k, v, bias=None, *, causal=False, scale=None, out=None, lse=None,
     out, lse = _outputs(q, out, lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                        bias.data_ptr() if bias is not None else None,
-                        out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, D, float(scale),
-                        int(bool(causal)), _dtype_code(q), stream.cuda_stream)
+    if window is not None:
+        if not causal:
+            raise ValueError("window requires causal=True")
+        st = lib.fa_forward_window(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                   bias.data_ptr() if bias is not None else None,
+                                   out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, D,
+                                   float(scale), int(window), _dtype_code(q), stream.cuda_stream)
+    else:
+        st = lib.fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            bias.data_ptr() if bias is not None else None,
+                            out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, D, float(scale),
+                            int(bool(causal)), _dtype_code(q), stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, fa_status_string(st))
     return out, lse
@@ -269,12 +285,13 @@ def merge(part_o, part_lse, dtype, *, out=None, lse=None, stream=None):
 
 
 def backward(q, k, v, o, lse, dout, bias=None, *, causal=False, scale=None, dq=None, dk=None,
-             dv=None, workspace=None, stream=None):
+             dv=None, workspace=None, stream=None, window=None):
     """dQ, dK, dV of attention(q, k, v [, bias]) through fa_backward.
 
     ``o`` and ``lse`` are the outputs of ``forward`` on the same arguments and
     ``dout`` the gradient with respect to ``o``.  bf16/fp16 tensors; outputs
-    and the workspace are allocated with torch unless given.
+    and the workspace are allocated with torch unless given.  ``window``
+    (requires ``causal``) calls fa_backward_window.
     """
     import torch
     lib = load_library()
@@ -292,12 +309,18 @@ def backward(q, k, v, o, lse, dout, bias=None, *, causal=False, scale=None, dq=N
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = lib.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                         bias.data_ptr() if bias is not None else None, o.data_ptr(),
-                         lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                         dv.data_ptr(), B, Hq, Hkv, Nq, Nk, D, float(scale), int(bool(causal)),
-                         _dtype_code(q), workspace.data_ptr(),
-                         workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(),
+            bias.data_ptr() if bias is not None else None, o.data_ptr(), lse.data_ptr(),
+            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nk, D,
+            float(scale))
+    tail = (_dtype_code(q), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            stream.cuda_stream)
+    if window is not None:
+        if not causal:
+            raise ValueError("window requires causal=True")
+        st = lib.fa_backward_window(*ptrs, int(window), *tail)
+    else:
+        st = lib.fa_backward(*ptrs, int(bool(causal)), *tail)
     if st != FA_OK:
         raise FaError(st, fa_status_string(st))
     return dq, dk, dv

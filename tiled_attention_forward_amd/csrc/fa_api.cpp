@@ -71,10 +71,11 @@ extern "C" int fa_check_args(const void* q, const void* k, const void* v, const 
   return FA_OK;
 }
 
-extern "C" int fa_forward(const void* q, const void* k, const void* v, const void* bias,
-                          void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
-                          int64_t Nk, int64_t D, float scale, int causal, int dtype,
-                          void* stream) {
+namespace {
+
+int forward_common(const void* q, const void* k, const void* v, const void* bias, void* o,
+                   float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                   int64_t D, float scale, int causal, int window, int dtype, void* stream) {
   const int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal,
                                dtype);
   if (st != FA_OK) return st;
@@ -94,9 +95,30 @@ extern "C" int fa_forward(const void* q, const void* k, const void* v, const voi
   a.D = int(D);
   a.scale = scale;
   a.causal = causal != 0;
+  a.window = window;
   a.dtype = dtype;
   a.stream = stream;
   return fa::launch_forward(a);
+}
+
+}  // namespace
+
+extern "C" int fa_forward(const void* q, const void* k, const void* v, const void* bias,
+                          void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                          int64_t Nk, int64_t D, float scale, int causal, int dtype,
+                          void* stream) {
+  return forward_common(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, 0, dtype,
+                        stream);
+}
+
+extern "C" int fa_forward_window(const void* q, const void* k, const void* v, const void* bias,
+                                 void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                                 int64_t Nq, int64_t Nk, int64_t D, float scale, int64_t window,
+                                 int dtype, void* stream) {
+  if (window < 1) return FA_ERR_BAD_SIZE;
+  if (window >= (int64_t(1) << 30)) return FA_ERR_TOO_LARGE;
+  return forward_common(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, 1, int(window),
+                        dtype, stream);
 }
 
 namespace {
@@ -194,6 +216,7 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, con
   a.D = int(D);
   a.scale = scale;
   a.causal = causal != 0;
+  a.window = 0;
   a.dtype = dtype;
   a.stream = stream;
   return fa::launch_forward_split(a, int(num_splits), workspace);
@@ -231,11 +254,13 @@ extern "C" int fa_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, in
   return FA_OK;
 }
 
-extern "C" int fa_backward(const void* q, const void* k, const void* v, const void* bias,
-                           const void* o, const float* lse, const void* dout, void* dq, void* dk,
-                           void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
-                           int64_t D, float scale, int causal, int dtype, void* workspace,
-                           int64_t workspace_bytes, void* stream) {
+namespace {
+
+int backward_common(const void* q, const void* k, const void* v, const void* bias, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv, int64_t B,
+                    int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, float scale,
+                    int causal, int window, int dtype, void* workspace, int64_t workspace_bytes,
+                    void* stream) {
   if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;  // 16-bit types only
   int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
   if (st != FA_OK) return st;
@@ -297,9 +322,33 @@ extern "C" int fa_backward(const void* q, const void* k, const void* v, const vo
   a.D = int(D);
   a.scale = scale;
   a.causal = causal != 0;
+  a.window = window;
   a.dtype = dtype;
   a.stream = stream;
   return fa::launch_backward(a);
+}
+
+}  // namespace
+
+extern "C" int fa_backward(const void* q, const void* k, const void* v, const void* bias,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                           void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                           int64_t D, float scale, int causal, int dtype, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+  return backward_common(q, k, v, bias, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, D, scale,
+                         causal, 0, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa_backward_window(const void* q, const void* k, const void* v, const void* bias,
+                                  const void* o, const float* lse, const void* dout, void* dq,
+                                  void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                                  int64_t Nq, int64_t Nk, int64_t D, float scale, int64_t window,
+                                  int dtype, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+  if (window < 1) return FA_ERR_BAD_SIZE;
+  if (window >= (int64_t(1) << 30)) return FA_ERR_TOO_LARGE;
+  return backward_common(q, k, v, bias, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, D, scale,
+                         1, int(window), dtype, workspace, workspace_bytes, stream);
 }
 
 extern "C" const char* fa_status_string(int status) {

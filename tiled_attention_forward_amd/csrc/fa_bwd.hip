@@ -70,6 +70,7 @@ struct BwdParams {
   float c;       // scale * log2(e)
   float scale;
   int bias_vec;  // bias rows allow 8-byte loads (Nk % 4 == 0)
+  int window;    // causal sliding window (keys i-window+1 .. i), 0 = none
   int64_t rows;  // B * Hq * Nq
 };
 
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (b, hq, 128-row query block), 64-key tiles.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL, bool BIAS>
+template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW>
 __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
@@ -293,6 +294,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
 
   int n_kv = (p.Nk + BN - 1) / BN;
   if (CAUSAL) n_kv = min(n_kv, blk_last / BN + 1);
+  // sliding window (causal only): row i sees keys i-W+1 .. i
+  const int W = (CAUSAL && WINDOW) ? p.window : 0;
+  const int j_lo = W > 0 ? min(n_kv, max(0, q_blk - W + 1) / BN) : 0;
+  const int wave_key_lo = W > 0 ? max(0, wq0 - W + 1) : 0;
 
   auto issue = [&](int j, int buf) {
     tl.issue(k_rs, smem[buf], wave, uint32_t(j) * BN * RB);
@@ -318,7 +323,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
       }
     }
     // register r of block kb: key key0 + kb*32 + 8*(r/4) + 4*g + r%4 of row qi
-    const bool need_mask = (key0 + BN > p.Nk) || (CAUSAL && key0 + BN - 1 > wq0);
+    const bool need_mask = (key0 + BN > p.Nk) || (CAUSAL && key0 + BN - 1 > wq0) ||
+                           (W > 0 && key0 <= wq0 + 31 - W);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       float bvals[16];
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
                        : fmaf(s[kb][r], p.c, -lse2);
         if (need_mask) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= p.Nk || (CAUSAL && key > qi)) t = -INFINITY;
+          if (key >= p.Nk || (CAUSAL && key > qi) || (W > 0 && key <= qi - W)) t = -INFINITY;
         }
         const float pr = __builtin_amdgcn_exp2f(t);
         s[kb][r] = pr * (dp[kb][r] - dlt);  // dS^T
@@ -366,15 +372,16 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
       }
   };
 
-  if (n_kv > 0) {
-    issue(0, 0);
+  if (n_kv > j_lo) {
+    issue(j_lo, 0);
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);
     __syncthreads();
   }
-  for (int j = 0; j < n_kv; ++j) {
-    const int cur = j & 1;
+  for (int j = j_lo; j < n_kv; ++j) {
+    const int cur = (j - j_lo) & 1;
     if (j + 1 < n_kv) issue(j + 1, cur ^ 1);
-    const bool active = wave_has_rows && (!CAUSAL || j * BN <= wq_last);
+    const bool active = wave_has_rows &&
+                        (!CAUSAL || (j * BN <= wq_last && j * BN + BN - 1 >= wave_key_lo));
     if (active) compute(j, cur);
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);
     __syncthreads();
@@ -388,7 +395,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
 // dK, dV: one workgroup per (b, hk, 128-key block), 64-row query tiles over
 // the group's packed rows r = (hq - hk*group)*Nq + i (query position r % Nq).
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL, bool BIAS>
+template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW>
 __global__ __launch_bounds__(kBwdThreads, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
@@ -471,12 +478,15 @@ __global__ __launch_bounds__(kBwdThreads, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_ke
   };
   auto pos_min = [&](int r0, int r1) { return (r0 / p.Nq == r1 / p.Nq) ? r0 % p.Nq : 0; };
   const int n_t = (R + BQ - 1) / BQ;
+  // sliding window (causal only): the query at position i sees keys i-W+1 .. i
+  const int W = (CAUSAL && WINDOW) ? p.window : 0;
   // a query tile matters to this workgroup unless every one of its queries
-  // precedes every key of the block (causal)
+  // precedes every key of the block (causal), or comes after the block's last
+  // key by W or more (window)
   auto tile_visible = [&](int t) {
     if (!CAUSAL) return true;
     const int r0 = t * BQ, r1 = min(r0 + BQ, R) - 1;
-    return pos_max(r0, r1) >= k_blk;
+    return pos_max(r0, r1) >= k_blk && (W == 0 || pos_min(r0, r1) <= k_blk + 127 + W - 1);
   };
   auto next_visible = [&](int t) {
     while (t < n_t && !tile_visible(t)) ++t;
@@ -518,6 +528,7 @@ __global__ __launch_bounds__(kBwdThreads, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_ke
       const int rb0 = r0 + qb * 32;  // first packed row of this 32-row block
       if (rb0 >= R) break;
       if (CAUSAL && pos_max(rb0, min(rb0 + 31, R - 1)) < kw0) continue;  // all masked
+      if (W > 0 && pos_min(rb0, min(rb0 + 31, R - 1)) > kw0 + 31 + W - 1) continue;
       f32x16 s, dp;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
@@ -535,7 +546,8 @@ __global__ __launch_bounds__(kBwdThreads, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_ke
       // register r: query row qb*32 + 8*(r/4) + 4*g + r%4 of the tile, key kj
       const bool tail = rb0 + 32 > R;
       const bool need_mask =
-          tail || (CAUSAL && pos_min(rb0, min(rb0 + 31, R - 1)) < kw0 + 31);
+          tail || (CAUSAL && pos_min(rb0, min(rb0 + 31, R - 1)) < kw0 + 31) ||
+          (W > 0 && pos_max(rb0, min(rb0 + 31, R - 1)) >= kw0 + W);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int qr = qb * 32 + 8 * q4 + 4 * g;  // tile row of register 4*q4
@@ -555,7 +567,7 @@ __global__ __launch_bounds__(kBwdThreads, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_ke
           if (need_mask) {
             const int row = r0 + qr + e;
             const int pos = straddle ? row % p.Nq : pos0 + qr + e;
-            if (row >= R || (CAUSAL && kj > pos)) tv = -INFINITY;
+            if (row >= R || (CAUSAL && kj > pos) || (W > 0 && kj <= pos - W)) tv = -INFINITY;
           }
           const float pr = __builtin_amdgcn_exp2f(tv);
           s[r] = pr;
@@ -612,16 +624,21 @@ hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool bias, hipStream_t 
   }
   const void* dq;
   const void* kv;
-  if (causal) {
-    dq = bias ? reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, true>)
-              : reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, false>);
-    kv = bias ? reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, true>)
-              : reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, false>);
+  if (causal && p.window > 0) {
+    dq = bias ? reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, true, true>)
+              : reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, false, true>);
+    kv = bias ? reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, true, true>)
+              : reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, false, true>);
+  } else if (causal) {
+    dq = bias ? reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, true, false>)
+              : reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, false, false>);
+    kv = bias ? reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, true, false>)
+              : reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, false, false>);
   } else {
-    dq = bias ? reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, false, true>)
-              : reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, false, false>);
-    kv = bias ? reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, false, true>)
-              : reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, false, false>);
+    dq = bias ? reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, false, true, false>)
+              : reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, false, false, false>);
+    kv = bias ? reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, false, true, false>)
+              : reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, false, false, false>);
   }
   if (g_dq) {
     e = hipLaunchKernel(dq, dim3(g_dq), dim3(kBwdThreads), args, 0, s);
@@ -660,6 +677,7 @@ int launch_backward(const BwdArgs& a) {
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
   p.bias_vec = (a.Nk % 4) == 0;
+  p.window = a.window;
   const int64_t lpr = a.D / 8;
   const int64_t rows_per_block = 256 / lpr;
   const int64_t want = (p.rows + rows_per_block - 1) / rows_per_block;

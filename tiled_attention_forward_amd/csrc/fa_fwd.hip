@@ -87,6 +87,7 @@ struct Params {
   float c;       // |scale| * log2(e), never 0 (see the launcher)
   u32 q_sign;    // sign bits XORed into Q when scale < 0
   int bias_vec;  // bias rows allow 16-byte vector loads
+  int window;         // causal sliding window (keys i-window+1 .. i), 0 = none
   // key-split path only: o and lse point at the fp32 partial outputs
   int n_splits;       // key ranges per row block
   int64_t part_rows;  // B * Hq * Nq, the row stride between splits
@@ -108,7 +109,8 @@ __device__ __forceinline__ int vt_pos_of_group(int kg) {  // kg = key / 4
 // contiguous in Q, O, LSE and bias), one workgroup per (batch, KV head,
 // 128-row block, key range); it writes the normalised partial O (fp32) and
 // partial LSE of its key range, to be combined by fa_merge_kernel.
-template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT>
+// WINDOW (with CAUSAL): sliding window of p.window keys per row.
+template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT, bool WINDOW>
 __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_kernel(Params p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
@@ -240,15 +242,21 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) qpos[qb] = SPLIT ? qi[qb] % p.Nq : qi[qb];
   const int wave_pos_max = pos_max(wq0, wq_last);
+  // Sliding window (causal only): the row at position i sees keys i-W+1 .. i.
+  const int W = (CAUSAL && WINDOW) ? p.window : 0;
+  const int wave_key_lo = W > 0 ? max(0, pos_min(wq0, wq_last) - W + 1) : 0;
 
   int n_kv = (p.Nk + BN - 1) / BN;
   if (CAUSAL) n_kv = min(n_kv, pos_max(q_blk, blk_last) / BN + 1);
+  // tiles wholly left of every row's window are skipped
+  const int j_lo = W > 0 ? min(n_kv, max(0, pos_min(q_blk, blk_last) - W + 1) / BN) : 0;
   // Key tiles [j_begin, j_end) of this workgroup: all visible tiles, or the
   // split's share of them (balanced, empty only when splits outnumber tiles).
-  int j_begin = 0, j_end = n_kv;
+  int j_begin = j_lo, j_end = n_kv;
   if constexpr (SPLIT) {
-    j_begin = int(int64_t(split) * n_kv / p.n_splits);
-    j_end = int(int64_t(split + 1) * n_kv / p.n_splits);
+    const int nt = n_kv - j_lo;
+    j_begin = j_lo + int(int64_t(split) * nt / p.n_splits);
+    j_end = j_lo + int(int64_t(split + 1) * nt / p.n_splits);
   }
 
   // ---- Q fragments: B operand of S^T = K Q^T, loaded once ---------------------
@@ -540,14 +548,16 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
       }
       const bool need_mask =
           (key0 + BN > p.Nk) ||
-          (CAUSAL && key0 + BN - 1 > pos_min(wq0 + 32 * qb, wq0 + 32 * qb + 31));
+          (CAUSAL && key0 + BN - 1 > pos_min(wq0 + 32 * qb, wq0 + 32 * qb + 31)) ||
+          (W > 0 && key0 <= pos_max(wq0 + 32 * qb, wq0 + 32 * qb + 31) - W);
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool dead = key >= p.Nk || (CAUSAL && key > qpos[qb]);
+            const bool dead = key >= p.Nk || (CAUSAL && key > qpos[qb]) ||
+                              (W > 0 && key <= qpos[qb] - W);
             if (dead) s[qb][kb][r] = -INFINITY;
           }
       }
@@ -657,10 +667,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
       dma_tile(j + 1, cur ^ 1);
       gload(j + 1);
     }
-    const bool active = wave_has_rows && (!CAUSAL || j * BN <= wave_pos_max);
+    // a wave skips tiles above its rows' diagonal and, with a window, tiles
+    // wholly left of its rows' windows
+    const bool active = wave_has_rows && (!CAUSAL || (j * BN <= wave_pos_max &&
+                                                      j * BN + BN - 1 >= wave_key_lo));
     if constexpr (BIAS) {
       const bool next_active =
-          has_next && wave_has_rows && (!CAUSAL || (j + 1) * BN <= wave_pos_max);
+          has_next && wave_has_rows &&
+          (!CAUSAL || ((j + 1) * BN <= wave_pos_max && (j + 1) * BN + BN - 1 >= wave_key_lo));
       if (next_active) load_bias(bnext, j + 1);
     }
     if (active) compute(j, cur);
@@ -825,17 +839,23 @@ __global__ __launch_bounds__(kMergeWaves * 64) void fa_merge_kernel(
   }
 }
 
-template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT>
+template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT,
+          bool WINDOW = false>
 hipError_t launch_one(const Params& p, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&p)};
   return hipLaunchKernel(
-      reinterpret_cast<const void*>(&fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT>),
+      reinterpret_cast<const void*>(&fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT, WINDOW>),
       dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
 template <typename T, int D, int BN, int QB, bool SPLIT>
 hipError_t launch_d(const Params& p, unsigned grid, hipStream_t s, bool causal, bool bias) {
   if (causal) {
+    if constexpr (!SPLIT) {
+      if (p.window > 0)
+        return bias ? launch_one<T, D, BN, QB, true, true, false, true>(p, grid, s)
+                    : launch_one<T, D, BN, QB, true, false, false, true>(p, grid, s);
+    }
     return bias ? launch_one<T, D, BN, QB, true, true, SPLIT>(p, grid, s)
                 : launch_one<T, D, BN, QB, true, false, SPLIT>(p, grid, s);
   }
@@ -855,6 +875,8 @@ hipError_t launch_t(const Params& p, unsigned grid, hipStream_t s, int D, bool c
   if (D == 64) {
     if constexpr (!std::is_same<T, float>::value && !SPLIT) {
       if (!bias) {
+        if (causal && p.window > 0)
+          return launch_one<T, 64, kBN64, kQB64, true, false, false, true>(p, grid, s);
         return causal ? launch_one<T, 64, kBN64, kQB64, true, false, false>(p, grid, s)
                       : launch_one<T, 64, kBN64, kQB64, false, false, false>(p, grid, s);
       }
@@ -889,6 +911,7 @@ Params make_params(const LaunchArgs& a, int rows_per_block, int n_rows) {
   const bool neg = a.scale < 0.f;
   p.q_sign = !neg ? 0u : (a.dtype == FA_DTYPE_FP32 ? 0x80000000u : 0x80008000u);
   p.bias_vec = (a.dtype == FA_DTYPE_FP32) ? (a.Nk % 4) == 0 : (a.Nk % 8) == 0;
+  p.window = a.window;
   p.n_splits = 1;
   p.part_rows = 0;
   return p;

@@ -16,6 +16,7 @@ struct LaunchArgs {
   int B, Hq, Hkv, Nq, Nk, D;
   float scale;
   int causal;
+  int window;     // causal sliding window, 0 = none
   int dtype;      // fa_dtype
   void* stream;   // hipStream_t
 };
@@ -57,6 +58,7 @@ struct BwdArgs {
   int B, Hq, Hkv, Nq, Nk, D;
   float scale;
   int causal;
+  int window;        // causal sliding window, 0 = none
   int dtype;
   void* stream;
 };
