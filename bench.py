@@ -125,14 +125,16 @@ def cpu_baseline_backward(w, q, k, v, dout, target_s: float):
             qs, gs = f(q[b:b + 1, hs]), f(dout[b:b + 1, hs])
             ks, vs = f(k[b:b + 1, hk:hk + 1]), f(v[b:b + 1, hk:hk + 1])
             t0 = time.perf_counter()
-            attention_backward(qs, ks, vs, gs, None, scale=w.scale, causal=w.causal)
+            attention_backward(qs, ks, vs, gs, None, scale=w.scale, causal=w.causal,
+                               window=w.window or None)
             t_used += time.perf_counter() - t0
             done += grp
             if t_used >= target_s:
                 break
         if t_used >= target_s:
             break
-    per_head = BACKWARD_FLOP_FACTOR * w.metric_flops() / (w.B * w.Hq)
+    per_head = BACKWARD_FLOP_FACTOR * (w.useful_flops() if w.window else w.metric_flops()) / (
+        w.B * w.Hq)
     return {"value": round(per_head * done / t_used / 1e12, 6), "unit": "TFLOPS",
             "cores": blas_threads(), "kind": "oracle",
             "sample": f"backward of {done} of {w.B * w.Hq} (batch, head) slices of {w.name}, "
@@ -157,12 +159,13 @@ def cpu_baseline(w, q, k, v, bias, target_s: float):
         vh = v[b, hk].float().cpu().numpy().astype(np.float64)
         bh = None if bias is None else bias[b, h].float().cpu().numpy().astype(np.float64)
         t0 = time.perf_counter()
-        attention_head_rows(qh, kh, vh, rows=rows, scale=w.scale, causal=w.causal, bias_rows=bh)
+        attention_head_rows(qh, kh, vh, rows=rows, scale=w.scale, causal=w.causal, bias_rows=bh,
+                            window=w.window or None)
         t_used += time.perf_counter() - t0
         done += 1
         if t_used >= target_s:
             break
-    per_head_flops = w.metric_flops() / (w.B * w.Hq)
+    per_head_flops = (w.useful_flops() if w.window else w.metric_flops()) / (w.B * w.Hq)
     return {"value": round(per_head_flops * done / t_used / 1e12, 6), "unit": "TFLOPS",
             "cores": blas_threads(), "kind": "oracle",
             "sample": f"{done} of {w.B * w.Hq} (batch, head) slices of {w.name}, fp64 NumPy, "
@@ -206,10 +209,13 @@ def main():
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws_bytes = binding.fa_backward_workspace_bytes(w.B, w.Hq, w.Nq)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-        entry = lib.fa_backward
+        binding.forward(q, k, v, None, causal=w.causal, scale=w.scale, out=o, lse=lse,
+                        window=w.window or None)
+        entry = lib.fa_backward_window if w.window else lib.fa_backward
         call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), None, o.data_ptr(), lse.data_ptr(),
                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.Hq,
-                     w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal), dtype_code,
+                     w.Hkv, w.Nq, w.Nk, w.D, float(w.scale),
+                     int(w.window) if w.window else int(w.causal), dtype_code,
                      workspace.data_ptr(), ws_bytes, stream.cuda_stream)
     elif w.path == "split":
         splits = args.splits or binding.fa_split_count(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D)
@@ -217,6 +223,9 @@ def main():
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         entry = lib.fa_forward_split
         call_args = call_args + (splits, workspace.data_ptr(), ws_bytes, stream.cuda_stream)
+    elif w.window:
+        entry = lib.fa_forward_window
+        call_args = call_args[:13] + (int(w.window), dtype_code, stream.cuda_stream)
     else:
         entry = lib.fa_forward
         call_args = call_args + (stream.cuda_stream,)
@@ -257,7 +266,10 @@ def main():
     assert torch.isfinite(lse).all(), "non-finite LSE in the benchmark output"
 
     fl = BACKWARD_FLOP_FACTOR if backward else 1.0
-    value = fl * w.metric_flops() / (ms_per_step / 1e3) / 1e12
+    # windowed attention: count the visible pairs only (the dense formula
+    # would credit work the window removes)
+    metric_flops = w.useful_flops() if w.window else w.metric_flops()
+    value = fl * metric_flops / (ms_per_step / 1e3) / 1e12
     peak = metrics.MFMA_PEAK_TFLOPS[w.dtype]
     ridge = peak * 1e12 / (metrics.HBM_PEAK_GBS * 1e9)   # flops per byte
     if not backward and w.useful_flops() / w.io_bytes() < ridge:
@@ -270,7 +282,10 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
     roof["traffic"] = traffic_for(w.name, args.pass_)
 
-    if backward:
+    if w.window:
+        metric = (f"attention {'backward ' if backward else ''}TFLOPS over visible pairs "
+                  f"({'2.5·' if backward else ''}4·D·pairs/t) at {w.name}")
+    elif backward:
         metric = f"attention backward TFLOPS (2.5·4·B·H·Nq·Nk·D/t) at {w.name}"
     elif w.name == HEADLINE:
         metric = METRIC
@@ -293,6 +308,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
                    "Nk": w.Nk, "D": w.D, "causal": w.causal, "bias": w.bias,
                    "path": w.path, "splits": splits, "pass": args.pass_,
+                   "window": w.window or None,
                    "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * value / metrics.MFMA_PEAK_TFLOPS["bf16"], 2),
         "useful_tflops": round(fl * w.useful_flops() / (ms_per_step / 1e3) / 1e12, 2),

@@ -21,7 +21,9 @@ Two more shapes exercise the key-split path, where row blocks alone leave most
 of the 256 compute units idle; the pages give no such benchmark, so they are
 synthetic choices: one decode step (Nq = 1) of the same 20/4-head, D = 128
 setup for 8 sequences over a 32768-entry KV cache, and a long sequence with
-only two heads (B = 1, H = 2, S = 16384, D = 64, 256 row blocks).
+only two heads (B = 1, H = 2, S = 16384, D = 64, 256 row blocks).  The
+sliding-window shape is the benchmark report shape with each row limited to
+its 1024 most recent keys.
 """
 
 from __future__ import annotations
@@ -47,6 +49,7 @@ class Workload:
     causal: bool
     bias: bool
     path: str = "fused"   # "fused": fa_forward; "split": fa_forward_split
+    window: int = 0       # causal sliding window (fa_forward_window), 0 = none
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -61,9 +64,14 @@ class Workload:
         return 4.0 * self.B * self.Hq * self.Nq * self.Nk * self.D
 
     def visible_pairs(self) -> int:
-        """Number of (query, key) pairs the mask leaves visible (top-left causal)."""
+        """Number of (query, key) pairs the mask leaves visible (top-left causal,
+        with the sliding window when there is one)."""
         if not self.causal:
             return self.B * self.Hq * self.Nq * self.Nk
+        if self.window:
+            per_head = sum(max(0, min(i, self.Nk - 1) - max(0, i - self.window + 1) + 1)
+                           for i in range(self.Nq))
+            return self.B * self.Hq * per_head
         per_head = 0
         # rows 0..Nq-1 see min(i+1, Nk) keys
         full = max(0, self.Nq - self.Nk)          # rows i >= Nk see all Nk keys
@@ -99,6 +107,8 @@ WORKLOADS = {
                  False, False, "split"),
         Workload("b1_h2_s16384_d64_bf16", 1, 2, 2, 16384, 16384, 64, "bf16", False, False,
                  "split"),
+        Workload("b2_h16_s4096_d64_bf16_swa1024", 2, 16, 16, 4096, 4096, 64, "bf16", True, False,
+                 window=1024),
     ]
 }
 
