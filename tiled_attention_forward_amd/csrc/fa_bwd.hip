@@ -46,6 +46,12 @@ namespace fa {
 namespace {
 
 constexpr int kBwdThreads = 256;  // 4 waves
+// dK/dV kernel at D = 64 without a logit term: 3 workgroups per compute unit
+// (168 VGPRs, a small spill) measured 11% faster than 2 (180 VGPRs) on the
+// B2 H16 S4096 causal backward; with a logit term the spill grows, so 2.
+#ifndef FA_DKDV_MINB64
+#define FA_DKDV_MINB64 3
+#endif
 constexpr int kQTile = 64;        // query rows per tile in the dK/dV kernel
 constexpr int kKTile = 64;        // keys per tile in the dQ kernel
 
@@ -396,7 +402,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
 // the group's packed rows r = (hq - hk*group)*Nq + i (query position r % Nq).
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW>
-__global__ __launch_bounds__(kBwdThreads, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads, (D == 64 ? (BIAS ? 2 : FA_DKDV_MINB64) : 1)) void fa_bwd_dkdv_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
   constexpr int BQ = kQTile;
