@@ -13,9 +13,8 @@
 //
 // Work layout (all choices made for CDNA4, not taken from the pages):
 //  * workgroup = 4 waves x 32 query rows = 128 rows of one (batch, query head);
-//    the 1-D grid lists the heaviest causal row blocks first, and consecutive
-//    blocks walk the heads so that a head's row blocks share one XCD when the
-//    head count is a multiple of 8;
+//    the 1-D grid lists the heaviest causal row blocks first and deals the
+//    blocks that read the same K/V rows to one XCD (see the id mapping);
 //  * each wave computes the transposed score block S^T = K . Q^T with
 //    32x32 MFMAs (bf16/fp16: v_mfma_f32_32x32x16, fp32: v_mfma_f32_32x32x2f32),
 //    so one lane holds one query row and 16 of the 32 keys of a block: row max
@@ -24,16 +23,19 @@
 //    lane owns the same query row in S^T and in O^T: the online-softmax
 //    rescale is a per-lane scalar and P feeds the MFMA B operand straight from
 //    the S^T registers without any shuffle;
-//  * K tiles sit in LDS row-major, V tiles transposed (d-major) with the keys
-//    of each 16-key group reordered so that every MFMA operand read is one
-//    16-byte ds_read per lane; rows are padded by 16 bytes so that 32 lanes
-//    reading 32 rows hit distinct banks;
-//  * two LDS buffers: tile j+1 is fetched from global memory into registers
-//    while tile j is being computed, then written to the other buffer; one
-//    barrier per tile;
+//  * bf16/fp16: K and V tiles go from HBM straight into LDS with buffer loads
+//    that carry the LDS flag, row-major and unpadded, the 16-byte chunks of
+//    each row XOR-swizzled so that both read patterns are free of bank
+//    conflicts; the V operand of P.V is read with the transposing
+//    ds_read_b64_tr_b16.  fp32: staged through registers, K padded, V stored
+//    transposed;
+//  * two LDS buffers: tile j+1 is requested while tile j is being computed;
+//    one barrier per tile;
 //  * exp is the hardware base-2 exponential with scale*log2(e) folded into one
-//    FMA; masks are applied only on tiles that cross the causal diagonal or
-//    the end of the keys, and tiles wholly above the diagonal are skipped.
+//    FMA; the rescale of the running output is skipped until the row max has
+//    grown by more than a threshold; masks are applied only on tiles that
+//    cross the causal diagonal, the window edge or the end of the keys, and
+//    tiles wholly outside every row's visible range are skipped.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -85,6 +87,7 @@ struct Params {
   int group;     // Hq / Hkv
   int n_qtiles;  // ceil(Nq / rows per workgroup)
   float c;       // |scale| * log2(e), never 0 (see the launcher)
+  float scale_abs;  // c / log2(e): the bias path scales in natural-log units
   u32 q_sign;    // sign bits XORed into Q when scale < 0
   int bias_vec;  // bias rows allow 16-byte vector loads
   int window;         // causal sliding window (keys i-window+1 .. i), 0 = none
@@ -151,19 +154,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, ln = lane & 31;
 
-  // Workgroup -> (head, query block).  Consecutive ids walk the heads, so
-  // with B*Hq a multiple of 8 all blocks of a head share one XCD (ids are
-  // dealt round-robin to the 8 XCDs).  Causal: the first half of the ranks
-  // take the heavy blocks in descending order and the second half the light
-  // ones in ascending order, so the two workgroups a CU receives from the
-  // two halves add up to about the same number of key tiles.
   // Workgroup id -> (head, query block).
-  //  * causal: ids are rank-major (id = rank * B*Hq + head) and the first
-  //    half of the ranks take the heavy query blocks in descending order,
-  //    the second half the light ones ascending, so co-resident workgroups
-  //    carry complementary amounts of work; with B*Hq a multiple of 8 all
-  //    blocks of a head also land on one XCD (ids are dealt round-robin to
-  //    the 8 XCDs), where they share the L2 copy of K and V;
+  //  * causal: ids are rank-major and the first half of the ranks take the
+  //    heavy query blocks in descending order, the second half the light ones
+  //    ascending, so co-resident workgroups carry complementary amounts of
+  //    work; the query heads of one KV head at one rank are dealt to one XCD
+  //    (ids go round-robin to the 8 XCDs), where they share the L2 copy of K
+  //    and V; with one query head per KV head and B*Hq a multiple of 8 all
+  //    blocks of a head land on one XCD;
   //  * non-causal (all blocks equal): the ids one XCD receives are renumbered
   //    to be consecutive in head-major order, so the query blocks of a head
   //    run at the same time on one XCD and re-read K and V from its L2.
@@ -188,8 +186,24 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   } else {
     int bh;
     if (CAUSAL) {
-      bh = int(blockIdx.x % unsigned(p.BH));
-      const int rank = int(blockIdx.x / unsigned(p.BH));
+      // Unit u = rank * (B*Hkv) + KV head: the `group` query heads of one KV
+      // head at one rank.  The ids come in runs of 8*group; in run k the id
+      // at offset r is member r/8 of unit 8k + r%8, so a unit's members all
+      // go to one XCD and stream the same K/V rows through its L2 (group = 1:
+      // the identity).  A tail shorter than a run keeps the plain order.
+      const unsigned G = unsigned(p.group), units_per_rank = unsigned(p.BH) / G;
+      const unsigned id = blockIdx.x, run = 8u * G, full = gridDim.x - gridDim.x % run;
+      unsigned unit, member;
+      if (id < full) {
+        const unsigned r = id % run;
+        unit = (id / run) * 8u + (r & 7u);
+        member = r >> 3;
+      } else {
+        unit = id / G;
+        member = id % G;
+      }
+      bh = int((unit % units_per_rank) * G + member);
+      const int rank = int(unit / units_per_rank);
       const int half = (p.n_qtiles + 1) / 2;
       tile = rank < half ? p.n_qtiles - 1 - rank : rank - half;
     } else {
@@ -216,6 +230,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh, uint32_t(p.Nk) * D * ESZ);
   const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh, uint32_t(p.Nk) * D * ESZ);
   const float c = p.c;
+  // Exponent factor.  Without a bias the row max and the exponent act on the
+  // raw scores s, p = 2^(s*c - m).  With one the logit t = s*|scale| + b is
+  // formed first (one FMA) and p = 2^(t*log2(e) - m).
+  const float scale_abs = p.scale_abs;
+  const float ce = BIAS ? kLog2e : c;
 
   const int q_blk = tile * BM;
   const int wq0 = q_blk + wave * QW;      // first row of this wave
@@ -544,7 +563,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            s[qb][kb][r] = fmaf(s[qb][kb][r], c, bias_at(qb, kb, r) * kLog2e);
+            s[qb][kb][r] = fmaf(s[qb][kb][r], scale_abs, bias_at(qb, kb, r));
       }
       const bool need_mask =
           (key0 + BN > p.Nk) ||
@@ -568,7 +587,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
       mx = partner_max(mx);
-      m_tile[qb] = BIAS ? mx : mx * c;  // c > 0, so max(s)*c = max(s*c)
+      m_tile[qb] = mx * ce;  // ce > 0, so max(s)*ce = max(s*ce)
       grow_any = grow_any || (m_tile[qb] > m_ref[qb] + kTau);  // -inf + kTau stays -inf
     }
     if (__builtin_amdgcn_ballot_w64(grow_any) != 0) {
@@ -596,7 +615,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float x = BIAS ? (s[qb][kb][r] + neg_m) : fmaf(s[qb][kb][r], c, neg_m);
+          const float x = fmaf(s[qb][kb][r], ce, neg_m);
           const float e = __builtin_amdgcn_exp2f(x);
           s[qb][kb][r] = e;
           rs[qb] += e;
@@ -908,6 +927,7 @@ Params make_params(const LaunchArgs& a, int rows_per_block, int n_rows) {
   float c = fabsf(a.scale) * kLog2e;
   if (!(c >= 1e-30f)) c = 1e-30f;
   p.c = c;
+  p.scale_abs = fmaxf(fabsf(a.scale), 1e-30f / kLog2e);
   const bool neg = a.scale < 0.f;
   p.q_sign = !neg ? 0u : (a.dtype == FA_DTYPE_FP32 ? 0x80000000u : 0x80008000u);
   p.bias_vec = (a.dtype == FA_DTYPE_FP32) ? (a.Nk % 4) == 0 : (a.Nk % 8) == 0;
