@@ -241,16 +241,22 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, ln = lane & 31;
 
-  // heaviest causal blocks first (as in the forward); non-causal: head-major
+  // Causal: heaviest blocks first (as in the forward), the query heads of one
+  // KV head at one rank dealt to one XCD.  Non-causal: head-major, the ids of
+  // one XCD consecutive, so that a head's blocks share that XCD's L2 copy of
+  // K and V.
   int bh, tile;
   if (CAUSAL) {
-    bh = int(blockIdx.x % unsigned(p.BH));
-    const int rank = int(blockIdx.x / unsigned(p.BH));
+    const unsigned G = unsigned(p.group), units_per_rank = unsigned(p.BH) / G;
+    const UnitMember um = xcd_group_units(blockIdx.x, gridDim.x, G);
+    bh = int((um.unit % units_per_rank) * G + um.member);
+    const int rank = int(um.unit / units_per_rank);
     const int half = (p.n_qblk + 1) / 2;
     tile = rank < half ? p.n_qblk - 1 - rank : rank - half;
   } else {
-    bh = int(blockIdx.x / unsigned(p.n_qblk));
-    tile = int(blockIdx.x % unsigned(p.n_qblk));
+    const unsigned logical = xcd_contiguous(blockIdx.x, gridDim.x);
+    bh = int(logical / unsigned(p.n_qblk));
+    tile = int(logical % unsigned(p.n_qblk));
   }
   const int b = bh / p.Hq, hk = (bh - b * p.Hq) / p.group;
   const int64_t kv_head = int64_t(b) * p.Hkv + hk;
@@ -418,15 +424,20 @@ __global__ __launch_bounds__(kBwdThreads, (D == 64 ? (BIAS ? 2 : FA_DKDV_MINB64)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, ln = lane & 31;
 
-  // causal: low key blocks see the most query rows; heavy blocks first
-  const int bhk = int(blockIdx.x % unsigned(p.BHkv));
-  const int rank = int(blockIdx.x / unsigned(p.BHkv));
-  int kt;
+  // Causal: low key blocks see the most query rows; heavy blocks first, rank
+  // major.  Non-causal: head-major with the ids of one XCD consecutive, so
+  // that the key blocks of a KV head run together on one XCD and stream the
+  // same Q and dO rows through its L2.
+  int bhk, kt;
   if (CAUSAL) {
+    bhk = int(blockIdx.x % unsigned(p.BHkv));
+    const int rank = int(blockIdx.x / unsigned(p.BHkv));
     const int half = (p.n_kblk + 1) / 2;
     kt = rank < half ? rank : p.n_kblk - 1 - (rank - half);
   } else {
-    kt = rank;
+    const unsigned logical = xcd_contiguous(blockIdx.x, gridDim.x);
+    bhk = int(logical / unsigned(p.n_kblk));
+    kt = int(logical % unsigned(p.n_kblk));
   }
   const int b = bhk / p.Hkv, hk = bhk - b * p.Hkv;
   const int64_t kv_head = int64_t(b) * p.Hkv + hk;

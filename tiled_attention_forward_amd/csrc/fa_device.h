@@ -145,4 +145,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
+// Workgroup ids are dealt round-robin to the 8 XCDs, each with its own L2.
+// Renumber so that the ids one XCD receives are consecutive: logical id
+// x*(full/8) + i for the i-th id of XCD x.  Used where all workgroups carry
+// equal work, so that the blocks of one head (consecutive logical ids) run on
+// one XCD at the same time and share its L2 copy of the head's operands.  The
+// last nblk % 8 ids keep their number.
+__device__ __forceinline__ unsigned xcd_contiguous(unsigned id, unsigned nblk) {
+  const unsigned full = nblk & ~7u;
+  return id < full ? (id & 7u) * (full >> 3) + (id >> 3) : id;
+}
+
+// Causal grids list their units rank-major (unit = rank * units_per_rank + u)
+// with `group` workgroups per unit, e.g. the query heads of one KV head.  The
+// ids come in runs of 8*group; in run k the id at offset r is member r/8 of
+// unit 8k + r%8, so the members of a unit all go to one XCD, one after the
+// other.  group = 1 is the identity; a tail shorter than a run keeps the plain
+// order (unit = id / group).
+struct UnitMember {
+  unsigned unit, member;
+};
+__device__ __forceinline__ UnitMember xcd_group_units(unsigned id, unsigned nblk, unsigned group) {
+  const unsigned run = 8u * group, full = nblk - nblk % run;
+  if (id < full) {
+    const unsigned r = id % run;
+    return {(id / run) * 8u + (r & 7u), r >> 3};
+  }
+  return {id / group, id % group};
+}
+
 }  // namespace fa

@@ -172,9 +172,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   int64_t row_base;  // global index (over B*Hq*Nq) of row 0 of this row space
   int n_rows;        // rows of this row space
   if constexpr (SPLIT) {
-    const unsigned nblk = gridDim.x, full = nblk & ~7u;
-    unsigned logical = blockIdx.x;
-    if (logical < full) logical = (logical & 7u) * (full >> 3) + (logical >> 3);
+    const unsigned logical = xcd_contiguous(blockIdx.x, gridDim.x);
     tile = int(logical % unsigned(p.n_qtiles));
     const unsigned rest = logical / unsigned(p.n_qtiles);
     split = int(rest % unsigned(p.n_splits));
@@ -186,30 +184,18 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   } else {
     int bh;
     if (CAUSAL) {
-      // Unit u = rank * (B*Hkv) + KV head: the `group` query heads of one KV
-      // head at one rank.  The ids come in runs of 8*group; in run k the id
-      // at offset r is member r/8 of unit 8k + r%8, so a unit's members all
-      // go to one XCD and stream the same K/V rows through its L2 (group = 1:
-      // the identity).  A tail shorter than a run keeps the plain order.
+      // unit = rank * (B*Hkv) + KV head: the `group` query heads of one KV
+      // head at one rank, dealt to one XCD, where they stream the same K/V
+      // rows through its L2
       const unsigned G = unsigned(p.group), units_per_rank = unsigned(p.BH) / G;
-      const unsigned id = blockIdx.x, run = 8u * G, full = gridDim.x - gridDim.x % run;
-      unsigned unit, member;
-      if (id < full) {
-        const unsigned r = id % run;
-        unit = (id / run) * 8u + (r & 7u);
-        member = r >> 3;
-      } else {
-        unit = id / G;
-        member = id % G;
-      }
+      const UnitMember um = xcd_group_units(blockIdx.x, gridDim.x, G);
+      const unsigned unit = um.unit, member = um.member;
       bh = int((unit % units_per_rank) * G + member);
       const int rank = int(unit / units_per_rank);
       const int half = (p.n_qtiles + 1) / 2;
       tile = rank < half ? p.n_qtiles - 1 - rank : rank - half;
     } else {
-      const unsigned nblk = gridDim.x, full = nblk & ~7u;
-      unsigned logical = blockIdx.x;
-      if (logical < full) logical = (logical & 7u) * (full >> 3) + (logical >> 3);
+      const unsigned logical = xcd_contiguous(blockIdx.x, gridDim.x);
       bh = int(logical / unsigned(p.n_qtiles));
       tile = int(logical % unsigned(p.n_qtiles));
     }
