@@ -58,6 +58,7 @@ __all__ = [
     "attention_partial",
     "merge_partials",
     "attention_backward",
+    "attention_chain",
 ]
 
 
@@ -346,3 +347,52 @@ def attention_backward(q, k, v, dout, bias=None, *, scale=None, causal=False, wi
             dq[b, h] = float(scale) * (ds @ k[b, hk])
             dk[b, hk] += float(scale) * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def attention_chain(q_layers, k_layers, v, *, scale=None, causal=False):
+    """Forward of the last layer of a Block Attention Residual chain.
+
+    "Block Attention Residual" Triton kernel post (iqiancheng.github.io), the
+    A_i formula and the block diagram: consecutive layers are grouped into
+    blocks of 4; inside a block, layer i adds the pre-softmax logits of layer
+    i-1 to its own scaled Q_i K_i^T before the softmax, and those logits
+    already carry layer i-2's, so the sum runs back to the block's first
+    layer; at a block boundary the residual is zero.
+
+    q_layers  list of the block's Q tensors up to the current layer, oldest
+              first, each [B, Hq, Nq, D]
+    k_layers  the matching K tensors, each [B, Hkv, Nk, D]
+    v         the current layer's V, [B, Hkv, Nk, D]
+
+    The steps follow the post's recursion, one (b, hq) at a time: the residual
+    starts at zero; each earlier layer l replaces it by its own logits
+    Q_l K_l^T * scale + residual; the current layer is then the forward above
+    with that residual as its additive logit term (none for a block's first
+    layer).  Every layer's product takes the same ``scale`` (the post divides
+    each by sqrt(d)); ``scale=None`` means 1/sqrt(D).  Returns ``(O, LSE)``.
+    """
+    n = len(q_layers)
+    if n < 1 or len(k_layers) != n:
+        raise ValueError("need as many K layers as Q layers, at least one")
+    q_cur, k_cur = q_layers[-1], k_layers[-1]
+    b_, hq_, hkv, nq, nk, d = _check_shapes(q_cur, k_cur, v, None)
+    for ql, kl in zip(q_layers, k_layers):
+        if tuple(ql.shape) != tuple(q_cur.shape) or tuple(kl.shape) != tuple(k_cur.shape):
+            raise ValueError("every layer of the chain has the same Q and K shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    group = hq_ // hkv
+    o = np.empty((b_, hq_, nq, d), dtype=np.float64)
+    lse = np.empty((b_, hq_, nq), dtype=np.float64)
+    rows = np.arange(nq, dtype=np.int64)
+    for b in range(b_):
+        for h in range(hq_):
+            hk = h // group
+            residual = None
+            for ql, kl in zip(q_layers[:-1], k_layers[:-1]):
+                logits = (_f64(ql[b, h]) @ _f64(kl[b, hk]).T) * float(scale)
+                residual = logits if residual is None else logits + residual
+            o[b, h], lse[b, h] = attention_head_rows(
+                q_cur[b, h], k_cur[b, hk], v[b, hk], rows=rows, scale=scale, causal=causal,
+                bias_rows=residual)
+    return o, lse
