@@ -6,7 +6,9 @@
 A step is one fa_forward call (one kernel launch) over the whole workload, with
 inputs already resident in HBM; for the key-split workloads it is one
 fa_forward_split call (the split kernel and the merge kernel, workspace
-allocated beforehand).  The default workload is B=2, H=16, S=4096,
+allocated beforehand); for the chain workload it is one fa_forward_chain call
+(the last layer of a 4-layer Block Attention Residual block, its logits
+recomputed from the Q and K of all four layers).  The default workload is B=2, H=16, S=4096,
 D=64, bf16, causal.  Timing follows the CUDA-event method of the Day 26 post
 (blog.ans20xx.com/posts/ai/day26): W untimed warm-up steps, then K steps with
 one event recorded before each step and one after the last, on the stream the
@@ -141,6 +143,37 @@ def cpu_baseline_backward(w, q, k, v, dout, target_s: float):
                       f"fp64 NumPy, {t_used:.1f} s"}
 
 
+def cpu_baseline_chain(w, q_layers, k_layers, v, target_s: float):
+    """Time the oracle's chain on whole heads until about target_s."""
+    import numpy as np
+
+    from oracle import attention_chain_head_rows
+
+    grp = w.Hq // w.Hkv
+    rows = np.arange(w.Nq)
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    done, t_used = 0, 0.0
+    for b in range(w.B):
+        for h in range(w.Hq):
+            hk = h // grp
+            qs = [f(t[b, h]) for t in q_layers]
+            ks = [f(t[b, hk]) for t in k_layers]
+            vh = f(v[b, hk])
+            t0 = time.perf_counter()
+            attention_chain_head_rows(qs, ks, vh, rows=rows, scale=w.scale, causal=w.causal)
+            t_used += time.perf_counter() - t0
+            done += 1
+            if t_used >= target_s:
+                break
+        if t_used >= target_s:
+            break
+    per_head = w.useful_flops() / (w.B * w.Hq)
+    return {"value": round(per_head * done / t_used / 1e12, 6), "unit": "TFLOPS",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hq} (batch, head) slices of {w.name}, fp64 NumPy, "
+                      f"{t_used:.1f} s"}
+
+
 def cpu_baseline(w, q, k, v, bias, target_s: float):
     """Time the oracle on whole heads of the same workload until about target_s."""
     import numpy as np
@@ -182,14 +215,19 @@ def main():
     import torch
 
     from tiled_attention_forward_amd import binding, metrics
-    from tiled_attention_forward_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+    from tiled_attention_forward_amd.workloads import (HEADLINE, WORKLOADS, make_chain_inputs,
+                                                       make_inputs)
 
     w = WORKLOADS[args.workload or HEADLINE]
     if args.path is not None and args.path != w.path:
         w = dataclasses.replace(w, path=args.path)
     dev = torch.device("cuda:0")
     lib = binding.load_library()
-    q, k, v, bias = make_inputs(w, seed=args.seed, device=dev)
+    if w.layers:
+        q_layers, k_layers, v = make_chain_inputs(w, w.layers, seed=args.seed, device=dev)
+        q, k, bias = q_layers[-1], k_layers[-1], None
+    else:
+        q, k, v, bias = make_inputs(w, seed=args.seed, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -199,6 +237,9 @@ def main():
                  w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal), dtype_code)
     splits = None
     backward = args.pass_ == "backward"
+    if w.layers and (backward or w.path != "fused"):
+        print("the chain workload is timed on the fused forward only", file=sys.stderr)
+        sys.exit(2)
     if backward:
         if w.bias or w.dtype == "fp32":
             print("the backward is timed on bias-free 16-bit workloads", file=sys.stderr)
@@ -223,6 +264,15 @@ def main():
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         entry = lib.fa_forward_split
         call_args = call_args + (splits, workspace.data_ptr(), ws_bytes, stream.cuda_stream)
+    elif w.layers:
+        import ctypes
+        ptrs = ctypes.c_void_p * w.layers
+        q_arr = ptrs(*[t.data_ptr() for t in q_layers])
+        k_arr = ptrs(*[t.data_ptr() for t in k_layers])
+        entry = lib.fa_forward_chain
+        call_args = (q_arr, k_arr, w.layers, v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal),
+                     dtype_code, stream.cuda_stream)
     elif w.window:
         entry = lib.fa_forward_window
         call_args = call_args[:13] + (int(w.window), dtype_code, stream.cuda_stream)
@@ -268,7 +318,7 @@ def main():
     fl = BACKWARD_FLOP_FACTOR if backward else 1.0
     # windowed attention: count the visible pairs only (the dense formula
     # would credit work the window removes)
-    metric_flops = w.useful_flops() if w.window else w.metric_flops()
+    metric_flops = w.useful_flops() if (w.window or w.layers) else w.metric_flops()
     value = fl * metric_flops / (ms_per_step / 1e3) / 1e12
     peak = metrics.MFMA_PEAK_TFLOPS[w.dtype]
     ridge = peak * 1e12 / (metrics.HBM_PEAK_GBS * 1e9)   # flops per byte
@@ -282,7 +332,10 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
     roof["traffic"] = traffic_for(w.name, args.pass_)
 
-    if w.window:
+    if w.layers:
+        metric = (f"chain attention TFLOPS over visible pairs (2·D·(layers+1)·pairs/t) at "
+                  f"{w.name}")
+    elif w.window:
         metric = (f"attention {'backward ' if backward else ''}TFLOPS over visible pairs "
                   f"({'2.5·' if backward else ''}4·D·pairs/t) at {w.name}")
     elif backward:
@@ -308,7 +361,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
                    "Nk": w.Nk, "D": w.D, "causal": w.causal, "bias": w.bias,
                    "path": w.path, "splits": splits, "pass": args.pass_,
-                   "window": w.window or None,
+                   "window": w.window or None, "layers": w.layers or None,
                    "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * value / metrics.MFMA_PEAK_TFLOPS["bf16"], 2),
         "useful_tflops": round(fl * w.useful_flops() / (ms_per_step / 1e3) / 1e12, 2),
@@ -317,8 +370,12 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = (cpu_baseline_backward(w, q, k, v, dout, args.cpu_seconds) if backward
-                               else cpu_baseline(w, q, k, v, bias, args.cpu_seconds))
+        if backward:
+            out["cpu_baseline"] = cpu_baseline_backward(w, q, k, v, dout, args.cpu_seconds)
+        elif w.layers:
+            out["cpu_baseline"] = cpu_baseline_chain(w, q_layers, k_layers, v, args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline(w, q, k, v, bias, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

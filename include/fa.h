@@ -115,6 +115,34 @@ int fa_forward_window(const void* q, const void* k, const void* v, const void* b
                       float scale, int64_t window, int dtype, void* stream);
 
 /*
+ * Block Attention Residual chain, forward of one layer ("Block Attention
+ * Residual" Triton kernel post, iqiancheng.github.io: the A_i formula and the
+ * 4-layer block diagram).  Inside a block, each layer adds the previous
+ * layer's pre-softmax logits to its own, and those carry the layer before, so
+ * layer p of a block (p = 0..3) sees
+ *     S = sum over l = 0..p of Q_l K_l^T * scale     (+ causal mask)
+ * and O = softmax(S) V_p, LSE as fa_forward.  The logits are recomputed tile
+ * by tile from the layers' Q and K; no Nq x Nk tensor is read or written.
+ *
+ *   q_layers, k_layers: HOST arrays of num_layers DEVICE pointers, oldest
+ *     layer first (the block's first layer) and the current layer last; every
+ *     Q_l is [B, Hq, Nq, D] and every K_l [B, Hkv, Nk, D], all of dtype, with
+ *     the GQA head mapping of fa_forward for every layer;
+ *   num_layers: 1 .. 4 (FA_ERR_BAD_SIZE otherwise); 1 is fa_forward without
+ *     a bias (a block's first layer);
+ *   v: the current layer's V, [B, Hkv, Nk, D];
+ *   o, lse, sizes, scale, causal, stream: as fa_forward; scale multiplies every
+ *     layer's product.
+ * bf16 and fp16 only (FA_ERR_DTYPE for fp32).  Errors as fa_forward for each
+ * layer's (Q_l, K_l) with v, o and lse, plus FA_ERR_NULL_POINTER for a NULL
+ * array.  The arrays are read during the call only.
+ */
+int fa_forward_chain(const void* const* q_layers, const void* const* k_layers,
+                     int64_t num_layers, const void* v, void* o, float* lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                     float scale, int causal, int dtype, void* stream);
+
+/*
  * Key-split ("flash-decode") forward.
  *
  * The same operation as fa_forward, for problems whose query-row blocks alone

@@ -59,6 +59,7 @@ __all__ = [
     "merge_partials",
     "attention_backward",
     "attention_chain",
+    "attention_chain_head_rows",
 ]
 
 
@@ -388,11 +389,26 @@ def attention_chain(q_layers, k_layers, v, *, scale=None, causal=False):
     for b in range(b_):
         for h in range(hq_):
             hk = h // group
-            residual = None
-            for ql, kl in zip(q_layers[:-1], k_layers[:-1]):
-                logits = (_f64(ql[b, h]) @ _f64(kl[b, hk]).T) * float(scale)
-                residual = logits if residual is None else logits + residual
-            o[b, h], lse[b, h] = attention_head_rows(
-                q_cur[b, h], k_cur[b, hk], v[b, hk], rows=rows, scale=scale, causal=causal,
-                bias_rows=residual)
+            o[b, h], lse[b, h] = attention_chain_head_rows(
+                [ql[b, h] for ql in q_layers], [kl[b, hk] for kl in k_layers], v[b, hk],
+                rows=rows, scale=scale, causal=causal)
     return o, lse
+
+
+def attention_chain_head_rows(q_rows_layers, k_layers, v, *, rows, scale, causal):
+    """``attention_chain`` for selected query rows of one (batch, query head).
+
+    q_rows_layers  per layer, oldest first, the [n, D] query rows
+    k_layers       per layer the [Nk, D] keys of the KV head these rows read
+    v              [Nk, D] the current layer's values
+    rows           [n] the rows' absolute query indices (for the causal mask)
+
+    The residual of row i depends only on row i of each Q layer, so a subset
+    of rows is the same recursion on fewer rows.
+    """
+    residual = None
+    for ql, kl in zip(q_rows_layers[:-1], k_layers[:-1]):
+        logits = (_f64(ql) @ _f64(kl).T) * float(scale)
+        residual = logits if residual is None else logits + residual
+    return attention_head_rows(q_rows_layers[-1], k_layers[-1], v, rows=rows, scale=scale,
+                               causal=causal, bias_rows=residual)

@@ -49,7 +49,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) == {"fa_check_args", "fa_forward", "fa_forward_split", "fa_merge",
                           "fa_split_count", "fa_split_workspace_bytes", "fa_backward",
                           "fa_backward_workspace_bytes", "fa_forward_window",
-                          "fa_backward_window", "fa_status_string", "fa_version"}
+                          "fa_backward_window", "fa_forward_chain", "fa_status_string",
+                          "fa_version"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
@@ -262,3 +263,28 @@ def test_window_rejections_before_launch():
              a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"])
     assert lib.fa_backward_window(*bargs, 0, a["dtype"], WS, 1 << 40, None) == 2
     assert lib.fa_backward_window(*bargs, 8, binding.FA_DTYPE_FP32, WS, 1 << 40, None) == 5
+
+
+def test_chain_rejections_before_launch():
+    Q0, K0 = 0x1000000000, 0x1100000000
+    a = dict(OK_ARGS)
+
+    def chain(qs, ks, n=None, **over):
+        b = dict(a, **over)
+        return binding.fa_forward_chain(qs, ks, b["v"], b["o"], b["lse"], b["B"], b["Hq"],
+                                        b["Hkv"], b["Nq"], b["Nk"], b["D"], b["scale"],
+                                        b["causal"], b["dtype"], None) if n is None else \
+            binding.load_library().fa_forward_chain(None, None, n, b["v"], b["o"], b["lse"],
+                                                    b["B"], b["Hq"], b["Hkv"], b["Nq"], b["Nk"],
+                                                    b["D"], b["scale"], b["causal"], b["dtype"],
+                                                    None)
+    assert chain(None, None, n=2) == 1                        # no layer arrays
+    assert chain([], []) == 2                                 # no layer
+    assert chain([Q0, Q] * 2 + [Q], [K0, K] * 2 + [K]) == 2   # five layers
+    assert chain([Q0, Q], [K0, K], dtype=binding.FA_DTYPE_FP32) == 5
+    assert chain([Q0, Q], [K0, K], D=96) == 4
+    assert chain([Q0, Q], [K0, K], Hq=3) == 3
+    assert chain([None, Q], [K0, K]) == 1                     # a layer's Q missing
+    assert chain([Q0, Q], [K0 + 8, K]) == 7                   # a layer's K misaligned
+    assert chain([Q0, Q], [K0, K], o=Q0) == 8                 # output over an earlier Q
+    assert chain([Q0, Q], [K0, K], B=0) == 0                  # empty: nothing launched

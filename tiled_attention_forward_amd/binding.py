@@ -61,6 +61,9 @@ def load_library():
     lib.fa_backward_window.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64,
                                        f32, i64, i32, p, i64, p]
     lib.fa_backward_window.restype = i32
+    lib.fa_forward_chain.argtypes = [ctypes.POINTER(p), ctypes.POINTER(p), i64, p, p, p, i64,
+                                     i64, i64, i64, i64, i64, f32, i32, i32, p]
+    lib.fa_forward_chain.restype = i32
     lib.fa_forward_split.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32, i32,
                                      i32, i64, p, i64, p]
     lib.fa_forward_split.restype = i32
@@ -216,6 +219,46 @@ def forward(q, k, v, bias=None, *, causal=False, scale=None, out=None, lse=None,
                             bias.data_ptr() if bias is not None else None,
                             out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, D, float(scale),
                             int(bool(causal)), _dtype_code(q), stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+    return out, lse
+
+
+def fa_forward_chain(q_ptrs, k_ptrs, v, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype,
+                     stream) -> int:
+    """fa_forward_chain with Python lists of device addresses for the layers."""
+    n = len(q_ptrs)
+    qa = (ctypes.c_void_p * max(n, 1))(*q_ptrs)
+    ka = (ctypes.c_void_p * max(len(k_ptrs), 1))(*k_ptrs)
+    return load_library().fa_forward_chain(qa, ka, n, v, o, lse, B, Hq, Hkv, Nq, Nk, D, scale,
+                                           causal, dtype, stream)
+
+
+def forward_chain(q_layers, k_layers, v, *, causal=False, scale=None, out=None, lse=None,
+                  stream=None):
+    """O, LSE of the last layer of a Block Attention Residual chain (fa_forward_chain).
+
+    q_layers / k_layers: the block's Q and K tensors up to the current layer,
+    oldest first (1 to 4 layers), each shaped like q / k of ``forward``; v is
+    the current layer's V.  The logits are sum_l Q_l K_l^T * scale.
+    """
+    import torch
+    lib = load_library()
+    if len(q_layers) != len(k_layers) or not q_layers:
+        raise ValueError("need as many K layers as Q layers, at least one")
+    B, Hq, Hkv, Nq, Nk, D = _check_inputs(q_layers[-1], k_layers[-1], v, None)
+    for ql, kl in zip(q_layers, k_layers):
+        _check_inputs(ql, kl, v, None)
+        if ql.shape != q_layers[-1].shape or ql.dtype != v.dtype or kl.dtype != v.dtype:
+            raise ValueError("every layer needs the shapes and dtype of the last one")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out, lse = _outputs(q_layers[-1], out, lse)
+    if stream is None:
+        stream = torch.cuda.current_stream(v.device)
+    st = fa_forward_chain([t.data_ptr() for t in q_layers], [t.data_ptr() for t in k_layers],
+                          v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, D,
+                          float(scale), int(bool(causal)), _dtype_code(v), stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, fa_status_string(st))
     return out, lse

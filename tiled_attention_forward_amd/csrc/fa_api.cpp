@@ -121,6 +121,42 @@ extern "C" int fa_forward_window(const void* q, const void* k, const void* v, co
                         dtype, stream);
 }
 
+extern "C" int fa_forward_chain(const void* const* q_layers, const void* const* k_layers,
+                                int64_t num_layers, const void* v, void* o, float* lse,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                int64_t D, float scale, int causal, int dtype, void* stream) {
+  if (q_layers == nullptr || k_layers == nullptr) return FA_ERR_NULL_POINTER;
+  if (num_layers < 1 || num_layers > fa::kMaxChainLayers) return FA_ERR_BAD_SIZE;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;
+  // each layer's operands against v, o and lse (sizes, pointers, overlap)
+  for (int64_t l = 0; l < num_layers; ++l) {
+    const int st = fa_check_args(q_layers[l], k_layers[l], v, nullptr, o, lse, B, Hq, Hkv, Nq,
+                                 Nk, D, scale, causal, dtype);
+    if (st != FA_OK) return st;
+  }
+  if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
+  const int n = int(num_layers);
+  fa::LaunchArgs a;
+  a.q = q_layers[n - 1];
+  a.k = k_layers[n - 1];
+  a.v = v;
+  a.bias = nullptr;
+  a.o = o;
+  a.lse = lse;
+  a.B = int(B);
+  a.Hq = int(Hq);
+  a.Hkv = int(Hkv);
+  a.Nq = int(Nq);
+  a.Nk = int(Nk);
+  a.D = int(D);
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.window = 0;
+  a.dtype = dtype;
+  a.stream = stream;
+  return fa::launch_forward_chain(a, q_layers, k_layers, n);
+}
+
 namespace {
 
 // Sizes of the key-split path, after the common checks: index limits of the
@@ -369,4 +405,4 @@ extern "C" const char* fa_status_string(int status) {
   }
 }
 
-extern "C" const char* fa_version(void) { return "fa 0.2.0 gfx950"; }
+extern "C" const char* fa_version(void) { return "fa 0.3.0 gfx950"; }

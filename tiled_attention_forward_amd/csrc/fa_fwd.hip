@@ -91,6 +91,10 @@ struct Params {
   u32 q_sign;    // sign bits XORed into Q when scale < 0
   int bias_vec;  // bias rows allow 16-byte vector loads
   int window;         // causal sliding window (keys i-window+1 .. i), 0 = none
+  // Block Attention Residual chain (NL > 1 instances): Q and K of every layer
+  // of the chain, oldest first; the last pair is also in q and k
+  const void* chain_q[kMaxChainLayers];
+  const void* chain_k[kMaxChainLayers];
   // key-split path only: o and lse point at the fp32 partial outputs
   int n_splits;       // key ranges per row block
   int64_t part_rows;  // B * Hq * Nq, the row stride between splits
@@ -113,7 +117,11 @@ __device__ __forceinline__ int vt_pos_of_group(int kg) {  // kg = key / 4
 // 128-row block, key range); it writes the normalised partial O (fp32) and
 // partial LSE of its key range, to be combined by fa_merge_kernel.
 // WINDOW (with CAUSAL): sliding window of p.window keys per row.
-template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT, bool WINDOW>
+// NL > 1 (Block Attention Residual chain): the logits are the sum over NL
+// layers of Q_l K_l^T * scale, the K tiles of all layers sharing one LDS
+// buffer with the V tile; 16-bit types, no bias, no key split, no window.
+template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT, bool WINDOW,
+          int NL>
 __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_kernel(Params p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
@@ -147,8 +155,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   constexpr int VTASKS = (BN / 4) * (D / VEC);            // 4-key x VEC-column tasks
   constexpr int VTPT = (VTASKS + kThreads - 1) / kThreads;
   static_assert(KCH * kThreads * VEC == BN * D, "K tile must split evenly");
+  static_assert(NL >= 1 && NL <= kMaxChainLayers, "chain length");
+  static_assert(NL == 1 || (VTR && !BIAS && !SPLIT && !WINDOW), "chain instances");
+  constexpr int KTL = NL * KT;       // elements of the K tiles of all layers
+  constexpr int BUF = KTL + VT;      // elements per LDS buffer
 
-  __shared__ __attribute__((aligned(16))) T smem[2 * (KT + VT)];
+  __shared__ __attribute__((aligned(16))) T smem[2 * BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -209,10 +221,18 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
 
   const T* Qh = static_cast<const T*>(p.q) + row_base * D;
   const T* Kh = static_cast<const T*>(p.k) + kv_head * p.Nk * D;
+  // per layer of a chain (NL = 1: the one Q and K above)
+  __amdgpu_buffer_rsrc_t ql_rs[NL], kl_rs[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    const T* ql = NL == 1 ? Qh : static_cast<const T*>(p.chain_q[l]) + row_base * D;
+    const T* kl = NL == 1 ? Kh : static_cast<const T*>(p.chain_k[l]) + kv_head * p.Nk * D;
+    ql_rs[l] = make_rsrc(ql, uint32_t(n_rows) * D * ESZ);
+    kl_rs[l] = make_rsrc(kl, uint32_t(p.Nk) * D * ESZ);
+  }
   const T* Vh = static_cast<const T*>(p.v) + kv_head * p.Nk * D;
   OutT* Oh = static_cast<OutT*>(p.o) + out_base * D;
   float* Lh = p.lse + out_base;
-  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(Qh, uint32_t(n_rows) * D * ESZ);
   const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh, uint32_t(p.Nk) * D * ESZ);
   const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh, uint32_t(p.Nk) * D * ESZ);
   const float c = p.c;
@@ -265,19 +285,21 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   }
 
   // ---- Q fragments: B operand of S^T = K Q^T, loaded once ---------------------
-  Frag qf[QB][NS];
+  Frag qf[NL][QB][NS];
+#pragma unroll
+  for (int l = 0; l < NL; ++l)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int off = (qi[qb] * D + s * KS + g * KP) * ESZ;  // rows past Nq read 0
       if constexpr (F32) {
-        const u32 raw = __builtin_amdgcn_raw_buffer_load_b32(q_rs, off, 0, 0);
-        qf[qb][s] = __builtin_bit_cast(float, raw ^ p.q_sign);
+        const u32 raw = __builtin_amdgcn_raw_buffer_load_b32(ql_rs[l], off, 0, 0);
+        qf[l][qb][s] = __builtin_bit_cast(float, raw ^ p.q_sign);
       } else {
-        u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(q_rs, off, 0, 0);
+        u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(ql_rs[l], off, 0, 0);
         raw ^= p.q_sign;
-        qf[qb][s] = __builtin_bit_cast(Frag, raw);
+        qf[l][qb][s] = __builtin_bit_cast(Frag, raw);
       }
     }
 
@@ -420,13 +442,20 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   // Issue the direct LDS loads of tile j into buffer buf (16-bit types).
   auto dma_tile = [&](int j, int buf) {
     if constexpr (VTR) {
-      char* base = reinterpret_cast<char*>(smem + buf * (KT + VT));
+      char* base = reinterpret_cast<char*>(smem + buf * BUF);
       const int soff = j * BN * D * ESZ;
 #pragma unroll
       for (int i = 0; i < DNI; ++i) {
         char* dst = base + (wave * DNI + i) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rs, (lds_void*)dst, 16, unsigned(dma_k[i]), unsigned(soff), 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rs, (lds_void*)(dst + KT * ESZ), 16,
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+          // (a const copy: with the array element itself as the argument the
+          // host pass silently emits no launch stub for the kernel)
+          const __amdgpu_buffer_rsrc_t kr = kl_rs[l];
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(dst + l * KT * ESZ), 16,
+                                                   unsigned(dma_k[i]), unsigned(soff), 0, 0);
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rs, (lds_void*)(dst + KTL * ESZ), 16,
                                                  unsigned(dma_v[i]), unsigned(soff), 0, 0);
       }
     }
@@ -459,8 +488,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
 
   auto sstore = [&](int buf) {
     if constexpr (VTR) return;  // the direct loads already wrote the tile
-    T* sK = smem + buf * (KT + VT);
-    T* sV = sK + KT;
+    T* sK = smem + buf * BUF;
+    T* sV = sK + KTL;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int cidx = tid + i * kThreads;
@@ -515,12 +544,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   }
 
   auto compute = [&](int j, int buf) {
-    const T* sK = smem + buf * (KT + VT);
-    const T* sV = sK + KT;
+    const T* sK = smem + buf * BUF;
+    const T* sV = sK + KTL;
     const int key0 = j * BN;
 
     // S^T = K_j Q^T  (rows: keys of the tile, columns: 32 query rows per block)
+    // (a chain sums the products of all its layers into the same registers)
     f32x16 s[QB][NKB];
+#pragma unroll
+    for (int l = 0; l < NL; ++l)
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
 #pragma unroll
@@ -529,12 +561,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
         if constexpr (F32) {
           kf = sK[(kb * 32 + ln) * KSTR + st * KS + g * KP];
         } else {
-          const char* src = reinterpret_cast<const char*>(sK) + kb * 32 * RB + k_off[st];
+          const char* src = reinterpret_cast<const char*>(sK + l * KT) + kb * 32 * RB + k_off[st];
           kf = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(src));
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          s[qb][kb] = E::mma(kf, qf[qb][st], st == 0 ? f32x16{} : s[qb][kb]);
+          s[qb][kb] = E::mma(kf, qf[l][qb][st], (l == 0 && st == 0) ? f32x16{} : s[qb][kb]);
       }
     }
 
@@ -845,12 +877,38 @@ __global__ __launch_bounds__(kMergeWaves * 64) void fa_merge_kernel(
 }
 
 template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT,
-          bool WINDOW = false>
+          bool WINDOW = false, int NL = 1>
 hipError_t launch_one(const Params& p, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&p)};
   return hipLaunchKernel(
-      reinterpret_cast<const void*>(&fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT, WINDOW>),
+      reinterpret_cast<const void*>(&fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT, WINDOW, NL>),
       dim3(grid), dim3(kThreads), args, 0, stream);
+}
+
+// Chain instances.  Keys per tile: the K tiles of all layers and the V tile
+// share each of the two LDS buffers, so tiles shrink to 32 keys where 64
+// would leave room for fewer than two workgroups per CU.
+template <typename T, int D, int NL>
+hipError_t launch_chain_nl(const Params& p, unsigned grid, hipStream_t s, bool causal) {
+  constexpr int BN = (D == 64 && NL == 2) ? 64 : 32;
+  return causal ? launch_one<T, D, BN, 1, true, false, false, false, NL>(p, grid, s)
+                : launch_one<T, D, BN, 1, false, false, false, false, NL>(p, grid, s);
+}
+
+template <typename T, int D>
+hipError_t launch_chain_d(const Params& p, unsigned grid, hipStream_t s, bool causal, int nl) {
+  switch (nl) {
+    case 2: return launch_chain_nl<T, D, 2>(p, grid, s, causal);
+    case 3: return launch_chain_nl<T, D, 3>(p, grid, s, causal);
+    default: return launch_chain_nl<T, D, 4>(p, grid, s, causal);
+  }
+}
+
+template <typename T>
+hipError_t launch_chain_t(const Params& p, unsigned grid, hipStream_t s, int D, bool causal,
+                          int nl) {
+  return D == 64 ? launch_chain_d<T, 64>(p, grid, s, causal, nl)
+                 : launch_chain_d<T, 128>(p, grid, s, causal, nl);
 }
 
 template <typename T, int D, int BN, int QB, bool SPLIT>
@@ -918,6 +976,7 @@ Params make_params(const LaunchArgs& a, int rows_per_block, int n_rows) {
   p.q_sign = !neg ? 0u : (a.dtype == FA_DTYPE_FP32 ? 0x80000000u : 0x80008000u);
   p.bias_vec = (a.dtype == FA_DTYPE_FP32) ? (a.Nk % 4) == 0 : (a.Nk % 8) == 0;
   p.window = a.window;
+  for (int l = 0; l < kMaxChainLayers; ++l) p.chain_q[l] = p.chain_k[l] = nullptr;
   p.n_splits = 1;
   p.part_rows = 0;
   return p;
@@ -986,6 +1045,22 @@ int launch_forward_split(const LaunchArgs& a, int n_splits, void* workspace) {
                static_cast<hipStream_t>(a.stream)) == hipSuccess
              ? FA_OK
              : FA_ERR_HIP;
+}
+
+int launch_forward_chain(const LaunchArgs& a, const void* const* q_layers,
+                         const void* const* k_layers, int n_layers) {
+  if (n_layers == 1) return launch_forward(a);
+  Params p = make_params(a, kWaves * 32, a.Nq);
+  for (int l = 0; l < kMaxChainLayers; ++l) {
+    p.chain_q[l] = l < n_layers ? q_layers[l] : nullptr;
+    p.chain_k[l] = l < n_layers ? k_layers[l] : nullptr;
+  }
+  const unsigned grid = unsigned(p.n_qtiles) * unsigned(p.BH);
+  hipStream_t s = static_cast<hipStream_t>(a.stream);
+  const hipError_t e = a.dtype == FA_DTYPE_BF16
+                           ? launch_chain_t<__bf16>(p, grid, s, a.D, a.causal, n_layers)
+                           : launch_chain_t<_Float16>(p, grid, s, a.D, a.causal, n_layers);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int launch_merge(const float* part_o, const float* part_lse, int n_parts, int64_t rows, int D,

@@ -73,6 +73,13 @@ inline int64_t backward_workspace_bytes(int64_t rows) {
   return (backward_lse2_offset(rows) + rows) * 4;
 }
 
+// Block Attention Residual chain: the logits are sum_l Q_l K_l^T * scale over
+// n_layers (1 .. kMaxChainLayers) layers, oldest first; a.q and a.k are the
+// last layer's (also q_layers[n-1], k_layers[n-1]), a.v its V.  16-bit types,
+// no bias, no window.  Arguments are already validated.
+constexpr int kMaxChainLayers = 4;
+int launch_forward_chain(const LaunchArgs& a, const void* const* q_layers,
+                         const void* const* k_layers, int n_layers);
 // Largest key-split count accepted.
 constexpr int kMaxSplits = 1024;
 

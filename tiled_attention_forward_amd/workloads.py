@@ -23,7 +23,10 @@ synthetic choices: one decode step (Nq = 1) of the same 20/4-head, D = 128
 setup for 8 sequences over a 32768-entry KV cache, and a long sequence with
 only two heads (B = 1, H = 2, S = 16384, D = 64, 256 row blocks).  The
 sliding-window shape is the benchmark report shape with each row limited to
-its 1024 most recent keys.
+its 1024 most recent keys.  The chain shape is the same GQA setup at the last
+layer of a 4-layer Block Attention Residual block, whose logits sum the Q K^T
+products of all four layers (in place of the dense logit tensor); its Q and K
+are drawn layer by layer (Q_l, then K_l, oldest layer first), then V.
 """
 
 from __future__ import annotations
@@ -50,6 +53,7 @@ class Workload:
     bias: bool
     path: str = "fused"   # "fused": fa_forward; "split": fa_forward_split
     window: int = 0       # causal sliding window (fa_forward_window), 0 = none
+    layers: int = 0       # Block Attention Residual chain length (fa_forward_chain), 0 = none
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -80,14 +84,17 @@ class Workload:
         return self.B * self.Hq * per_head
 
     def useful_flops(self) -> float:
-        """2 matmuls x 2 flops x D per visible (query, key) pair."""
-        return 4.0 * self.D * self.visible_pairs()
+        """2 flops x D per visible (query, key) pair for each product: Q K^T
+        (one per chain layer) and P V."""
+        return 2.0 * self.D * (max(1, self.layers) + 1) * self.visible_pairs()
 
     def io_bytes(self) -> int:
-        """Algorithmic HBM bytes: read Q, K, V (and the visible bias entries), write O and LSE."""
+        """Algorithmic HBM bytes: read Q, K, V (every layer's Q and K for a
+        chain; the visible bias entries), write O and LSE."""
         esz = torch.tensor([], dtype=self.torch_dtype).element_size()
-        qo = 2 * self.B * self.Hq * self.Nq * self.D * esz
-        kv = 2 * self.B * self.Hkv * self.Nk * self.D * esz
+        nl = max(1, self.layers)
+        qo = (nl + 1) * self.B * self.Hq * self.Nq * self.D * esz
+        kv = (nl + 1) * self.B * self.Hkv * self.Nk * self.D * esz
         lse = self.B * self.Hq * self.Nq * 4
         bias = self.visible_pairs() * esz if self.bias else 0
         return qo + kv + lse + bias
@@ -109,6 +116,8 @@ WORKLOADS = {
                  "split"),
         Workload("b2_h16_s4096_d64_bf16_swa1024", 2, 16, 16, 4096, 4096, 64, "bf16", True, False,
                  window=1024),
+        Workload("b1_hq20_hkv4_s8192_d128_bf16_causal_chain4", 1, 20, 4, 8192, 8192, 128, "bf16",
+                 True, False, layers=4),
     ]
 }
 
@@ -143,6 +152,26 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu"):
             for h in range(w.Hq):
                 bias[b, h] = draw((w.Nq, w.Nk))
     return q, k, v, bias
+
+
+def make_chain_inputs(w: Workload, n_layers: int, seed: int = 0, device="cpu"):
+    """Draw (q_layers, k_layers, v) for an n_layers chain of workload ``w``:
+    Q_0, K_0, Q_1, K_1, ... in that order from one seeded generator, then V,
+    each as ``make_inputs`` draws Q, K and V."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed))
+    dt = w.torch_dtype
+
+    def draw(shape):
+        return torch.randn(shape, generator=g, dtype=torch.float32, device=dev).to(dt)
+
+    qs, ks = [], []
+    for _ in range(n_layers):
+        qs.append(draw((w.B, w.Hq, w.Nq, w.D)))
+        ks.append(draw((w.B, w.Hkv, w.Nk, w.D)))
+    v = draw((w.B, w.Hkv, w.Nk, w.D))
+    return qs, ks, v
 
 
 def sample_rows(n: int, count: int, seed: int = 0, tile: int = 64):
