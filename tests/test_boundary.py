@@ -92,7 +92,8 @@ def test_empty_problem_needs_no_pointers_and_launches_nothing():
 @pytest.mark.parametrize("over,code", [
     (dict(B=-1), 2), (dict(Nq=-5), 2), (dict(Nk=-1), 2), (dict(Hkv=0), 2),
     (dict(Hq=5, Hkv=2), 3), (dict(Hq=4, Hkv=3), 3),
-    (dict(D=80), 4), (dict(D=96), 4), (dict(D=32), 4), (dict(D=256), 4), (dict(D=0), 4),
+    (dict(D=72), 4), (dict(D=112), 4), (dict(D=32), 4), (dict(D=256), 4), (dict(D=0), 4),
+    (dict(D=96, dtype=binding.FA_DTYPE_FP32), 4),
     (dict(dtype=3), 5), (dict(dtype=-1), 5),
     (dict(scale=math.nan), 6), (dict(scale=math.inf), 6), (dict(scale=-math.inf), 6),
     (dict(q=Q + 8), 7), (dict(k=K + 4), 7), (dict(v=V + 2), 7), (dict(o=O + 8), 7),
@@ -107,10 +108,17 @@ def test_rejections(over, code):
 
 
 def test_head_dim_pitfall_is_an_error_not_a_truncation():
-    """A 96-wide head with a 64-wide kernel block silently drops columns in the
-    kernel of the xnwp.cn post (§5.1, §6.4); here every unsupported D is refused."""
-    for d in (1, 16, 63, 65, 80, 96, 127, 129, 192):
+    """A 96-wide head with a 64-wide kernel block silently drops columns, and an
+    80-wide one reads past the row, in the kernel of the xnwp.cn post (§5.1,
+    §6.4); here 80 and 96 run in a 128-wide tile (bf16/fp16) and every other
+    unsupported D is refused."""
+    for d in (1, 16, 63, 65, 72, 88, 112, 127, 129, 192):
         assert check(D=d) == 4
+    for d in (64, 80, 96, 128):
+        assert check(D=d) == 0
+        assert check(D=d, dtype=binding.FA_DTYPE_FP16) == 0
+    assert check(D=80, dtype=binding.FA_DTYPE_FP32) == 4
+    assert check(D=96, dtype=binding.FA_DTYPE_FP32) == 4
 
 
 def test_forward_binding_rejects_cpu_tensors():
@@ -152,7 +160,7 @@ def test_split_workspace_bytes_layout():
         assert binding.fa_split_workspace_bytes(2, 4, 100, 64, s) == o_pad + s * rows * 4
     assert binding.fa_split_workspace_bytes(1, 1, 1, 128, 1) == 512 + 4
     assert binding.fa_split_workspace_bytes(0, 4, 100, 64, 2) == 0
-    for bad, code in ((dict(num_splits=0), 2), (dict(num_splits=1025), 2), (dict(D=96), 4),
+    for bad, code in ((dict(num_splits=0), 2), (dict(num_splits=1025), 2), (dict(D=72), 4),
                       (dict(B=-1), 2)):
         a = {**dict(B=2, Hq=4, Nq=100, D=64, num_splits=2), **bad}
         with pytest.raises(binding.FaError) as e:
@@ -186,7 +194,7 @@ def test_split_rejections_before_launch():
     assert split_status(workspace_bytes=need - 1) == 11
     assert split_status(workspace=O) == 8            # workspace over the output
     assert split_status(workspace=Q - 256) == 8      # runs into q
-    assert split_status(D=96) == 4 and split_status(q=None) == 1   # the common checks first
+    assert split_status(D=72) == 4 and split_status(q=None) == 1   # the common checks first
     # packed rows of one KV head: (Hq/Hkv) * Nq * D * 2 bytes must stay below 2^31
     assert split_status(Hq=64, Hkv=1, Nq=1 << 18, B=1, workspace_bytes=1 << 62) == 9
     # empty problem: nothing launched, no workspace needed
@@ -234,7 +242,8 @@ def test_backward_workspace_bytes():
 
 def test_backward_rejections_before_launch():
     assert bwd_status(dtype=binding.FA_DTYPE_FP32) == 5       # 16-bit types only
-    assert bwd_status(D=96) == 4 and bwd_status(q=None) == 1   # the forward's checks first
+    assert bwd_status(D=72) == 4 and bwd_status(q=None) == 1   # the forward's checks first
+    assert bwd_status(D=96) == 4 and bwd_status(D=80) == 4      # forward-only head dims
     assert bwd_status(dout=None) == 1 and bwd_status(dq=None) == 1
     assert bwd_status(dk=None) == 1 and bwd_status(dv=None) == 1
     assert bwd_status(dq=DQ + 8) == 7 and bwd_status(dout=GO + 4) == 7
@@ -258,7 +267,7 @@ def test_window_rejections_before_launch():
     assert lib.fa_forward_window(*args, 0, a["dtype"], None) == 2
     assert lib.fa_forward_window(*args, -3, a["dtype"], None) == 2
     assert lib.fa_forward_window(*args, 1 << 30, a["dtype"], None) == 9
-    assert lib.fa_forward_window(*args[:11], 96, a["scale"], 16, a["dtype"], None) == 4
+    assert lib.fa_forward_window(*args[:11], 72, a["scale"], 16, a["dtype"], None) == 4
     bargs = (a["q"], a["k"], a["v"], None, a["o"], a["lse"], GO, DQ, DK, DV, a["B"], a["Hq"],
              a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"])
     assert lib.fa_backward_window(*bargs, 0, a["dtype"], WS, 1 << 40, None) == 2
@@ -282,7 +291,7 @@ def test_chain_rejections_before_launch():
     assert chain([], []) == 2                                 # no layer
     assert chain([Q0, Q] * 2 + [Q], [K0, K] * 2 + [K]) == 2   # five layers
     assert chain([Q0, Q], [K0, K], dtype=binding.FA_DTYPE_FP32) == 5
-    assert chain([Q0, Q], [K0, K], D=96) == 4
+    assert chain([Q0, Q], [K0, K], D=96) == 4                 # chain: 64 and 128 only
     assert chain([Q0, Q], [K0, K], Hq=3) == 3
     assert chain([None, Q], [K0, K]) == 1                     # a layer's Q missing
     assert chain([Q0, Q], [K0 + 8, K]) == 7                   # a layer's K misaligned

@@ -54,6 +54,13 @@ EDGE = [
     (1, 2, 2, 70, 70, 64, "fp32", True, False),
     (1, 2, 1, 129, 131, 128, "fp16", False, True),
     (3, 2, 2, 65, 63, 64, "fp16", True, True),
+    # head dims 80 and 96 (the xnwp.cn post, §5.1 and §6.4): 128-wide tiles
+    (1, 2, 2, 1000, 1000, 80, "bf16", True, False),
+    (1, 4, 2, 333, 517, 96, "fp16", False, True),
+    (2, 10, 2, 200, 300, 80, "fp16", True, True),
+    (1, 2, 1, 517, 333, 96, "bf16", True, False),
+    (1, 1, 1, 1, 1, 80, "bf16", False, False),
+    (1, 2, 2, 130, 70, 96, "bf16", False, False),
 ]
 
 
@@ -174,6 +181,8 @@ WINDOW_CASES = [
     (1, 2, 2, 700, 900, 128, "bf16", True, 129),     # Nk > Nq
     (1, 2, 2, 200, 200, 64, "fp32", False, 64),
     (1, 2, 2, 200, 200, 64, "bf16", False, 200),     # window = Nk: plain causal
+    (1, 2, 2, 300, 300, 96, "bf16", False, 50),
+    (1, 2, 1, 513, 513, 80, "fp16", True, 100),
 ]
 
 
@@ -216,3 +225,34 @@ def test_window_full_size_sampled(gpu_device):
                     o_ref, l_ref)
         _log(st)
         assert_within(st, "bf16", f"window 1024 b{bb} h{h}")
+
+
+@pytest.mark.parametrize("D", [80, 96])
+def test_narrow_head_writes_only_its_columns(gpu_device, D):
+    """With D = 80 the kernel computes 96 output columns; the 16 past the row
+    must not be stored (they would land on the next row, and past the last
+    row outside the tensor).  The output sits at the start of a larger buffer
+    whose tail is a sentinel."""
+    w = custom(1, 2, 2, 129, 200, D, "bf16", True, False)
+    q, k, v, _ = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=9))
+    n = q.numel()
+    buf = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device=gpu_device)
+    out = buf[:n].view(q.shape)
+    o, lse = binding.forward(q, k, v, None, causal=True, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[n:] == 7.0)
+    from oracle import attention_forward
+    from tests.parity import assert_within, errors
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v), None, scale=w.scale, causal=True)
+    assert_within(errors(f64(o), lse.cpu().numpy(), o_ref, l_ref), "bf16", f"D={D}")
+
+
+def test_head_dim_80_full_size_sampled(gpu_device):
+    """The benchmark report shape (B2 H16 S4096 causal) with 80-wide heads."""
+    w = custom(2, 16, 16, 4096, 4096, 80, "bf16", True, False)
+    _log("full-size D=80")
+    q, k, v, _ = make_inputs(w, seed=3, device=gpu_device)
+    o, lse = run_gpu(q, k, v, None, w.scale, True)
+    st = sampled_check(q, k, v, None, w.scale, True, "bf16", [(0, 0), (1, 15)],
+                       sample_rows(w.Nq, 64, seed=3), o, lse, "D=80 full size")
+    _log(st)

@@ -39,6 +39,8 @@ SPLIT_CASES = [
     (1, 1, 1, 1, 1, 64, "bf16", True, False, 1),
     (1, 4, 4, 1000, 1000, 64, "bf16", True, False, 2),
     (1, 2, 2, 700, 1, 128, "bf16", True, False, 3),       # one key, splits mostly empty
+    (2, 8, 2, 1, 1000, 96, "bf16", False, False, 3),      # head dims 80 and 96
+    (1, 4, 2, 300, 300, 80, "fp16", True, True, 4),
 ]
 
 

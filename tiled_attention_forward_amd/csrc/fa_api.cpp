@@ -41,7 +41,9 @@ extern "C" int fa_check_args(const void* q, const void* k, const void* v, const 
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_BAD_SIZE;
   if (Hq > 0 && Hkv < 1) return FA_ERR_BAD_SIZE;
   if (Hq > 0 && Hq % Hkv != 0) return FA_ERR_HEAD_GROUPS;
-  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  // 64 and 128; 80 and 96 for the 16-bit types (kept in a 128-wide tile)
+  const bool dim_ok = D == 64 || D == 128 || ((D == 80 || D == 96) && esz == 2);
+  if (!dim_ok) return FA_ERR_HEAD_DIM;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   const bool empty = (B == 0 || Hq == 0 || Nq == 0);
   if (empty) return FA_OK;
@@ -128,6 +130,7 @@ extern "C" int fa_forward_chain(const void* const* q_layers, const void* const* 
   if (q_layers == nullptr || k_layers == nullptr) return FA_ERR_NULL_POINTER;
   if (num_layers < 1 || num_layers > fa::kMaxChainLayers) return FA_ERR_BAD_SIZE;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   // each layer's operands against v, o and lse (sizes, pointers, overlap)
   for (int64_t l = 0; l < num_layers; ++l) {
     const int st = fa_check_args(q_layers[l], k_layers[l], v, nullptr, o, lse, B, Hq, Hkv, Nq,
@@ -179,7 +182,7 @@ extern "C" int fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64
   if (bytes == nullptr) return FA_ERR_NULL_POINTER;
   if (B < 0 || Hq < 0 || Nq < 0 || D < 0) return FA_ERR_BAD_SIZE;
   if (num_splits < 1 || num_splits > fa::kMaxSplits) return FA_ERR_BAD_SIZE;
-  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 64 && D != 80 && D != 96 && D != 128) return FA_ERR_HEAD_DIM;
   const __int128 rows = __int128(B) * Hq * Nq;
   if (rows * D * 4 * num_splits >= (__int128(1) << 62)) return FA_ERR_TOO_LARGE;
   *bytes = fa::split_workspace_bytes(int64_t(rows), D, num_splits);
@@ -192,7 +195,7 @@ extern "C" int fa_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, in
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_BAD_SIZE;
   if (Hq > 0 && Hkv < 1) return FA_ERR_BAD_SIZE;
   if (Hq > 0 && Hq % Hkv != 0) return FA_ERR_HEAD_GROUPS;
-  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 64 && D != 80 && D != 96 && D != 128) return FA_ERR_HEAD_DIM;
   *num_splits = 1;
   if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
   const int64_t lim = int64_t(1) << 30;
@@ -300,6 +303,7 @@ int backward_common(const void* q, const void* k, const void* v, const void* bia
   if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;  // 16-bit types only
   int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
   if (st != FA_OK) return st;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;   // the backward kernels' tiles
   const int esz = elem_bytes(dtype);
   const bool no_rows = (B == 0 || Hq == 0 || Nq == 0);
   const bool no_keys = (B == 0 || Hkv == 0 || Nk == 0);
@@ -393,7 +397,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_NULL_POINTER: return "a required pointer is NULL";
     case FA_ERR_BAD_SIZE: return "a size is negative, or Hkv < 1";
     case FA_ERR_HEAD_GROUPS: return "Hq is not a multiple of Hkv";
-    case FA_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
+    case FA_ERR_HEAD_DIM:
+      return "head dimension D must be 64 or 128 (80 or 96: bf16/fp16 forward and key split)";
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_SCALE: return "scale is not finite";
     case FA_ERR_ALIGNMENT: return "a tensor pointer is misaligned (16 bytes; lse 4 bytes)";

@@ -130,7 +130,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   constexpr bool OUT_F32 = F32 || SPLIT;
   constexpr int KP = E::KP;
   constexpr int KS = 2 * KP;         // contraction length of one MFMA
-  constexpr int NS = D / KS;         // MFMAs per 32x32 score block
+  // Head dims 80 and 96 (16-bit types): the LDS tiles keep the 128-wide row
+  // layout, the chunks past the real row are zero-filled by out-of-range loads,
+  // and the products run over ceil(D/16) contraction steps and ceil(D/32)
+  // output column blocks; only the real columns are stored.
+  constexpr int DL = (D == 80 || D == 96) ? 128 : D;   // LDS row width, elements
+  static_assert(D == 64 || D == 80 || D == 96 || D == 128, "head dim");
+  static_assert(D == DL || !F32, "fp32 takes head dims 64 and 128");
+  constexpr int NS = (D + KS - 1) / KS;  // MFMAs per 32x32 score block
   constexpr int ESZ = sizeof(T);
   constexpr int VEC = 16 / ESZ;      // elements per 16-byte vector
   // 16-bit types: K and V tiles go from HBM straight into LDS (buffer loads
@@ -141,20 +148,21 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   constexpr bool VTR = !F32;
   constexpr int KSTR = D + VEC;      // fp32: K tile row stride, elements
   constexpr int VSTR = BN + VEC;     // fp32: V^T tile row stride, elements
-  constexpr int RB = D * ESZ;        // 16-bit: bytes per K/V tile row
-  constexpr int CPR = D / VEC;       // 16-byte chunks per row
-  constexpr int KT = VTR ? BN * D : BN * KSTR;   // elements per K buffer
-  constexpr int VT = VTR ? BN * D : D * VSTR;    // elements per V buffer
+  constexpr int RB = DL * ESZ;       // 16-bit: bytes per K/V tile row
+  constexpr int CPR = DL / VEC;      // 16-byte chunks per LDS tile row
+  constexpr int CPRG = D * ESZ / 16; // 16-byte chunks per row in HBM
+  constexpr int KT = VTR ? BN * DL : BN * KSTR;  // elements per K buffer
+  constexpr int VT = VTR ? BN * DL : D * VSTR;   // elements per V buffer
   constexpr int DNI = VTR ? BN * CPR / (64 * kWaves) : 1;  // LDS loads per wave per matrix
   static_assert(!VTR || DNI * 64 * kWaves == BN * CPR, "tile must split into whole wave loads");
   constexpr int NKB = BN / 32;       // 32-key blocks per tile
-  constexpr int NDB = D / 32;        // 32-wide column blocks of the output
+  constexpr int NDB = (D + 31) / 32; // 32-wide column blocks of the output
   constexpr int QW = 32 * QB;        // query rows per wave
   constexpr int BM = kWaves * QW;    // query rows per workgroup
   constexpr int KCH = BN * D / VEC / kThreads;            // K vectors per thread
   constexpr int VTASKS = (BN / 4) * (D / VEC);            // 4-key x VEC-column tasks
   constexpr int VTPT = (VTASKS + kThreads - 1) / kThreads;
-  static_assert(KCH * kThreads * VEC == BN * D, "K tile must split evenly");
+  static_assert(VTR || KCH * kThreads * VEC == BN * D, "K tile must split evenly");
   static_assert(NL >= 1 && NL <= kMaxChainLayers, "chain length");
   static_assert(NL == 1 || (VTR && !BIAS && !SPLIT && !WINDOW), "chain instances");
   constexpr int KTL = NL * KT;       // elements of the K tiles of all layers
@@ -417,15 +425,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   for (int i = 0; i < DNI; ++i) {
     const int q = (wave * DNI + i) * 64 + lane;   // physical chunk index in the tile
     const int row = q / CPR, pc = q % CPR;
-    dma_k[i] = (row * D + (pc ^ lds_swizzle_rows<D>(row)) * VEC) * ESZ;
-    dma_v[i] = (row * D + (pc ^ lds_swizzle_tr<D>(row)) * VEC) * ESZ;
+    // logical chunks past the row (D = 80, 96) get an offset past every
+    // resource range (2^31 plus a tile offset below 2^31: no wrap), so the
+    // load writes zeros
+    const int lk = pc ^ lds_swizzle_rows<DL>(row), lv = pc ^ lds_swizzle_tr<DL>(row);
+    dma_k[i] = lk < CPRG ? (row * D + lk * VEC) * ESZ : int(0x80000000u);
+    dma_v[i] = lv < CPRG ? (row * D + lv * VEC) * ESZ : int(0x80000000u);
   }
   // K operand reads: lane (row ln of a 32-key block, lane half g) reads
   // logical chunk 2*st + g.
   int k_off[VTR ? NS : 1];
 #pragma unroll
   for (int st = 0; st < (VTR ? NS : 1); ++st)
-    k_off[st] = ln * RB + (((2 * st + g) ^ lds_swizzle_rows<D>(ln)) * 16);
+    k_off[st] = ln * RB + (((2 * st + g) ^ lds_swizzle_rows<DL>(ln)) * 16);
   // Transposed V reads (ds_read_b64_tr_b16): within each 16-lane group, lane
   // 4a+b receives element b of the 8-byte chunks read by lanes a, a+4, a+8,
   // a+12.  So lane s of the group reads row 4g + s/4 (and 8 rows further for
@@ -436,7 +448,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   for (int db = 0; db < (VTR ? NDB : 1); ++db) {
     const int r = 4 * g + ((lane >> 2) & 3);
     const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    v_off[db] = r * RB + ((c ^ lds_swizzle_tr<D>(r)) * 16) + 8 * (lane & 1);
+    v_off[db] = r * RB + ((c ^ lds_swizzle_tr<DL>(r)) * 16) + 8 * (lane & 1);
   }
 
   // Issue the direct LDS loads of tile j into buffer buf (16-bit types).
@@ -750,7 +762,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
           a4[e] = acc[qb][db][8 * pr + e] * inv;
           b4[e] = acc[qb][db][8 * pr + 4 + e] * inv;
         }
-        OutT* dst = Oh + int64_t(qi[qb]) * D + db * 32 + 16 * pr + 8 * g;
+        const int col = db * 32 + 16 * pr + 8 * g;  // first of this lane's 8 columns
+        OutT* dst = Oh + int64_t(qi[qb]) * D + col;
         if constexpr (OUT_F32) {
           const u32x4 aw = __builtin_bit_cast(u32x4, a4), bw = __builtin_bit_cast(u32x4, b4);
           u32x4 ao, bo;
@@ -761,7 +774,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
             ao[e] = r0;
             bo[e] = r1;
           }
-          if (row_ok) {
+          if (row_ok && (D % 32 == 0 || col < D)) {
             reinterpret_cast<u32x4*>(dst)[0] = ao;
             reinterpret_cast<u32x4*>(dst)[1] = bo;
           }
@@ -775,7 +788,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
             out[e] = r0;
             out[2 + e] = r1;
           }
-          if (row_ok) *reinterpret_cast<u32x4*>(dst) = out;
+          if (row_ok && (D % 32 == 0 || col < D)) *reinterpret_cast<u32x4*>(dst) = out;
         }
       }
     if (row_ok && g == 0)
@@ -930,7 +943,9 @@ hipError_t launch_d(const Params& p, unsigned grid, hipStream_t s, bool causal, 
 // reads per MFMA, but only fit in registers for 16-bit inputs with D = 64 and
 // no bias tile; every other instance keeps one.  The key-split path keeps one.
 constexpr int query_blocks(int dtype, int D, bool bias, bool split) {
-  return split ? 1 : (dtype != FA_DTYPE_FP32 && D == 64 && !bias) ? kQB64 : (D == 64 ? 1 : kQB128);
+  return split ? 1
+               : (dtype != FA_DTYPE_FP32 && D == 64 && !bias) ? kQB64
+               : (D == 128) ? kQB128 : 1;
 }
 
 template <typename T, bool SPLIT>
@@ -945,6 +960,10 @@ hipError_t launch_t(const Params& p, unsigned grid, hipStream_t s, int D, bool c
       }
     }
     return launch_d<T, 64, kBN64, 1, SPLIT>(p, grid, s, causal, bias);
+  }
+  if constexpr (!std::is_same<T, float>::value) {
+    if (D == 80) return launch_d<T, 80, kBN128, 1, SPLIT>(p, grid, s, causal, bias);
+    if (D == 96) return launch_d<T, 96, kBN128, 1, SPLIT>(p, grid, s, causal, bias);
   }
   return launch_d<T, 128, kBN128, SPLIT ? 1 : kQB128, SPLIT>(p, grid, s, causal, bias);
 }
