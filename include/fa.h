@@ -60,8 +60,12 @@ typedef enum fa_status {
                            /* k or v is NULL while Nk > 0                             */
   FA_ERR_BAD_SIZE = 2,     /* a size is negative, or Hkv < 1 while Hq > 0                */
   FA_ERR_HEAD_GROUPS = 3,  /* Hq is not a multiple of Hkv                                */
-  FA_ERR_HEAD_DIM = 4,     /* D is not 64 or 128 (other head sizes are rejected, never   */
-                           /* silently truncated)                                        */
+  FA_ERR_HEAD_DIM = 4,     /* D is not 64 or 128, nor 80 or 96 with bf16/fp16 (these     */
+                           /* forward-only sizes run in 128-wide tiles, per the xnwp.cn  */
+                           /* post, §5.1 and §6.4: a block narrower than the head drops  */
+                           /* or misreads columns); the backward and the residual chain  */
+                           /* take 64 and 128.  Other sizes are rejected, never silently  */
+                           /* truncated                                                  */
   FA_ERR_DTYPE = 5,        /* dtype is not one of fa_dtype                               */
   FA_ERR_SCALE = 6,        /* scale is NaN or infinite                                   */
   FA_ERR_ALIGNMENT = 7,    /* a tensor pointer is not aligned as required above          */
@@ -186,7 +190,7 @@ int fa_forward_split(const void* q, const void* k, const void* v, const void* bi
  * partial O, float32 [num_splits][B*Hq*Nq][D], then partial LSE, float32
  * [num_splits][B*Hq*Nq], from the next 256-byte boundary.  Pure host code.
  * Returns FA_ERR_BAD_SIZE for negative sizes or num_splits outside
- * [1, 1024], FA_ERR_HEAD_DIM for D not 64 or 128, FA_ERR_NULL_POINTER for a
+ * [1, 1024], FA_ERR_HEAD_DIM for D not 64, 80, 96 or 128, FA_ERR_NULL_POINTER for a
  * NULL bytes.
  */
 int fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t D,
