@@ -187,10 +187,10 @@ def cpu_baseline(w, q, k, v, bias, target_s: float):
     heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
     for b, h in heads:
         hk = h // grp
-        qh = q[b, h].float().cpu().numpy().astype(np.float64)
-        kh = k[b, hk].float().cpu().numpy().astype(np.float64)
-        vh = v[b, hk].float().cpu().numpy().astype(np.float64)
-        bh = None if bias is None else bias[b, h].float().cpu().numpy().astype(np.float64)
+        qh = q[b, h].cpu().float().numpy().astype(np.float64)
+        kh = k[b, hk].cpu().float().numpy().astype(np.float64)
+        vh = v[b, hk].cpu().float().numpy().astype(np.float64)
+        bh = None if bias is None else bias[b, h].cpu().float().numpy().astype(np.float64)
         t0 = time.perf_counter()
         attention_head_rows(qh, kh, vh, rows=rows, scale=w.scale, causal=w.causal, bias_rows=bh,
                             window=w.window or None)
@@ -228,7 +228,8 @@ def main():
         q, k, bias = q_layers[-1], k_layers[-1], None
     else:
         q, k, v, bias = make_inputs(w, seed=args.seed, device=dev)
-    o = torch.empty_like(q)
+    # FP8 (E4M3) inputs give a bf16 output
+    o = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "fp8" else q.dtype, device=dev)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     dtype_code = binding._dtype_code(q)
@@ -241,7 +242,7 @@ def main():
         print("the chain workload is timed on the fused forward only", file=sys.stderr)
         sys.exit(2)
     if backward:
-        if w.bias or w.dtype == "fp32":
+        if w.bias or w.dtype in ("fp32", "fp8"):
             print("the backward is timed on bias-free 16-bit workloads", file=sys.stderr)
             sys.exit(2)
         g = torch.Generator(device=dev).manual_seed(args.seed + 1000)

@@ -46,11 +46,19 @@
 extern "C" {
 #endif
 
-/* Element type of q, k, v, bias and o. */
+/* Element type of q, k, v, bias and o.
+ * FA_DTYPE_FP8_E4M3: q, k and v in the OCP 8-bit E4M3 format (bias 7, largest
+ * finite 448, the gfx950 native FP8); o is bf16; no bias.  The FP8 direction
+ * of "FlashAttention principles and Triton practice" (xnwp.cn/news/15505), §7,
+ * which asks for its precision loss to be evaluated: the probabilities are
+ * rounded to E4M3 for the P.V product (the other arithmetic as for 16-bit
+ * inputs).  fa_forward only (fused, with or without the causal mask), D = 64
+ * or 128; the other entry points return FA_ERR_DTYPE for it. */
 typedef enum fa_dtype {
   FA_DTYPE_BF16 = 0,
   FA_DTYPE_FP16 = 1,
-  FA_DTYPE_FP32 = 2
+  FA_DTYPE_FP32 = 2,
+  FA_DTYPE_FP8_E4M3 = 3
 } fa_dtype;
 
 /* Status codes returned by every entry point. */

@@ -20,7 +20,8 @@ LSE_TOL = 1e-3
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
-    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+    # (to the host first: the host converts every dtype, FP8 included, exactly)
+    return t.detach().cpu().to(torch.float32).numpy().astype(np.float64)
 
 
 def errors(o, lse, o_ref, lse_ref):
@@ -111,3 +112,31 @@ def rounding_bound_check(q, k, v, bias, scale, causal, dtype, o, lse, what=""):
     err = np.abs(f64(o) - o_ref)
     assert np.all(err <= bound), f"{what}: worst err/bound {float((err / bound).max())}"
     assert np.abs(lse.cpu().numpy() - l_ref).max() <= LSE_TOL, f"{what}: LSE"
+
+
+def fp8_bound_check(q, k, v, scale, causal, o, lse, what=""):
+    """FP8 (E4M3) inputs: the kernel rounds each probability to E4M3 before P.V,
+    as p' = p * 2^7 relative to its running max reference (p' in (0, 2^8]):
+    relative error <= 2^-4 for normal values, absolute <= 2^-10 below E4M3's
+    smallest normal 2^-6, in units where the row's sum is >= 2^7.  O is rounded
+    once to bf16.  So elementwise
+        |dO_i| <= 2^-4 (P.|V|)_i + 2^-17 sum_{visible j} |v_j| + 2^-9 |O_i| + 1e-4,
+    with the sum over row i's visible keys (the oracle with Q = 0 and |V| gives
+    its mean).  The inputs are decoded exactly, so the scores carry no input
+    rounding; LSE is formed from the unrounded p and keeps its 1e-3 bar.
+    Returns (max |dO|, mean |dO|, worst err / bound)."""
+    bq, bk, bv = f64(q), f64(k), f64(v)
+    o_ref, l_ref = attention_forward(bq, bk, bv, None, scale=scale, causal=causal)
+    o_abs, _ = attention_forward(bq, bk, np.abs(bv), None, scale=scale, causal=causal)
+    m_abs, _ = attention_forward(np.zeros_like(bq), bk, np.abs(bv), None, scale=scale,
+                                 causal=causal)
+    nq, nk = bq.shape[2], bk.shape[2]
+    count = (np.minimum(np.arange(nq) + 1, nk) if causal else np.full(nq, nk)).astype(np.float64)
+    bound = (2.0 ** -4 * o_abs + 2.0 ** -17 * m_abs * count[None, None, :, None]
+             + 2.0 ** -9 * np.abs(o_ref) + 1e-4)
+    err = np.abs(f64(o) - o_ref)
+    ratio = float((err / bound).max(initial=0.0))
+    assert np.all(err <= bound), f"{what}: worst err/bound {ratio}"
+    dl = np.abs(lse.cpu().numpy().astype(np.float64) - l_ref)
+    assert dl.max(initial=0.0) <= LSE_TOL, f"{what}: LSE {dl.max()}"
+    return float(err.max(initial=0.0)), float(err.mean()) if err.size else 0.0, ratio

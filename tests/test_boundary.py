@@ -94,7 +94,9 @@ def test_empty_problem_needs_no_pointers_and_launches_nothing():
     (dict(Hq=5, Hkv=2), 3), (dict(Hq=4, Hkv=3), 3),
     (dict(D=72), 4), (dict(D=112), 4), (dict(D=32), 4), (dict(D=256), 4), (dict(D=0), 4),
     (dict(D=96, dtype=binding.FA_DTYPE_FP32), 4),
-    (dict(dtype=3), 5), (dict(dtype=-1), 5),
+    (dict(dtype=4), 5), (dict(dtype=-1), 5),
+    (dict(dtype=binding.FA_DTYPE_FP8_E4M3, bias=BIAS), 5),   # FP8 takes no logit term
+    (dict(dtype=binding.FA_DTYPE_FP8_E4M3, D=80), 4),
     (dict(scale=math.nan), 6), (dict(scale=math.inf), 6), (dict(scale=-math.inf), 6),
     (dict(q=Q + 8), 7), (dict(k=K + 4), 7), (dict(v=V + 2), 7), (dict(o=O + 8), 7),
     (dict(bias=BIAS + 8), 7), (dict(lse=L + 2), 7),
@@ -297,3 +299,22 @@ def test_chain_rejections_before_launch():
     assert chain([Q0, Q], [K0 + 8, K]) == 7                   # a layer's K misaligned
     assert chain([Q0, Q], [K0, K], o=Q0) == 8                 # output over an earlier Q
     assert chain([Q0, Q], [K0, K], B=0) == 0                  # empty: nothing launched
+
+
+def test_fp8_rejections_before_launch():
+    fp8 = binding.FA_DTYPE_FP8_E4M3
+    assert check(dtype=fp8) == 0 and check(dtype=fp8, D=128) == 0
+    # the bf16 output is twice the size of the FP8 q: [O, O + 2*|q|) must be clear
+    nq_fp8 = 2 * 4 * 100 * 64
+    assert check(dtype=fp8, o=O, lse=O + nq_fp8 + 256) == 8
+    assert check(dtype=fp8, o=O, lse=O + 2 * nq_fp8) == 0
+    lib = binding.load_library()
+    a = dict(OK_ARGS)
+    args = (a["q"], a["k"], a["v"], None, a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+            a["Nq"], a["Nk"], a["D"], a["scale"])
+    assert lib.fa_forward_window(*args, 16, fp8, None) == 5
+    assert lib.fa_forward_split(*args, 1, fp8, 2, WS, 1 << 40, None) == 5
+    bargs = (a["q"], a["k"], a["v"], None, a["o"], a["lse"], GO, DQ, DK, DV, a["B"], a["Hq"],
+             a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"])
+    assert lib.fa_backward(*bargs, 1, fp8, WS, 1 << 40, None) == 5
+    assert binding.fa_merge(WS, WS + 4096, 2, 10, 64, O, L, fp8, None) == 5

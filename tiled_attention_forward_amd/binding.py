@@ -20,7 +20,7 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 
-FA_DTYPE_BF16, FA_DTYPE_FP16, FA_DTYPE_FP32 = 0, 1, 2
+FA_DTYPE_BF16, FA_DTYPE_FP16, FA_DTYPE_FP32, FA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
 FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_BAD_SIZE", 3: "FA_ERR_HEAD_GROUPS",
@@ -155,7 +155,7 @@ def fa_version() -> str:
 def _dtype_code(t) -> int:
     import torch
     codes = {torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_FP16,
-             torch.float32: FA_DTYPE_FP32}
+             torch.float32: FA_DTYPE_FP32, torch.float8_e4m3fn: FA_DTYPE_FP8_E4M3}
     if t.dtype not in codes:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return codes[t.dtype]
@@ -182,7 +182,9 @@ def _outputs(q, out, lse):
     import torch
     B, Hq, Nq, _ = q.shape
     if out is None:
-        out = torch.empty_like(q)
+        # FP8 (E4M3) inputs give a bf16 output
+        odt = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     return out, lse

@@ -16,6 +16,7 @@ int elem_bytes(int dtype) {
     case FA_DTYPE_BF16: return 2;
     case FA_DTYPE_FP16: return 2;
     case FA_DTYPE_FP32: return 4;
+    case FA_DTYPE_FP8_E4M3: return 1;
     default: return 0;
   }
 }
@@ -44,6 +45,9 @@ extern "C" int fa_check_args(const void* q, const void* k, const void* v, const 
   // 64 and 128; 80 and 96 for the 16-bit types (kept in a 128-wide tile)
   const bool dim_ok = D == 64 || D == 128 || ((D == 80 || D == 96) && esz == 2);
   if (!dim_ok) return FA_ERR_HEAD_DIM;
+  const bool fp8 = dtype == FA_DTYPE_FP8_E4M3;
+  if (fp8 && bias != nullptr) return FA_ERR_DTYPE;  // FP8 takes no logit term
+  const int oesz = fp8 ? 2 : esz;                    // FP8 inputs give a bf16 o
   if (!isfinite(scale)) return FA_ERR_SCALE;
   const bool empty = (B == 0 || Hq == 0 || Nq == 0);
   if (empty) return FA_OK;
@@ -62,11 +66,12 @@ extern "C" int fa_check_args(const void* q, const void* k, const void* v, const 
       (bias != nullptr && !aligned(bias, 16)) || !aligned(lse, 4))
     return FA_ERR_ALIGNMENT;
   const uint64_t nq_b = uint64_t(B) * Hq * Nq * D * esz;
+  const uint64_t no_b = uint64_t(B) * Hq * Nq * D * oesz;
   const uint64_t nkv_b = uint64_t(B) * Hkv * Nk * D * esz;
   const uint64_t nb_b = bias ? uint64_t(B) * Hq * Nq * Nk * esz : 0;
   const uint64_t nl_b = uint64_t(B) * Hq * Nq * 4;
-  if (overlap(o, nq_b, q, nq_b) || overlap(o, nq_b, k, nkv_b) || overlap(o, nq_b, v, nkv_b) ||
-      overlap(o, nq_b, bias, nb_b) || overlap(o, nq_b, lse, nl_b) ||
+  if (overlap(o, no_b, q, nq_b) || overlap(o, no_b, k, nkv_b) || overlap(o, no_b, v, nkv_b) ||
+      overlap(o, no_b, bias, nb_b) || overlap(o, no_b, lse, nl_b) ||
       overlap(lse, nl_b, q, nq_b) || overlap(lse, nl_b, k, nkv_b) ||
       overlap(lse, nl_b, v, nkv_b) || overlap(lse, nl_b, bias, nb_b))
     return FA_ERR_OVERLAP;
@@ -119,6 +124,7 @@ extern "C" int fa_forward_window(const void* q, const void* k, const void* v, co
                                  int dtype, void* stream) {
   if (window < 1) return FA_ERR_BAD_SIZE;
   if (window >= (int64_t(1) << 30)) return FA_ERR_TOO_LARGE;
+  if (dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_DTYPE;  // fused FP8 forward only
   return forward_common(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, 1, int(window),
                         dtype, stream);
 }
@@ -222,6 +228,7 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, con
                                 int64_t Nq, int64_t Nk, int64_t D, float scale, int causal,
                                 int dtype, int64_t num_splits, void* workspace,
                                 int64_t workspace_bytes, void* stream) {
+  if (dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_DTYPE;  // fused FP8 forward only
   int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
@@ -264,7 +271,7 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, con
 extern "C" int fa_merge(const float* part_o, const float* part_lse, int64_t num_parts,
                         int64_t rows, int64_t D, void* o, float* lse, int dtype, void* stream) {
   const int esz = elem_bytes(dtype);
-  if (esz == 0) return FA_ERR_DTYPE;
+  if (esz == 0 || dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_DTYPE;
   if (num_parts < 0 || rows < 0 || D < 0) return FA_ERR_BAD_SIZE;
   if (D < 4 || D > 65536 || D % 4 != 0) return FA_ERR_HEAD_DIM;
   if (rows == 0) return FA_OK;
@@ -300,7 +307,7 @@ int backward_common(const void* q, const void* k, const void* v, const void* bia
                     int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, float scale,
                     int causal, int window, int dtype, void* workspace, int64_t workspace_bytes,
                     void* stream) {
-  if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;  // 16-bit types only
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;  // 16-bit only
   int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;   // the backward kernels' tiles

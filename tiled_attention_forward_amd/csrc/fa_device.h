@@ -21,6 +21,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -82,6 +84,33 @@ struct Elem<float> {
   }
 };
 
+// OCP FP8 E4M3 (bias 7, 3 mantissa bits, no infinity, largest finite 448), the
+// gfx950 native 8-bit float.  A one-byte storage type; values are only ever
+// touched as bytes, by the matrix cores and by v_cvt_pk_fp8_f32.
+struct fp8e4m3 {
+  uint8_t bits;
+};
+
+// FP8 operands of v_mfma_f32_32x32x16_fp8_fp8 are laid out like the 16-bit
+// ones of the 32x32x16 instructions (lane l: row l % 32, contraction values
+// 8 * (l / 32) .. + 7), one byte each: 8 bytes per lane.
+template <>
+struct Elem<fp8e4m3> {
+  static constexpr int KP = 8;
+  using Frag = long;
+  static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, c, 0, 0, 0);
+  }
+  // 8 floats -> 8 bytes, value i in byte i (round to nearest even)
+  static __device__ __forceinline__ Frag pack8(f32x8 x) {
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
+    return __builtin_bit_cast(Frag, u32x2{u32(lo), u32(hi)});
+  }
+};
+
 // {own value, value of lane l^32} in some order, via v_permlane32_swap.  The
 // two results are copied out of the returned vector as values before being
 // reinterpreted: applying __builtin_bit_cast to the element lvalue r[1] reads
@@ -136,6 +165,26 @@ template <int D>
 __device__ __forceinline__ int lds_swizzle_tr(int r) {
   if constexpr (D == 64) return ((r >> 1) & 1) << 2;
   return (r & 3) << 2;
+}
+
+// FP8 tiles (rows of D bytes: 4 chunks at D = 64, 8 at D = 128).
+//  * row reads (ds_read_b128, 16 lanes per cycle, 16 consecutive rows, one
+//    logical chunk): a 64-byte row covers 16 banks, so rows r and r+4 start
+//    on the same bank: chunk c ^ ((r >> 2) & 3); a 128-byte row covers 32:
+//    chunk c ^ ((r >> 1) & 7), as for 16-bit rows of 64 elements;
+//  * transposed reads (ds_read_b64_tr_b8, 32 lanes per cycle): 8 rows
+//    {0..3, 8..11} (+ a multiple of 4) of two adjacent chunks, both halves of
+//    each; rows r and r+8 must land apart (64-byte rows: chunk c ^ 2 for the
+//    second 8 rows), and at 128 bytes rows 2 apart too.
+template <int D>
+__device__ __forceinline__ int f8_swizzle_rows(int r) {
+  if constexpr (D == 64) return (r >> 2) & 3;
+  return (r >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int f8_swizzle_tr(int r) {
+  if constexpr (D == 64) return ((r >> 3) & 1) << 1;
+  return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2);
 }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0

@@ -126,7 +126,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   using E = Elem<T>;
   using Frag = typename E::Frag;
   constexpr bool F32 = std::is_same<T, float>::value;
-  using OutT = typename std::conditional<SPLIT, float, T>::type;
+  constexpr bool F8 = std::is_same<T, fp8e4m3>::value;
+  // outputs: fp32 partials (key split); bf16 for FP8 inputs; else the input type
+  using OutT = typename std::conditional<
+      SPLIT, float, typename std::conditional<F8, __bf16, T>::type>::type;
   constexpr bool OUT_F32 = F32 || SPLIT;
   constexpr int KP = E::KP;
   constexpr int KS = 2 * KP;         // contraction length of one MFMA
@@ -165,6 +168,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   static_assert(VTR || KCH * kThreads * VEC == BN * D, "K tile must split evenly");
   static_assert(NL >= 1 && NL <= kMaxChainLayers, "chain length");
   static_assert(NL == 1 || (VTR && !BIAS && !SPLIT && !WINDOW), "chain instances");
+  static_assert(!F8 || (NL == 1 && !BIAS && !SPLIT && !WINDOW && D == DL), "FP8 instances");
+  // FP8: P is stored as e4m3 for the P.V product.  It is taken as
+  // 2^(t - m_ref + 7) with the rescale threshold at 1, so every p lies in
+  // (0, 2^8] (e4m3 reaches 448) and values down to 2^-13 of the row max stay
+  // normal numbers (e4m3's smallest is 2^-6); l and O carry the same factor.
+  constexpr float kTauT = F8 ? 1.f : kTau;
+  constexpr float kPShift = F8 ? 7.f : 0.f;
+  constexpr int NKO = F8 ? NS / 2 : NS;   // K fragment reads per 32-key block
   constexpr int KTL = NL * KT;       // elements of the K tiles of all layers
   constexpr int BUF = KTL + VT;      // elements per LDS buffer
 
@@ -301,7 +312,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int off = (qi[qb] * D + s * KS + g * KP) * ESZ;  // rows past Nq read 0
-      if constexpr (F32) {
+      if constexpr (F8) {
+        if (s % 2 == 0) {  // steps s and s+1 from chunk s + g (see the K reads)
+          u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(ql_rs[l], qi[qb] * D + (s + g) * 16, 0, 0);
+          raw ^= p.q_sign;
+          qf[l][qb][s] = __builtin_bit_cast(Frag, u32x2{raw[0], raw[1]});
+          qf[l][qb][s + 1] = __builtin_bit_cast(Frag, u32x2{raw[2], raw[3]});
+        }
+      } else if constexpr (F32) {
         const u32 raw = __builtin_amdgcn_raw_buffer_load_b32(ql_rs[l], off, 0, 0);
         qf[l][qb][s] = __builtin_bit_cast(float, raw ^ p.q_sign);
       } else {
@@ -404,6 +422,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
     if constexpr (F32) {
       const u32 w = bcur[qb][kb][r >> 2][r & 3];
       return __builtin_bit_cast(float, w);
+    } else if constexpr (F8) {
+      return 0.f;  // FP8 instances take no bias
     } else {
       const u32 w = bcur[qb][kb][r >> 2][(r & 3) >> 1];
       return E::widen((r & 1) ? (w >> 16) : (w & 0xffffu));
@@ -414,6 +434,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   u32x4 kreg[VTR ? 1 : KCH];
   u32x4 vreg[VTR ? 1 : VTPT][4];   // fp32 V^T path: 4 keys x VEC columns per task
 
+  // LDS chunk swizzles of this instance (K read by rows, V read transposed)
+  auto swz_k = [](int r) {
+    if constexpr (F8) return f8_swizzle_rows<D>(r);
+    else return lds_swizzle_rows<DL>(r);
+  };
+  auto swz_v = [](int r) {
+    if constexpr (F8) return f8_swizzle_tr<D>(r);
+    else return lds_swizzle_tr<DL>(r);
+  };
   // 16-bit layout: chunk c (16 bytes) of tile row r sits at chunk
   // c ^ lds_swizzle_rows<D>(r) in K (read by rows) and c ^ lds_swizzle_tr<D>(r)
   // in V (read transposed); both bank-conflict free.
@@ -428,16 +457,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
     // logical chunks past the row (D = 80, 96) get an offset past every
     // resource range (2^31 plus a tile offset below 2^31: no wrap), so the
     // load writes zeros
-    const int lk = pc ^ lds_swizzle_rows<DL>(row), lv = pc ^ lds_swizzle_tr<DL>(row);
+    const int lk = pc ^ swz_k(row), lv = pc ^ swz_v(row);
     dma_k[i] = lk < CPRG ? (row * D + lk * VEC) * ESZ : int(0x80000000u);
     dma_v[i] = lv < CPRG ? (row * D + lv * VEC) * ESZ : int(0x80000000u);
   }
   // K operand reads: lane (row ln of a 32-key block, lane half g) reads
   // logical chunk 2*st + g.
-  int k_off[VTR ? NS : 1];
+  // (FP8: one 16-byte read feeds two MFMA steps, its first 8 bytes the
+  // contraction slots of step 2p and its last 8 those of step 2p+1, so read p
+  // takes chunk 2p + g; Q is loaded in the same order)
+  int k_off[VTR ? NKO : 1];
 #pragma unroll
-  for (int st = 0; st < (VTR ? NS : 1); ++st)
-    k_off[st] = ln * RB + (((2 * st + g) ^ lds_swizzle_rows<DL>(ln)) * 16);
+  for (int st = 0; st < (VTR ? NKO : 1); ++st)
+    k_off[st] = ln * RB + (((2 * st + g) ^ swz_k(ln)) * 16);
   // Transposed V reads (ds_read_b64_tr_b16): within each 16-lane group, lane
   // 4a+b receives element b of the 8-byte chunks read by lanes a, a+4, a+8,
   // a+12.  So lane s of the group reads row 4g + s/4 (and 8 rows further for
@@ -448,7 +480,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   for (int db = 0; db < (VTR ? NDB : 1); ++db) {
     const int r = 4 * g + ((lane >> 2) & 3);
     const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    v_off[db] = r * RB + ((c ^ lds_swizzle_tr<DL>(r)) * 16) + 8 * (lane & 1);
+    v_off[db] = r * RB + ((c ^ swz_v(r)) * 16) + 8 * (lane & 1);
+    if constexpr (F8) {
+      // ds_read_b64_tr_b8: within each 16-lane group, lane 8a+b receives byte
+      // b of the 8-byte chunks read by lanes a, a+2, ..., a+14.  Lane 16m+r
+      // (a = r % 2, j = r / 2) reads key row 4*(m/2) + j (j < 4) or + j + 4
+      // of the 16-key group, bytes 8a.. of chunk 2*db + m % 2; lane L then
+      // holds column 32*db + L % 32 for keys k16+4g+0..3, k16+4g+8..11 (g =
+      // L / 32): the order of P in the S^T registers.
+      const int m = lane >> 4, r16 = lane & 15, a = r16 & 1, jj = r16 >> 1;
+      const int rr = 4 * (m >> 1) + (jj < 4 ? jj : jj + 4);
+      const int cc = 2 * db + (m & 1);
+      v_off[db] = rr * RB + ((cc ^ swz_v(rr)) * 16) + 8 * a;
+    }
   }
 
   // Issue the direct LDS loads of tile j into buffer buf (16-bit types).
@@ -570,7 +614,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         Frag kf;
-        if constexpr (F32) {
+        if constexpr (F8) {
+          const char* src = reinterpret_cast<const char*>(sK + l * KT) + kb * 32 * RB + k_off[st / 2];
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
+          kf = (st % 2 == 0) ? __builtin_bit_cast(Frag, u32x2{raw[0], raw[1]})
+                             : __builtin_bit_cast(Frag, u32x2{raw[2], raw[3]});
+        } else if constexpr (F32) {
           kf = sK[(kb * 32 + ln) * KSTR + st * KS + g * KP];
         } else {
           const char* src = reinterpret_cast<const char*>(sK + l * KT) + kb * 32 * RB + k_off[st];
@@ -618,12 +667,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
       mx = partner_max(mx);
       m_tile[qb] = mx * ce;  // ce > 0, so max(s)*ce = max(s*ce)
-      grow_any = grow_any || (m_tile[qb] > m_ref[qb] + kTau);  // -inf + kTau stays -inf
+      grow_any = grow_any || (m_tile[qb] > m_ref[qb] + kTauT);  // -inf + kTau stays -inf
     }
     if (__builtin_amdgcn_ballot_w64(grow_any) != 0) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const bool grow = m_tile[qb] > m_ref[qb] + kTau;
+        const bool grow = m_tile[qb] > m_ref[qb] + kTauT;
         // rows that grow: alpha = 2^(m_ref - m_tile), which is 0 while m_ref = -inf
         const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref[qb] - m_tile[qb]) : 1.f;
         m_ref[qb] = grow ? m_tile[qb] : m_ref[qb];
@@ -639,7 +688,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
     float rs[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float neg_m = (m_ref[qb] == -INFINITY) ? 0.f : -m_ref[qb];  // no exp(-inf + inf)
+      const float neg_m = (m_ref[qb] == -INFINITY) ? 0.f : kPShift - m_ref[qb];  // no exp(-inf + inf)
       rs[qb] = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -685,10 +734,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
             // the S^T registers hold P in.  Each transposed read gives every
             // lane 4 consecutive keys of its column d = 32*db + lane%32.
             const char* src = reinterpret_cast<const char*>(sV) + (kb * 32 + 16 * h) * RB + v_off[db];
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 8 * RB));
-            const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
-            const Frag vf = __builtin_bit_cast(Frag, u32x4{lw[0], lw[1], hw[0], hw[1]});
+            Frag vf;
+            if constexpr (F8) {
+              vf = __builtin_bit_cast(Frag, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)src));
+            } else {
+              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
+              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 8 * RB));
+              const u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
+              vf = __builtin_bit_cast(Frag, u32x4{lw[0], lw[1], hw[0], hw[1]});
+            }
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) acc[qb][db] = E::mma(vf, pf[qb], acc[qb][db]);
           }
@@ -779,7 +833,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
             reinterpret_cast<u32x4*>(dst)[1] = bo;
           }
         } else {
-          const u32x2 aw = E::narrow4(a4), bw = E::narrow4(b4);
+          const u32x2 aw = Elem<OutT>::narrow4(a4), bw = Elem<OutT>::narrow4(b4);
           u32x4 out;
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
@@ -792,7 +846,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
         }
       }
     if (row_ok && g == 0)
-      Lh[qi[qb]] = (l_tot > 0.f) ? m_ref[qb] * kLn2 + logf(l_tot) : -INFINITY;
+      Lh[qi[qb]] = (l_tot > 0.f) ? (m_ref[qb] - kPShift) * kLn2 + logf(l_tot) : -INFINITY;
   }
 }
 
@@ -944,6 +998,7 @@ hipError_t launch_d(const Params& p, unsigned grid, hipStream_t s, bool causal, 
 // no bias tile; every other instance keeps one.  The key-split path keeps one.
 constexpr int query_blocks(int dtype, int D, bool bias, bool split) {
   return split ? 1
+               : dtype == FA_DTYPE_FP8_E4M3                   ? 1
                : (dtype != FA_DTYPE_FP32 && D == 64 && !bias) ? kQB64
                : (D == 128) ? kQB128 : 1;
 }
@@ -992,7 +1047,10 @@ Params make_params(const LaunchArgs& a, int rows_per_block, int n_rows) {
   p.c = c;
   p.scale_abs = fmaxf(fabsf(a.scale), 1e-30f / kLog2e);
   const bool neg = a.scale < 0.f;
-  p.q_sign = !neg ? 0u : (a.dtype == FA_DTYPE_FP32 ? 0x80000000u : 0x80008000u);
+  p.q_sign = !neg                          ? 0u
+             : a.dtype == FA_DTYPE_FP32     ? 0x80000000u
+             : a.dtype == FA_DTYPE_FP8_E4M3 ? 0x80808080u
+                                            : 0x80008000u;
   p.bias_vec = (a.dtype == FA_DTYPE_FP32) ? (a.Nk % 4) == 0 : (a.Nk % 8) == 0;
   p.window = a.window;
   for (int l = 0; l < kMaxChainLayers; ++l) p.chain_q[l] = p.chain_k[l] = nullptr;
@@ -1001,10 +1059,23 @@ Params make_params(const LaunchArgs& a, int rows_per_block, int n_rows) {
   return p;
 }
 
+// FP8 inputs: fused forward without a bias, D = 64 or 128 (checked by the API).
+hipError_t launch_f8(const Params& p, unsigned grid, hipStream_t s, int D, bool causal) {
+  using F8 = fp8e4m3;
+  if (D == 64)
+    return causal ? launch_one<F8, 64, 64, 1, true, false, false>(p, grid, s)
+                  : launch_one<F8, 64, 64, 1, false, false, false>(p, grid, s);
+  return causal ? launch_one<F8, 128, 64, 1, true, false, false>(p, grid, s)
+                : launch_one<F8, 128, 64, 1, false, false, false>(p, grid, s);
+}
+
 template <bool SPLIT>
 hipError_t dispatch(const Params& p, unsigned grid, const LaunchArgs& a) {
   hipStream_t s = static_cast<hipStream_t>(a.stream);
   const bool bias = a.bias != nullptr;
+  if constexpr (!SPLIT) {
+    if (a.dtype == FA_DTYPE_FP8_E4M3) return launch_f8(p, grid, s, a.D, a.causal);
+  }
   switch (a.dtype) {
     case FA_DTYPE_BF16: return launch_t<__bf16, SPLIT>(p, grid, s, a.D, a.causal, bias);
     case FA_DTYPE_FP16: return launch_t<_Float16, SPLIT>(p, grid, s, a.D, a.causal, bias);

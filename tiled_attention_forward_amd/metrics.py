@@ -5,8 +5,9 @@ Nothing here runs on the GPU or touches the attention arithmetic itself.
 
 from __future__ import annotations
 
-# MI355X published dense peaks (bf16/fp16 MFMA, fp32 MFMA) and HBM3E bandwidth.
-MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}
+# MI355X published dense peaks (bf16/fp16 MFMA, FP8 MFMA at twice the 16-bit
+# rate, fp32 MFMA) and HBM3E bandwidth.
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2, "fp32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
 

@@ -26,7 +26,8 @@ sliding-window shape is the benchmark report shape with each row limited to
 its 1024 most recent keys.  The chain shape is the same GQA setup at the last
 layer of a 4-layer Block Attention Residual block, whose logits sum the Q K^T
 products of all four layers (in place of the dense logit tensor); its Q and K
-are drawn layer by layer (Q_l, then K_l, oldest layer first), then V.
+are drawn layer by layer (Q_l, then K_l, oldest layer first), then V.  The
+FP8 shape is the benchmark report shape with Q, K and V rounded to E4M3.
 """
 
 from __future__ import annotations
@@ -36,7 +37,8 @@ from dataclasses import dataclass
 
 import torch
 
-_DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+_DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16,
+           "fp8": torch.float8_e4m3fn}
 
 
 @dataclass(frozen=True)
@@ -92,8 +94,9 @@ class Workload:
         """Algorithmic HBM bytes: read Q, K, V (every layer's Q and K for a
         chain; the visible bias entries), write O and LSE."""
         esz = torch.tensor([], dtype=self.torch_dtype).element_size()
+        oesz = 2 if self.dtype == "fp8" else esz   # FP8 inputs give a bf16 output
         nl = max(1, self.layers)
-        qo = (nl + 1) * self.B * self.Hq * self.Nq * self.D * esz
+        qo = self.B * self.Hq * self.Nq * self.D * (nl * esz + oesz)
         kv = (nl + 1) * self.B * self.Hkv * self.Nk * self.D * esz
         lse = self.B * self.Hq * self.Nq * 4
         bias = self.visible_pairs() * esz if self.bias else 0
@@ -116,6 +119,7 @@ WORKLOADS = {
                  "split"),
         Workload("b2_h16_s4096_d64_bf16_swa1024", 2, 16, 16, 4096, 4096, 64, "bf16", True, False,
                  window=1024),
+        Workload("b2_h16_s4096_d64_fp8_causal", 2, 16, 16, 4096, 4096, 64, "fp8", True, False),
         Workload("b1_hq20_hkv4_s8192_d128_bf16_causal_chain4", 1, 20, 4, 8192, 8192, 128, "bf16",
                  True, False, layers=4),
     ]
