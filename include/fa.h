@@ -71,7 +71,8 @@ typedef enum fa_status {
   FA_ERR_HEAD_DIM = 4,     /* D is not 64 or 128, nor 80 or 96 with bf16/fp16 (these     */
                            /* forward-only sizes run in 128-wide tiles, per the xnwp.cn  */
                            /* post, §5.1 and §6.4: a block narrower than the head drops  */
-                           /* or misreads columns); the backward and the residual chain  */
+                           /* or misreads columns), nor 256 with bf16/fp16 in fa_forward */
+                           /* (fused, no window); the backward and the residual chain    */
                            /* take 64 and 128.  Other sizes are rejected, never silently  */
                            /* truncated                                                  */
   FA_ERR_DTYPE = 5,        /* dtype is not one of fa_dtype                               */

@@ -92,7 +92,8 @@ def test_empty_problem_needs_no_pointers_and_launches_nothing():
 @pytest.mark.parametrize("over,code", [
     (dict(B=-1), 2), (dict(Nq=-5), 2), (dict(Nk=-1), 2), (dict(Hkv=0), 2),
     (dict(Hq=5, Hkv=2), 3), (dict(Hq=4, Hkv=3), 3),
-    (dict(D=72), 4), (dict(D=112), 4), (dict(D=32), 4), (dict(D=256), 4), (dict(D=0), 4),
+    (dict(D=72), 4), (dict(D=112), 4), (dict(D=32), 4), (dict(D=512), 4), (dict(D=0), 4),
+    (dict(D=256, dtype=binding.FA_DTYPE_FP32), 4),
     (dict(D=96, dtype=binding.FA_DTYPE_FP32), 4),
     (dict(dtype=4), 5), (dict(dtype=-1), 5),
     (dict(dtype=binding.FA_DTYPE_FP8_E4M3, bias=BIAS), 5),   # FP8 takes no logit term
@@ -116,7 +117,7 @@ def test_head_dim_pitfall_is_an_error_not_a_truncation():
     unsupported D is refused."""
     for d in (1, 16, 63, 65, 72, 88, 112, 127, 129, 192):
         assert check(D=d) == 4
-    for d in (64, 80, 96, 128):
+    for d in (64, 80, 96, 128, 256):
         assert check(D=d) == 0
         assert check(D=d, dtype=binding.FA_DTYPE_FP16) == 0
     assert check(D=80, dtype=binding.FA_DTYPE_FP32) == 4
@@ -197,6 +198,7 @@ def test_split_rejections_before_launch():
     assert split_status(workspace=O) == 8            # workspace over the output
     assert split_status(workspace=Q - 256) == 8      # runs into q
     assert split_status(D=72) == 4 and split_status(q=None) == 1   # the common checks first
+    assert split_status(D=256) == 4
     # packed rows of one KV head: (Hq/Hkv) * Nq * D * 2 bytes must stay below 2^31
     assert split_status(Hq=64, Hkv=1, Nq=1 << 18, B=1, workspace_bytes=1 << 62) == 9
     # empty problem: nothing launched, no workspace needed
@@ -246,6 +248,7 @@ def test_backward_rejections_before_launch():
     assert bwd_status(dtype=binding.FA_DTYPE_FP32) == 5       # 16-bit types only
     assert bwd_status(D=72) == 4 and bwd_status(q=None) == 1   # the forward's checks first
     assert bwd_status(D=96) == 4 and bwd_status(D=80) == 4      # forward-only head dims
+    assert bwd_status(D=256) == 4
     assert bwd_status(dout=None) == 1 and bwd_status(dq=None) == 1
     assert bwd_status(dk=None) == 1 and bwd_status(dv=None) == 1
     assert bwd_status(dq=DQ + 8) == 7 and bwd_status(dout=GO + 4) == 7
@@ -270,6 +273,7 @@ def test_window_rejections_before_launch():
     assert lib.fa_forward_window(*args, -3, a["dtype"], None) == 2
     assert lib.fa_forward_window(*args, 1 << 30, a["dtype"], None) == 9
     assert lib.fa_forward_window(*args[:11], 72, a["scale"], 16, a["dtype"], None) == 4
+    assert lib.fa_forward_window(*args[:11], 256, a["scale"], 16, a["dtype"], None) == 4
     bargs = (a["q"], a["k"], a["v"], None, a["o"], a["lse"], GO, DQ, DK, DV, a["B"], a["Hq"],
              a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"])
     assert lib.fa_backward_window(*bargs, 0, a["dtype"], WS, 1 << 40, None) == 2

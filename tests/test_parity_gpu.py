@@ -61,6 +61,11 @@ EDGE = [
     (1, 2, 1, 517, 333, 96, "bf16", True, False),
     (1, 1, 1, 1, 1, 80, "bf16", False, False),
     (1, 2, 2, 130, 70, 96, "bf16", False, False),
+    # head dim 256: 32-key tiles
+    (1, 2, 2, 300, 300, 256, "bf16", True, False),
+    (1, 4, 2, 257, 190, 256, "fp16", False, False),
+    (2, 4, 1, 130, 170, 256, "bf16", True, True),
+    (1, 2, 2, 1, 1, 256, "bf16", False, True),
 ]
 
 
@@ -255,4 +260,15 @@ def test_head_dim_80_full_size_sampled(gpu_device):
     o, lse = run_gpu(q, k, v, None, w.scale, True)
     st = sampled_check(q, k, v, None, w.scale, True, "bf16", [(0, 0), (1, 15)],
                        sample_rows(w.Nq, 64, seed=3), o, lse, "D=80 full size")
+    _log(st)
+
+
+def test_head_dim_256_full_size_sampled(gpu_device):
+    """The benchmark report shape (B2 H16 S4096 causal) with 256-wide heads."""
+    w = custom(2, 16, 16, 4096, 4096, 256, "bf16", True, False)
+    _log("full-size D=256")
+    q, k, v, _ = make_inputs(w, seed=6, device=gpu_device)
+    o, lse = run_gpu(q, k, v, None, w.scale, True)
+    st = sampled_check(q, k, v, None, w.scale, True, "bf16", [(0, 0), (1, 15)],
+                       sample_rows(w.Nq, 64, seed=6), o, lse, "D=256 full size")
     _log(st)

@@ -42,8 +42,8 @@ extern "C" int fa_check_args(const void* q, const void* k, const void* v, const 
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_BAD_SIZE;
   if (Hq > 0 && Hkv < 1) return FA_ERR_BAD_SIZE;
   if (Hq > 0 && Hq % Hkv != 0) return FA_ERR_HEAD_GROUPS;
-  // 64 and 128; 80 and 96 for the 16-bit types (kept in a 128-wide tile)
-  const bool dim_ok = D == 64 || D == 128 || ((D == 80 || D == 96) && esz == 2);
+  // 64 and 128; 80, 96 (kept in a 128-wide tile) and 256 for the 16-bit types
+  const bool dim_ok = D == 64 || D == 128 || ((D == 80 || D == 96 || D == 256) && esz == 2);
   if (!dim_ok) return FA_ERR_HEAD_DIM;
   const bool fp8 = dtype == FA_DTYPE_FP8_E4M3;
   if (fp8 && bias != nullptr) return FA_ERR_DTYPE;  // FP8 takes no logit term
@@ -125,6 +125,7 @@ extern "C" int fa_forward_window(const void* q, const void* k, const void* v, co
   if (window < 1) return FA_ERR_BAD_SIZE;
   if (window >= (int64_t(1) << 30)) return FA_ERR_TOO_LARGE;
   if (dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_DTYPE;  // fused FP8 forward only
+  if (D == 256) return FA_ERR_HEAD_DIM;                 // fused forward only
   return forward_common(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, 1, int(window),
                         dtype, stream);
 }
@@ -229,6 +230,7 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, con
                                 int dtype, int64_t num_splits, void* workspace,
                                 int64_t workspace_bytes, void* stream) {
   if (dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_DTYPE;  // fused FP8 forward only
+  if (D == 256) return FA_ERR_HEAD_DIM;                 // fused forward only
   int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
@@ -405,7 +407,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_BAD_SIZE: return "a size is negative, or Hkv < 1";
     case FA_ERR_HEAD_GROUPS: return "Hq is not a multiple of Hkv";
     case FA_ERR_HEAD_DIM:
-      return "head dimension D must be 64 or 128 (80 or 96: bf16/fp16 forward and key split)";
+      return "head dimension D must be 64 or 128 (80, 96: bf16/fp16 forward, window and key "
+             "split; 256: bf16/fp16 fused forward)";
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_SCALE: return "scale is not finite";
     case FA_ERR_ALIGNMENT: return "a tensor pointer is misaligned (16 bytes; lse 4 bytes)";

@@ -156,6 +156,8 @@ __device__ __forceinline__ int lds_swizzle(int r) {
 // lds_swizzle_tr<D> for transposed reads.  The latter ignores bit 3 of r, so
 // the second transposed read of a 16-row group (rows +8) sits at a fixed
 // 8-row byte offset from the first.
+// Rows of 256 or 512 bytes (D = 128, 256) start on the same bank, so both use
+// the same values (chunk indices stay inside the row: XOR values below 16).
 template <int D>
 __device__ __forceinline__ int lds_swizzle_rows(int r) {
   if constexpr (D == 64) return (r >> 1) & 7;

@@ -122,7 +122,7 @@ __device__ __forceinline__ int vt_pos_of_group(int kg) {  // kg = key / 4
 // buffer with the V tile; 16-bit types, no bias, no key split, no window.
 template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT, bool WINDOW,
           int NL>
-__global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : (D == 256 && BIAS) ? 1 : 2)) void fa_fwd_kernel(Params p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
   constexpr bool F32 = std::is_same<T, float>::value;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : 2)) void fa_fwd_ke
   // and the products run over ceil(D/16) contraction steps and ceil(D/32)
   // output column blocks; only the real columns are stored.
   constexpr int DL = (D == 80 || D == 96) ? 128 : D;   // LDS row width, elements
-  static_assert(D == 64 || D == 80 || D == 96 || D == 128, "head dim");
+  static_assert(D == 64 || D == 80 || D == 96 || D == 128 || D == 256, "head dim");
   static_assert(D == DL || !F32, "fp32 takes head dims 64 and 128");
   constexpr int NS = (D + KS - 1) / KS;  // MFMAs per 32x32 score block
   constexpr int ESZ = sizeof(T);
@@ -993,6 +993,21 @@ hipError_t launch_d(const Params& p, unsigned grid, hipStream_t s, bool causal, 
               : launch_one<T, D, BN, QB, false, false, SPLIT>(p, grid, s);
 }
 
+// Head dim 256 (16-bit, fused, no window): 32-key tiles, 64 KB of LDS per
+// workgroup.  Without a bias two workgroups share a compute unit (256 VGPRs
+// per lane); the bias tile's registers would spill there, so the bias
+// instances take one workgroup per compute unit and the accumulator registers
+// (B2 H16 S4096 causal: 322 us at two, 414 at one; with a bias, H8: 549 us
+// spilling at two, 214 at one).
+template <typename T>
+hipError_t launch_d256(const Params& p, unsigned grid, hipStream_t s, bool causal, bool bias) {
+  if (causal)
+    return bias ? launch_one<T, 256, 32, 1, true, true, false>(p, grid, s)
+                : launch_one<T, 256, 32, 1, true, false, false>(p, grid, s);
+  return bias ? launch_one<T, 256, 32, 1, false, true, false>(p, grid, s)
+              : launch_one<T, 256, 32, 1, false, false, false>(p, grid, s);
+}
+
 // 32-row query blocks per wave.  Two blocks (64 rows) halve the K/V operand
 // reads per MFMA, but only fit in registers for 16-bit inputs with D = 64 and
 // no bias tile; every other instance keeps one.  The key-split path keeps one.
@@ -1019,6 +1034,9 @@ hipError_t launch_t(const Params& p, unsigned grid, hipStream_t s, int D, bool c
   if constexpr (!std::is_same<T, float>::value) {
     if (D == 80) return launch_d<T, 80, kBN128, 1, SPLIT>(p, grid, s, causal, bias);
     if (D == 96) return launch_d<T, 96, kBN128, 1, SPLIT>(p, grid, s, causal, bias);
+    if constexpr (!SPLIT) {
+      if (D == 256) return launch_d256<T>(p, grid, s, causal, bias);
+    }
   }
   return launch_d<T, 128, kBN128, SPLIT ? 1 : kQB128, SPLIT>(p, grid, s, causal, bias);
 }
