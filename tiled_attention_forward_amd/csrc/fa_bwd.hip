@@ -52,6 +52,14 @@ constexpr int kBwdThreads = 256;  // 4 waves
 #ifndef FA_DKDV_MINB64
 #define FA_DKDV_MINB64 3
 #endif
+// dK/dV kernel at D = 128: the key block's K and V sit in LDS (64 KB, one
+// workgroup per compute unit), except in the non-causal instance without a
+// logit term, where they sit in registers and two workgroups share a compute
+// unit (256 VGPRs and a 120-byte spill: B8 H32 S2048 backward 2.47 -> 2.38 ms;
+// the causal instances spill twice as much there and ran 18% slower).
+constexpr bool dkdv_kv_in_registers(int D, bool causal, bool bias) {
+  return D == 64 || (D == 128 && !causal && !bias);
+}
 constexpr int kQTile = 64;        // query rows per tile in the dK/dV kernel
 constexpr int kKTile = 64;        // keys per tile in the dQ kernel
 
@@ -408,14 +416,16 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
 // the group's packed rows r = (hq - hk*group)*Nq + i (query position r % Nq).
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW>
-__global__ __launch_bounds__(kBwdThreads, (D == 64 ? (BIAS ? 2 : FA_DKDV_MINB64) : 1)) void fa_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads, (D == 64 ? (BIAS ? 2 : FA_DKDV_MINB64)
+                                                   : dkdv_kv_in_registers(D, CAUSAL, BIAS) ? 2 : 1))
+void fa_bwd_dkdv_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
   constexpr int BQ = kQTile;
   constexpr int NS = D / 16, NDB = D / 32, NQB = BQ / 32;
   constexpr int RB = D * 2;
   constexpr int TILE = BQ * RB;               // bytes per Q (or dO) tile
-  constexpr bool KV_LDS = (D == 128);         // K/V of the block in LDS, else registers
+  constexpr bool KV_LDS = !dkdv_kv_in_registers(D, CAUSAL, BIAS);  // K/V of the block in LDS, else registers
   constexpr int KVB = KV_LDS ? 128 * RB : 16; // bytes per K (or V) block in LDS
   // per stage: Q tile, dO tile, lse2[BQ], delta[BQ]
   constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
