@@ -68,12 +68,9 @@ constexpr int kThreads = kWaves * 64;
 #define FA_MINB64 2
 #endif
 // Key-split instances at D = 128 without a bias (decode-like shapes, bound by
-// the K/V stream): 32-key tiles in a ring of 3 LDS buffers, so two tiles are
-// in flight per workgroup and three workgroups fit a compute unit (decode B8
-// 20/4 heads, 32768 keys: 96.5 us against 100.6 with two 64-key buffers).
-#ifndef FA_SPLIT_NBUF
-#define FA_SPLIT_NBUF 3
-#endif
+// the K/V stream): 32-key tiles, 163-166 VGPRs, so three workgroups fit a
+// compute unit (decode B8 20/4 heads, 32768 keys: 96.2 us against 100.5 with
+// 64-key tiles; a third LDS buffer adds nothing, 96.8 us).
 #ifndef FA_SPLIT_BN128
 #define FA_SPLIT_BN128 32
 #endif
@@ -188,14 +185,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : (D == 256 && BIAS)
   constexpr int NKO = F8 ? NS / 2 : NS;   // K fragment reads per 32-key block
   constexpr int KTL = NL * KT;       // elements of the K tiles of all layers
   constexpr int BUF = KTL + VT;      // elements per LDS buffer
-  // LDS buffers: two (tile j+1 loads while tile j is computed), or a deeper
-  // ring for the D = 128 key-split instances without a bias, which stream far
-  // more K/V bytes than they compute on (their only loads in the loop are the
-  // tiles', so the wait can count them)
-  constexpr int NBUF = (SPLIT && !BIAS && VTR && D == 128) ? FA_SPLIT_NBUF : 2;
-  static_assert(NBUF >= 2 && NBUF <= 4, "LDS ring depth");
-
-  __shared__ __attribute__((aligned(16))) T smem[NBUF * BUF];
+  // two LDS buffers: tile j+1 loads while tile j is computed
+  __shared__ __attribute__((aligned(16))) T smem[2 * BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -767,79 +758,48 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : (D == 256 && BIAS)
     }
   };
 
-  if constexpr (NBUF > 2) {
-    // ---- main loop, ring of NBUF buffers: tile j in buffer (j - j_begin) % NBUF;
-    // tiles j+1 .. j+NBUF-2 stay in flight while tile j is computed.  At the
-    // top of iteration j: wait for this wave's loads of tile j (the later
-    // tiles' may remain), barrier (tile j visible everywhere, every wave done
-    // with tile j-1), then refill tile j-1's buffer with tile j+NBUF-1.
-    constexpr int PER_TILE = 2 * DNI;  // direct loads per wave per tile (K and V)
-    auto wait_tiles_after = [&](int ahead) {
-      // s_waitcnt immediate: vmcnt bits [3:0] and [15:14]
-      constexpr int v1 = PER_TILE, v2 = 2 * PER_TILE;
-      if (ahead >= 2)
-        __builtin_amdgcn_s_waitcnt(kWaitVmem0 | (v2 & 15) | ((v2 >> 4) << 14));
-      else if (ahead == 1)
-        __builtin_amdgcn_s_waitcnt(kWaitVmem0 | (v1 & 15) | ((v1 >> 4) << 14));
-      else
-        __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-    };
-    static_assert(2 * PER_TILE < 64, "vmcnt range");
+  // ---- main loop: double-buffered K/V tiles -------------------------------------
+  // Tile j+1 is requested (into the other LDS buffer, or into registers for
+  // fp32) before tile j is computed; one barrier per tile.  The buffer being
+  // filled was last read in the previous iteration, before its barrier.
+  if (j_end > j_begin) {
+    dma_tile(j_begin, 0);
+    gload(j_begin);
+    if constexpr (BIAS) load_bias(bcur, j_begin);
+    sstore(0);
+    if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    __syncthreads();
+  }
+  for (int j = j_begin; j < j_end; ++j) {
+    const int cur = (j - j_begin) & 1;
+    const bool has_next = j + 1 < j_end;
+    if (has_next) {
+      dma_tile(j + 1, cur ^ 1);
+      gload(j + 1);
+    }
+    // a wave skips tiles above its rows' diagonal and, with a window, tiles
+    // wholly left of its rows' windows
+    const bool active = wave_has_rows && (!CAUSAL || (j * BN <= wave_pos_max &&
+                                                      j * BN + BN - 1 >= wave_key_lo));
+    if constexpr (BIAS) {
+      const bool next_active =
+          has_next && wave_has_rows &&
+          (!CAUSAL || ((j + 1) * BN <= wave_pos_max && (j + 1) * BN + BN - 1 >= wave_key_lo));
+      if (next_active) load_bias(bnext, j + 1);
+    }
+    if (active) compute(j, cur);
+    if constexpr (BIAS) {
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i)
-      if (j_begin + i < j_end) dma_tile(j_begin + i, i);
-    for (int j = j_begin; j < j_end; ++j) {
-      wait_tiles_after(min(NBUF - 2, j_end - 1 - j));
-      __syncthreads();
-      if (j + NBUF - 1 < j_end) dma_tile(j + NBUF - 1, (j + NBUF - 1 - j_begin) % NBUF);
-      const bool active = wave_has_rows && (!CAUSAL || (j * BN <= wave_pos_max &&
-                                                        j * BN + BN - 1 >= wave_key_lo));
-      if (active) compute(j, (j - j_begin) % NBUF);
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) bcur[qb][kb][q4] = bnext[qb][kb][q4];
     }
-  } else {
-    // ---- main loop: double-buffered K/V tiles -------------------------------------
-    // Tile j+1 is requested (into the other LDS buffer, or into registers for
-    // fp32) before tile j is computed; one barrier per tile.  The buffer being
-    // filled was last read in the previous iteration, before its barrier.
-    if (j_end > j_begin) {
-      dma_tile(j_begin, 0);
-      gload(j_begin);
-      if constexpr (BIAS) load_bias(bcur, j_begin);
-      sstore(0);
-      if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-      __syncthreads();
-    }
-    for (int j = j_begin; j < j_end; ++j) {
-      const int cur = (j - j_begin) & 1;
-      const bool has_next = j + 1 < j_end;
-      if (has_next) {
-        dma_tile(j + 1, cur ^ 1);
-        gload(j + 1);
-      }
-      // a wave skips tiles above its rows' diagonal and, with a window, tiles
-      // wholly left of its rows' windows
-      const bool active = wave_has_rows && (!CAUSAL || (j * BN <= wave_pos_max &&
-                                                        j * BN + BN - 1 >= wave_key_lo));
-      if constexpr (BIAS) {
-        const bool next_active =
-            has_next && wave_has_rows &&
-            (!CAUSAL || ((j + 1) * BN <= wave_pos_max && (j + 1) * BN + BN - 1 >= wave_key_lo));
-        if (next_active) load_bias(bnext, j + 1);
-      }
-      if (active) compute(j, cur);
-      if constexpr (BIAS) {
-  #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-  #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-  #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) bcur[qb][kb][q4] = bnext[qb][kb][q4];
-      }
-      if (has_next) sstore(cur ^ 1);
-      // the direct LDS loads of this wave are done before the barrier publishes them
-      if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-      __syncthreads();
-    }
+    if (has_next) sstore(cur ^ 1);
+    // the direct LDS loads of this wave are done before the barrier publishes them
+    if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 -----------------------------
@@ -1086,9 +1046,13 @@ hipError_t launch_t(const Params& p, unsigned grid, hipStream_t s, int D, bool c
     }
   }
   if constexpr (SPLIT) {
-    // (the bias instances keep two 64-key buffers)
-    if (!bias) return launch_d<T, 128, FA_SPLIT_BN128, 1, SPLIT>(p, grid, s, causal, false);
-    return launch_d<T, 128, kBN128, 1, SPLIT>(p, grid, s, causal, true);
+    // (32-key tiles without a bias, 64 with one)
+    constexpr int BS = FA_SPLIT_BN128;
+    if (causal)
+      return bias ? launch_one<T, 128, kBN128, 1, true, true, true>(p, grid, s)
+                  : launch_one<T, 128, BS, 1, true, false, true>(p, grid, s);
+    return bias ? launch_one<T, 128, kBN128, 1, false, true, true>(p, grid, s)
+                : launch_one<T, 128, BS, 1, false, false, true>(p, grid, s);
   } else {
     return launch_d<T, 128, kBN128, kQB128, SPLIT>(p, grid, s, causal, bias);
   }
