@@ -366,15 +366,23 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
                 b_rs, (row_off + 8 * (r >> 2) + (r & 3)) * 2, 0, 0));
         }
       }
+      // logits, then one masking pass for the whole block (tested once,
+      // not per register), then P and dS^T
+      float t[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        t[r] = BIAS ? fmaf(s[kb][r], p.c, fmaf(bvals[r], kLog2e, -lse2))
+                    : fmaf(s[kb][r], p.c, -lse2);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= p.Nk || (CAUSAL && key > qi) || (W > 0 && key <= qi - W)) t[r] = -INFINITY;
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float t = BIAS ? fmaf(s[kb][r], p.c, fmaf(bvals[r], kLog2e, -lse2))
-                       : fmaf(s[kb][r], p.c, -lse2);
-        if (need_mask) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= p.Nk || (CAUSAL && key > qi) || (W > 0 && key <= qi - W)) t = -INFINITY;
-        }
-        const float pr = __builtin_amdgcn_exp2f(t);
+        const float pr = __builtin_amdgcn_exp2f(t[r]);
         s[kb][r] = pr * (dp[kb][r] - dlt);  // dS^T
       }
     }
@@ -575,28 +583,42 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       const bool need_mask =
           tail || (CAUSAL && pos_min(rb0, min(rb0 + 31, R - 1)) < kw0 + 31) ||
           (W > 0 && pos_max(rb0, min(rb0 + 31, R - 1)) >= kw0 + W);
+      // logits, then one masking pass for the whole block (tested once,
+      // not per register), then P and dS
+      // (the logits replace the scores in s)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int qr = qb * 32 + 8 * q4 + 4 * g;  // tile row of register 4*q4
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + qr);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + qr);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * q4 + e;
-          float tv = fmaf(s[r], p.c, -l4[e]);
+          s[r] = fmaf(s[r], p.c, -l4[e]);
           if constexpr (BIAS) {
             // key kj's column of tile row qr + e (2-byte loads: the lanes of a
             // wave read 32 adjacent keys of one row)
             const u32 bw = __builtin_amdgcn_raw_buffer_load_b16(
                 b_rs, ((qr + e) * p.Nk + min(kj, p.Nk)) * 2, 0, 0);
-            tv = fmaf(E::widen(bw), kLog2e, tv);
+            s[r] = fmaf(E::widen(bw), kLog2e, s[r]);
           }
-          if (need_mask) {
-            const int row = r0 + qr + e;
-            const int pos = straddle ? row % p.Nq : pos0 + qr + e;
-            if (row >= R || (CAUSAL && kj > pos) || (W > 0 && kj <= pos - W)) tv = -INFINITY;
-          }
-          const float pr = __builtin_amdgcn_exp2f(tv);
+        }
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qr = qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);  // tile row of register r
+          const int row = r0 + qr;
+          const int pos = straddle ? row % p.Nq : pos0 + qr;
+          if (row >= R || (CAUSAL && kj > pos) || (W > 0 && kj <= pos - W)) s[r] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + qb * 32 + 8 * q4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          const float pr = __builtin_amdgcn_exp2f(s[r]);
           s[r] = pr;
           dp[r] = pr * (dp[r] - d4[e]);  // dS
         }
