@@ -73,6 +73,7 @@ CASES = [
     (1, 2, 2, 1, 1, 64, "bf16", False, False),
     (1, 3, 3, 65, 63, 128, "fp16", True, True),
     (1, 2, 2, 1000, 1000, 64, "bf16", True, False),
+    (1, 6, 2, 7, 40, 64, "bf16", True, True),        # group 3, fewer rows than a tile
 ]
 
 
@@ -145,6 +146,7 @@ WINDOW_CASES = [
     (1, 4, 1, 200, 260, 128, "bf16", True, 100),     # GQA, bias, Nk > Nq
     (2, 2, 2, 513, 513, 64, "fp16", False, 129),
     (1, 5, 1, 64, 64, 64, "bf16", False, 5),          # group 5: row tiles cross heads
+    (1, 3, 1, 20, 20, 128, "bf16", False, 6),         # group 3, fewer rows than a tile
 ]
 
 

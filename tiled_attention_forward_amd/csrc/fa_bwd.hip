@@ -505,54 +505,42 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     dva[db] = f32x16{};
   }
 
-  // Query positions covered by packed rows [r0, r1]: a run inside one head
-  // covers r0 % Nq .. r1 % Nq; a run across a head boundary is taken to cover
-  // 0 .. Nq-1 (a safe over-estimate).
-  auto pos_max = [&](int r0, int r1) {
-    return (r0 / p.Nq == r1 / p.Nq) ? r1 % p.Nq : p.Nq - 1;
-  };
-  auto pos_min = [&](int r0, int r1) { return (r0 / p.Nq == r1 / p.Nq) ? r0 % p.Nq : 0; };
-  const int n_t = (R + BQ - 1) / BQ;
-  // sliding window (causal only): the query at position i sees keys i-W+1 .. i
+  // Query tiles: BQ rows i0 .. i0+BQ-1 of one query head h of the group
+  // (packed row r0 = h*Nq + i0), so a row's query position is i0 plus its
+  // offset in the tile; rows at or past Nq belong to the next head (or lie
+  // past the group's last row, where the loads return 0) and are masked.
+  // Tiles ti = i0 / BQ in [ti_lo, ti_end) of every head matter to this
+  // workgroup: causal, a tile whose last position precedes the block's first
+  // key sees none of it; with a window, a tile whose first position comes W or
+  // more after the block's last key sees none either.
   const int W = (CAUSAL && WINDOW) ? p.window : 0;
-  // a query tile matters to this workgroup unless every one of its queries
-  // precedes every key of the block (causal), or comes after the block's last
-  // key by W or more (window)
-  auto tile_visible = [&](int t) {
-    if (!CAUSAL) return true;
-    const int r0 = t * BQ, r1 = min(r0 + BQ, R) - 1;
-    return pos_max(r0, r1) >= k_blk && (W == 0 || pos_min(r0, r1) <= k_blk + 127 + W - 1);
-  };
-  auto next_visible = [&](int t) {
-    while (t < n_t && !tile_visible(t)) ++t;
-    return t;
-  };
+  const int NT = (p.Nq + BQ - 1) / BQ;  // tiles per head
+  const int ti_lo = CAUSAL ? min(NT, k_blk / BQ) : 0;
+  const int ti_end = W > 0 ? min(NT, (k_blk + 126 + W) / BQ + 1) : NT;
+  const int n_vis = max(0, ti_end - ti_lo);  // visible tiles per head
 
-  auto issue = [&](int t, int buf) {
+  auto issue = [&](int r0, int buf) {
     char* st = smem + buf * STAGE;
-    const uint32_t soff = uint32_t(t) * BQ * RB;
+    const uint32_t soff = uint32_t(r0) * RB;
     tl.issue(q_rs, st, wave, soff);
     tl.issue(g_rs, st + TILE, wave, soff);
     // lse2 and delta: 64 floats each, by 16 lanes of waves 0 and 1
     if (wave == 0) {
       if (lane < 16)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(l_rs, (lds_void*)(st + 2 * TILE), 16,
-                                                 unsigned(lane * 16), uint32_t(t) * BQ * 4, 0, 0);
+                                                 unsigned(lane * 16), uint32_t(r0) * 4, 0, 0);
     } else if (wave == 1) {
       if (lane < 16)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d_rs, (lds_void*)(st + 2 * TILE + BQ * 4), 16,
-                                                 unsigned(lane * 16), uint32_t(t) * BQ * 4, 0, 0);
+                                                 unsigned(lane * 16), uint32_t(r0) * 4, 0, 0);
     }
   };
 
-  auto compute = [&](int t, int buf) {
+  auto compute = [&](int r0, int i0, int buf) {
     const char* sQ = smem + buf * STAGE;
     const char* sG = sQ + TILE;
     const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
     const float* sD = sL + BQ;
-    const int r0 = t * BQ;
-    const bool straddle = (r0 / p.Nq) != ((r0 + BQ - 1) / p.Nq);
-    const int pos0 = r0 % p.Nq;
     // bias rows of this tile (reads past the group's rows or keys return 0)
     const T* btile = BIAS ? static_cast<const T*>(p.bias) + (row_base + r0) * p.Nk
                           : static_cast<const T*>(p.q);
@@ -560,10 +548,11 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         make_rsrc(btile, BIAS ? uint32_t(min(BQ, R - r0)) * uint32_t(p.Nk) * 2 : 0u);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      const int rb0 = r0 + qb * 32;  // first packed row of this 32-row block
-      if (rb0 >= R) break;
-      if (CAUSAL && pos_max(rb0, min(rb0 + 31, R - 1)) < kw0) continue;  // all masked
-      if (W > 0 && pos_min(rb0, min(rb0 + 31, R - 1)) > kw0 + 31 + W - 1) continue;
+      const int ib0 = i0 + qb * 32;  // query position of this 32-row block's first row
+      if (ib0 >= p.Nq) break;
+      const int ib1 = min(ib0 + 31, p.Nq - 1);  // and of its last valid row
+      if (CAUSAL && ib1 < kw0) continue;  // all masked
+      if (W > 0 && ib0 > kw0 + 31 + W - 1) continue;
       f32x16 s, dp;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
@@ -579,10 +568,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         dp = E::mma(ga, vb, st == 0 ? f32x16{} : dp);
       }
       // register r: query row qb*32 + 8*(r/4) + 4*g + r%4 of the tile, key kj
-      const bool tail = rb0 + 32 > R;
+      const bool tail = ib0 + 32 > p.Nq;
       const bool need_mask =
-          tail || (CAUSAL && pos_min(rb0, min(rb0 + 31, R - 1)) < kw0 + 31) ||
-          (W > 0 && pos_max(rb0, min(rb0 + 31, R - 1)) >= kw0 + W);
+          tail || (CAUSAL && ib0 < kw0 + 31) || (W > 0 && ib1 >= kw0 + W);
       // logits, then one masking pass for the whole block (tested once,
       // not per register), then P and dS
       // (the logits replace the scores in s)
@@ -606,10 +594,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int qr = qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);  // tile row of register r
-          const int row = r0 + qr;
-          const int pos = straddle ? row % p.Nq : pos0 + qr;
-          if (row >= R || (CAUSAL && kj > pos) || (W > 0 && kj <= pos - W)) s[r] = -INFINITY;
+          const int pos = i0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);  // register r's row
+          if (pos >= p.Nq || (CAUSAL && kj > pos) || (W > 0 && kj <= pos - W)) s[r] = -INFINITY;
         }
       }
 #pragma unroll
@@ -639,18 +625,25 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  int t = next_visible(0);
-  if (t < n_t) issue(t, 0);
+  // the visible tiles in order: head h, tile ti (i0 = ti * BQ)
+  const int n_tiles = n_vis > 0 ? p.group * n_vis : 0;
+  int h = 0, ti = ti_lo;
+  if (n_tiles > 0) issue(ti * BQ, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   __syncthreads();
   int buf = 0;
-  while (t < n_t) {
-    const int tn = next_visible(t + 1);
-    if (tn < n_t) issue(tn, buf ^ 1);
-    compute(t, buf);
+  for (int u = 0; u < n_tiles; ++u) {
+    int hn = h, tn = ti + 1;  // the next visible tile
+    if (tn == ti_end) {
+      tn = ti_lo;
+      ++hn;
+    }
+    if (u + 1 < n_tiles) issue(hn * p.Nq + tn * BQ, buf ^ 1);
+    compute(h * p.Nq + ti * BQ, ti * BQ, buf);
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);
     __syncthreads();
-    t = tn;
+    h = hn;
+    ti = tn;
     buf ^= 1;
   }
 
