@@ -129,7 +129,15 @@ __device__ __forceinline__ int vt_pos_of_group(int kg) {  // kg = key / 4
 // buffer with the V tile; 16-bit types, no bias, no key split, no window.
 template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT, bool WINDOW,
           int NL>
-__global__ __launch_bounds__(kThreads, (D == 64 ? FA_MINB64 : (D == 256 && BIAS) ? 1 : 2)) void fa_fwd_kernel(Params p) {
+// (waves per SIMD asked of the compiler: fp32 at D = 128 with 64-key tiles
+// holds 137 KB of LDS, so one workgroup per compute unit, and the D = 256
+// bias instances keep their accumulators in AGPRs at one)
+__global__ __launch_bounds__(kThreads,
+                             (D == 64                                                  ? FA_MINB64
+                              : (D == 256 && BIAS)                                     ? 1
+                              : (std::is_same<T, float>::value && D == 128 && BN == 64) ? 1
+                                                                                        : 2))
+void fa_fwd_kernel(Params p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
   constexpr bool F32 = std::is_same<T, float>::value;
