@@ -664,13 +664,19 @@ void fa_fwd_kernel(Params p) {
           (CAUSAL && key0 + BN - 1 > pos_min(wq0 + 32 * qb, wq0 + 32 * qb + 31)) ||
           (W > 0 && key0 <= pos_max(wq0 + 32 * qb, wq0 + 32 * qb + 31) - W);
       if (need_mask) {
+        // Register r of block kb holds the key at a constant offset from the
+        // lane's first key key0 + 4g; the visible keys are those at offsets
+        // in [lo, hi): below Nk, not after the row's position (causal), and
+        // not W or more before it (window).
+        const int first = key0 + 4 * g;
+        const int hi = (CAUSAL ? min(p.Nk, qpos[qb] + 1) : p.Nk) - first;
+        const int lo = qpos[qb] - W + 1 - first;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool dead = key >= p.Nk || (CAUSAL && key > qpos[qb]) ||
-                              (W > 0 && key <= qpos[qb] - W);
+            const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+            const bool dead = off >= hi || (W > 0 && off < lo);
             if (dead) s[qb][kb][r] = -INFINITY;
           }
       }
