@@ -71,6 +71,12 @@ constexpr int kThreads = kWaves * 64;
 // the K/V stream): 32-key tiles, 163-166 VGPRs, so three workgroups fit a
 // compute unit (decode B8 20/4 heads, 32768 keys: 96.2 us against 100.5 with
 // 64-key tiles; a third LDS buffer adds nothing, 96.8 us).
+#ifndef FA_OPAQUE_KOFF
+#define FA_OPAQUE_KOFF 1
+#endif
+#ifndef FA_SCALAR_WAVE
+#define FA_SCALAR_WAVE 1
+#endif
 #ifndef FA_SPLIT_BN128
 #define FA_SPLIT_BN128 32
 #endif
@@ -483,8 +489,12 @@ void fa_fwd_kernel(Params p) {
   // takes chunk 2p + g; Q is loaded in the same order)
   int k_off[VTR ? NKO : 1];
 #pragma unroll
-  for (int st = 0; st < (VTR ? NKO : 1); ++st)
+  for (int st = 0; st < (VTR ? NKO : 1); ++st) {
     k_off[st] = ln * RB + (((2 * st + g) ^ swz_k(ln)) * 16);
+    // (kept whole: split into its row and chunk parts, each read would cost
+    // two adds instead of one)
+    if (FA_OPAQUE_KOFF) asm volatile("" : "+v"(k_off[st]));
+  }
   // Transposed V reads (ds_read_b64_tr_b16): within each 16-lane group, lane
   // 4a+b receives element b of the 8-byte chunks read by lanes a, a+4, a+8,
   // a+12.  So lane s of the group reads row 4g + s/4 (and 8 rows further for
@@ -510,14 +520,16 @@ void fa_fwd_kernel(Params p) {
     }
   }
 
-  // Issue the direct LDS loads of tile j into buffer buf (16-bit types).
+  // Issue the direct LDS loads of tile j into buffer buf (16-bit types); the
+  // wave index is taken as a scalar, so the destination (M0) is scalar work.
+  const int wave_s = FA_SCALAR_WAVE ? __builtin_amdgcn_readfirstlane(wave) : wave;
   auto dma_tile = [&](int j, int buf) {
     if constexpr (VTR) {
       char* base = reinterpret_cast<char*>(smem + buf * BUF);
       const int soff = j * BN * D * ESZ;
 #pragma unroll
       for (int i = 0; i < DNI; ++i) {
-        char* dst = base + (wave * DNI + i) * 1024;
+        char* dst = base + (wave_s * DNI + i) * 1024;
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
           // (a const copy: with the array element itself as the argument the
