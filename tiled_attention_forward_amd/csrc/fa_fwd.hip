@@ -77,6 +77,10 @@ constexpr int kThreads = kWaves * 64;
 #ifndef FA_SCALAR_WAVE
 #define FA_SCALAR_WAVE 1
 #endif
+#ifndef FA_SPLIT_KV_STREAM
+#define FA_SPLIT_KV_STREAM 1
+#endif
+constexpr int kPolicyNT = 2;  // buffer-load cache policy: non-temporal
 #ifndef FA_SPLIT_BN128
 #define FA_SPLIT_BN128 32
 #endif
@@ -134,7 +138,7 @@ __device__ __forceinline__ int vt_pos_of_group(int kg) {  // kg = key / 4
 // layers of Q_l K_l^T * scale, the K tiles of all layers sharing one LDS
 // buffer with the V tile; 16-bit types, no bias, no key split, no window.
 template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT, bool WINDOW,
-          int NL>
+          int NL, int KVPOL>
 // (waves per SIMD asked of the compiler: fp32 at D = 128 with 64-key tiles
 // holds 137 KB of LDS, so one workgroup per compute unit, and the D = 256
 // bias instances keep their accumulators in AGPRs at one)
@@ -522,6 +526,7 @@ void fa_fwd_kernel(Params p) {
 
   // Issue the direct LDS loads of tile j into buffer buf (16-bit types); the
   // wave index is taken as a scalar, so the destination (M0) is scalar work.
+  // KVPOL is the loads' cache policy (see launch_one).
   const int wave_s = FA_SCALAR_WAVE ? __builtin_amdgcn_readfirstlane(wave) : wave;
   auto dma_tile = [&](int j, int buf) {
     if constexpr (VTR) {
@@ -536,10 +541,10 @@ void fa_fwd_kernel(Params p) {
           // host pass silently emits no launch stub for the kernel)
           const __amdgpu_buffer_rsrc_t kr = kl_rs[l];
           __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(dst + l * KT * ESZ), 16,
-                                                   unsigned(dma_k[i]), unsigned(soff), 0, 0);
+                                                   unsigned(dma_k[i]), unsigned(soff), 0, KVPOL);
         }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rs, (lds_void*)(dst + KTL * ESZ), 16,
-                                                 unsigned(dma_v[i]), unsigned(soff), 0, 0);
+                                                 unsigned(dma_v[i]), unsigned(soff), 0, KVPOL);
       }
     }
   };
@@ -976,13 +981,25 @@ __global__ __launch_bounds__(kMergeWaves * 64) void fa_merge_kernel(
   }
 }
 
+// Cache policy of the K/V tile loads: in the key split, when a KV head's
+// packed rows fit one row block (decode-like shapes), every K/V tile is read
+// by exactly one workgroup, and the loads carry the non-temporal hint (decode
+// B8 20/4 heads, 32768 keys: 82.6 against 96.4 us); everywhere else other row
+// blocks of the head re-read the tiles from L2, and the hint costs about 4%.
+// The choice is a template argument: a branch on it inside the tile loop cost
+// 1.3% on the split instances that do not take it.
 template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT,
           bool WINDOW = false, int NL = 1>
 hipError_t launch_one(const Params& p, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&p)};
-  return hipLaunchKernel(
-      reinterpret_cast<const void*>(&fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT, WINDOW, NL>),
-      dim3(grid), dim3(kThreads), args, 0, stream);
+  const void* fn = reinterpret_cast<const void*>(
+      &fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT, WINDOW, NL, 0>);
+  if constexpr (SPLIT && FA_SPLIT_KV_STREAM && !std::is_same<T, float>::value) {
+    if (p.n_qtiles == 1)
+      fn = reinterpret_cast<const void*>(
+          &fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT, WINDOW, NL, kPolicyNT>);
+  }
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
 }
 
 // Chain instances.  Keys per tile: the K tiles of all layers and the V tile
