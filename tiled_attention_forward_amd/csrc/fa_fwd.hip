@@ -126,6 +126,27 @@ __device__ __forceinline__ int vt_pos_of_group(int kg) {  // kg = key / 4
   return (kg >> 2) * 16 + sigma * 4;
 }
 
+// One 16-byte-per-lane direct HBM->LDS load, issued from inline assembly (M0
+// holds the wave's LDS destination).  The compiler then neither knows nor
+// waits for it: the builtin's load draws a wait for every outstanding vector
+// load before the first transposed V read of the tile, which also drains the
+// bias loads of the next tile issued at the top of the loop.  The kernel's
+// own vmcnt(0) before the tile barrier covers these loads.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int POL>
+__device__ __forceinline__ void dma16_asm(__amdgpu_buffer_rsrc_t rs, lds_void* dst,
+                                          unsigned voff, unsigned soff) {
+  const unsigned m = static_cast<unsigned>(reinterpret_cast<size_t>(dst));
+  if constexpr (POL == kPolicyNT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :: "s"(m), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(m), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // SPLIT = false: one workgroup per (batch, query head, 128-row block); O and
 // LSE are final.
 // SPLIT = true (key-split path): the query heads that share a KV head are
@@ -540,11 +561,18 @@ void fa_fwd_kernel(Params p) {
           // (a const copy: with the array element itself as the argument the
           // host pass silently emits no launch stub for the kernel)
           const __amdgpu_buffer_rsrc_t kr = kl_rs[l];
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(dst + l * KT * ESZ), 16,
-                                                   unsigned(dma_k[i]), unsigned(soff), 0, KVPOL);
+          if constexpr (BIAS)
+            dma16_asm<KVPOL>(kr, (lds_void*)(dst + l * KT * ESZ), unsigned(dma_k[i]),
+                             unsigned(soff));
+          else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(dst + l * KT * ESZ), 16,
+                                                     unsigned(dma_k[i]), unsigned(soff), 0, KVPOL);
         }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rs, (lds_void*)(dst + KTL * ESZ), 16,
-                                                 unsigned(dma_v[i]), unsigned(soff), 0, KVPOL);
+        if constexpr (BIAS)
+          dma16_asm<KVPOL>(v_rs, (lds_void*)(dst + KTL * ESZ), unsigned(dma_v[i]), unsigned(soff));
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rs, (lds_void*)(dst + KTL * ESZ), 16,
+                                                   unsigned(dma_v[i]), unsigned(soff), 0, KVPOL);
       }
     }
   };
