@@ -1009,6 +1009,51 @@ __global__ __launch_bounds__(kMergeWaves * 64) void fa_merge_kernel(
   }
 }
 
+// Few partial results (up to kMergeFew): one lane per (row, 4 columns) loops
+// over the parts itself, with no exchange between waves.  The arithmetic is
+// the one above in the same order (with at most one part per wave there it
+// is bit-identical); the split kernels' many-part decode merges keep the
+// kernel above, which spreads the parts of a row over the waves.
+constexpr int kMergeFew = 4;
+template <typename T>
+__global__ __launch_bounds__(256) void fa_merge_few_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, int n_parts,
+    int64_t rows, int d4, T* __restrict__ o, float* __restrict__ lse) {
+  constexpr bool F32 = std::is_same<T, float>::value;
+  const int64_t total = rows * d4;
+  const int64_t D = int64_t(4) * d4;
+  for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < total;
+       t += int64_t(gridDim.x) * 256) {
+    const int64_t row = t / d4;
+    const int c4 = int(t - row * d4);
+    float m = -INFINITY;
+    for (int sp = 0; sp < n_parts; ++sp) m = fmaxf(m, part_lse[sp * rows + row]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+      for (int sp = 0; sp < n_parts; ++sp) {
+        const float ls = part_lse[sp * rows + row];
+        if (ls == -INFINITY) continue;
+        const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(part_o + (sp * rows + row) * D + 4 * c4);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= inv;
+    T* dst = o + row * D + 4 * c4;
+    if constexpr (F32) {
+      *reinterpret_cast<f32x4*>(dst) = acc;
+    } else {
+      *reinterpret_cast<u32x2*>(dst) = Elem<T>::narrow4(acc);
+    }
+    if (c4 == 0) lse[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
+  }
+}
+
 // Cache policy of the K/V tile loads: in the key split, when a KV head's
 // packed rows fit one row block (decode-like shapes), every K/V tile is read
 // by exactly one workgroup, and the loads carry the non-temporal hint (decode
@@ -1193,6 +1238,26 @@ hipError_t merge(const float* part_o, const float* part_lse, int n_parts, int64_
                  void* o, float* lse, int dtype, hipStream_t s) {
   const int d4 = D / 4;
   const int64_t total = rows * d4;
+  if (n_parts <= kMergeFew) {
+    // one lane per item, up to 32 workgroups per CU; the kernel strides over the rest
+    const int64_t want_few = (total + 255) / 256;
+    const unsigned grid_few = unsigned(want_few < 8192 ? want_few : 8192);
+    switch (dtype) {
+      case FA_DTYPE_BF16:
+        fa_merge_few_kernel<__bf16><<<grid_few, 256, 0, s>>>(part_o, part_lse, n_parts, rows, d4,
+                                                             static_cast<__bf16*>(o), lse);
+        break;
+      case FA_DTYPE_FP16:
+        fa_merge_few_kernel<_Float16><<<grid_few, 256, 0, s>>>(
+            part_o, part_lse, n_parts, rows, d4, static_cast<_Float16*>(o), lse);
+        break;
+      default:
+        fa_merge_few_kernel<float><<<grid_few, 256, 0, s>>>(part_o, part_lse, n_parts, rows, d4,
+                                                            static_cast<float*>(o), lse);
+        break;
+    }
+    return hipGetLastError();
+  }
   // one workgroup per 64 items, up to 64 per CU; the kernel strides over the rest
   const int64_t want = (total + 63) / 64;
   const unsigned grid = unsigned(want < 16384 ? want : 16384);
