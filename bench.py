@@ -44,9 +44,11 @@ sys.path.insert(0, ROOT)
 PAGE_FLASH_ATTN_V2_TFLOPS = 11.57
 METRIC = ("attention TFLOPS (4·B·H·S²·D/t) and % MFMA bf16 peak at "
           "B2 H16 S4096 D64 causal")
+# (the build script too: its compiler flags shape the generated code)
 KERNEL_SOURCES = {
     p: [os.path.join(ROOT, "tiled_attention_forward_amd", "csrc", f)
         for f in (("fa_fwd.hip", "fa_device.h") if p == "forward" else ("fa_bwd.hip", "fa_device.h"))]
+    + [os.path.join(ROOT, "tiled_attention_forward_amd", "build.py")]
     for p in ("forward", "backward")
 }
 BACKWARD_FLOP_FACTOR = 2.5  # five products against the forward's two

@@ -31,6 +31,12 @@ DEVICE = [
     f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source flags.  The forward kernels are scheduled with LLVM's
+# iterative ILP strategy, which interleaves their exponentials and matrix
+# products better than the default on most instances (B2 H16 S4096 D64 causal
+# 83.6 -> 81.8 us, GQA 20/4 S8192 D128 causal 353 -> 343 us; B8 H32 S2048
+# D128 1% slower), with bit-identical results.
+SOURCE_FLAGS = {"fa_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def hipcc() -> str:
@@ -49,7 +55,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             path = os.path.join(CSRC, src)
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc, *COMMON, *DEVICE, *extra_flags, *lang, "-c", path, "-o", obj]
+            cmd = [cc, *COMMON, *DEVICE, *SOURCE_FLAGS.get(src, []), *extra_flags, *lang, "-c", path, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             res = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
