@@ -59,6 +59,21 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(names) <= exported, set(names) - exported
 
 
+def test_library_imports_no_allocator():
+    """O(N) memory (xnwp.cn post, §2.2; kwkr.cn tutorial, §1.3): the library
+    never materialises S or P, and more than that allocates nothing at all.  It
+    imports no HIP (or C) allocation routine, so no call can hide an N x N
+    buffer behind a pointer the caller never sees."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", binding.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    imported = set(re.findall(r"\bU\s+(\w+)", out))
+    alloc = {n for n in imported
+             if re.match(r"(hip\w*Malloc\w*|hip\w*Alloc\w*|hipMemCreate|hipMemPool\w*|"
+                         r"malloc|calloc|realloc|_Zn[wa]m\w*)$", n)}
+    assert not alloc, alloc
+    assert "hipLaunchKernel" in imported  # the scan itself sees the HIP imports
+
+
 def test_version_and_status_strings():
     assert binding.fa_version().startswith("fa ") and "gfx950" in binding.fa_version()
     for code in range(0, 12):

@@ -1,0 +1,144 @@
+"""Whole-tensor GPU parity at the full workload sizes.
+
+fa_forward runs each full workload in the launch configuration bench.py times
+(one call over the whole problem); every element of O and every LSE value is
+then compared with the fp64 oracle, one (batch, head) at a time to bound host
+memory.  The bars are those of the workloads (max |dO| <= 1e-2, mean |dO| <=
+1e-3 over all of O, max |dLSE| <= 1e-3), evaluated over the whole tensors, as
+the Day 26 post's numeric-alignment check reports max and mean error over the
+whole output (blog.ans20xx.com/posts/ai/day26, "numeric alignment").
+
+The inputs are drawn on the host (``make_inputs`` with the CPU generator), so
+the same seed gives the same values on any machine and the oracle side of
+these cases can be reproduced without a GPU.  With bf16 outputs, rounding O
+alone moves an element by up to half a unit in the last place: 0.0078 for
+|O| in [2, 4), 0.0156 from 4 up.  Each case also reports, as a diagnostic,
+the largest distance in output units of the last place between the GPU's O and
+the oracle's O rounded to the output type.
+"""
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_head_rows
+from tests.parity import LSE_TOL, O_TOL, f64
+from tiled_attention_forward_amd import binding
+from tiled_attention_forward_amd.workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def _ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def whole_tensor_stats(w, seed, dev):
+    """Run fa_forward on the whole workload, compare every output element with
+    the oracle.  Returns the error statistics over all of O and LSE."""
+    t0 = time.time()
+    q, k, v, bias = make_inputs(w, seed=seed, device="cpu")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    bd = None if bias is None else bias.to(dev)
+    o, lse = binding.forward(qd, kd, vd, bd, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o_h, lse_h = o.cpu(), lse.cpu()
+    del qd, kd, vd, bd, o, lse
+    torch.cuda.empty_cache()
+    grp = w.Hq // w.Hkv
+    rows = np.arange(w.Nq)
+    n = 0
+    sum_abs = 0.0
+    max_abs = 0.0
+    lse_max = 0.0
+    max_ulps = 0.0
+    worst = None
+    for b in range(w.B):
+        for h in range(w.Hq):
+            hk = h // grp
+            o_ref, l_ref = attention_head_rows(
+                f64(q[b, h]), f64(k[b, hk]), f64(v[b, hk]), rows=rows, scale=w.scale,
+                causal=w.causal, bias_rows=None if bias is None else f64(bias[b, h]))
+            og = f64(o_h[b, h])
+            assert np.isfinite(og).all(), f"non-finite O in (b={b}, h={h})"
+            d = np.abs(og - o_ref)
+            i = np.unravel_index(int(d.argmax()), d.shape)
+            if d[i] > max_abs:
+                max_abs = float(d[i])
+                worst = (b, h, int(i[0]), int(i[1]), float(o_ref[i]), float(og[i]))
+            sum_abs += float(d.sum())
+            n += d.size
+            lse_max = max(lse_max, float(np.abs(lse_h[b, h].double().numpy() - l_ref).max()))
+            if w.dtype == "bf16":
+                r = torch.from_numpy(o_ref).to(torch.bfloat16).double().numpy()
+                max_ulps = max(max_ulps, float((np.abs(og - r) / _ulp_bf16(o_ref)).max()))
+    return {"max_abs": max_abs, "mean_abs": sum_abs / n, "lse_max": lse_max, "n": n,
+            "worst (b, h, row, col, ref, gpu)": worst, "max_ulps_vs_rounded_oracle": max_ulps,
+            "seconds": round(time.time() - t0, 1)}
+
+
+def _check(st, dtype, what):
+    mx, mean = O_TOL[dtype]
+    assert st["max_abs"] <= mx, f"{what}: max abs {st}"
+    assert st["mean_abs"] <= mean, f"{what}: mean abs {st}"
+    assert st["lse_max"] <= LSE_TOL, f"{what}: LSE {st}"
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_whole_tensor_b2_h16_s4096_d64_causal(gpu_device, seed):
+    """The benchmark report shape, every element, seeds 0-3."""
+    name = "b2_h16_s4096_d64_bf16_causal"
+    _log(f"whole-tensor {name} seed {seed}")
+    st = whole_tensor_stats(WORKLOADS[name], seed, gpu_device)
+    _log(st)
+    _check(st, "bf16", f"{name}/{seed}")
+
+
+def test_whole_tensor_b8_h32_s2048_d128(gpu_device):
+    """The wide-head shape whose S and P would take 4.2 GB, every element."""
+    name = "b8_h32_s2048_d128_bf16"
+    _log(f"whole-tensor {name} seed 0")
+    st = whole_tensor_stats(WORKLOADS[name], 0, gpu_device)
+    _log(st)
+    _check(st, "bf16", name)
+
+
+def test_whole_tensor_gqa_bias_s8192(gpu_device):
+    """GQA 20/4 heads with the dense additive logit tensor, every element."""
+    name = "b1_hq20_hkv4_s8192_d128_bf16_causal_bias"
+    _log(f"whole-tensor {name} seed 0")
+    st = whole_tensor_stats(WORKLOADS[name], 0, gpu_device)
+    _log(st)
+    _check(st, "bf16", name)
+
+
+def test_no_n2_memory_b8_h32_s2048_d128(gpu_device):
+    """S and P of this shape would take 4.29 GB (2.15 GB each: the kwkr.cn
+    tutorial, §1.2, "about 4.2 GB"); the forward keeps them on chip.  With the
+    outputs preallocated, the device's free memory is the same before and
+    after the call, and torch allocated nothing during it."""
+    w = WORKLOADS["b8_h32_s2048_d128_bf16"]
+    q, k, v, _ = make_inputs(w, seed=0, device=gpu_device)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=gpu_device)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(gpu_device)
+    base = torch.cuda.memory_allocated(gpu_device)
+    free0, total = torch.cuda.mem_get_info(gpu_device)
+    binding.forward(q, k, v, None, causal=False, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info(gpu_device)
+    peak = torch.cuda.max_memory_allocated(gpu_device) - base
+    s_and_p = 2 * w.B * w.Hq * w.Nq * w.Nk * 2   # bf16 S and P
+    _log(f"free before {free0}, after {free1}, torch peak growth {peak}, S+P {s_and_p}")
+    assert peak == 0
+    assert abs(free0 - free1) < (16 << 20) < s_and_p
+    assert torch.isfinite(lse).all()

@@ -165,6 +165,10 @@ def _check_inputs(q, k, v, bias):
     for name, t in (("q", q), ("k", k), ("v", v)) + ((("bias", bias),) if bias is not None else ()):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a CUDA tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D, got shape {tuple(t.shape)}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         if t.dtype != q.dtype:
@@ -178,15 +182,58 @@ def _check_inputs(q, k, v, bias):
     return B, Hq, Hkv, Nq, Nk, D
 
 
+def _check_buffer(name, t, shape, dtype, device):
+    """A caller-supplied output or workspace tensor must be exactly what the
+    kernels will write through a raw pointer: the C ABI cannot see a tensor's
+    size, so a wrong shape, dtype, stride or device would send the kernels
+    past the allocation.  Raises ValueError (TypeError for a non-tensor)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, not {type(t).__name__}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(t, need, device):
+    """A caller-supplied workspace: a contiguous tensor on ``device`` of at least
+    ``need`` bytes (the C ABI checks the byte count it is given; this makes
+    sure that count describes memory the tensor really owns)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"workspace must be a torch.Tensor, not {type(t).__name__}")
+    if t.device != device or not t.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"workspace holds {t.numel() * t.element_size()} bytes, "
+                         f"{need} needed")
+
+
+def _out_dtype(q):
+    import torch
+    # FP8 (E4M3) inputs give a bf16 output
+    return torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+
+
 def _outputs(q, out, lse):
+    """Allocate O [B,Hq,Nq,D] and LSE [B,Hq,Nq] float32 on q's device, or check
+    the caller's."""
     import torch
     B, Hq, Nq, _ = q.shape
+    odt = _out_dtype(q)
     if out is None:
-        # FP8 (E4M3) inputs give a bf16 output
-        odt = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
         out = torch.empty(q.shape, dtype=odt, device=q.device)
+    else:
+        _check_buffer("out", out, q.shape, odt, q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    else:
+        _check_buffer("lse", lse, (B, Hq, Nq), torch.float32, q.device)
     return out, lse
 
 
@@ -284,6 +331,8 @@ def forward_split(q, k, v, bias=None, *, causal=False, scale=None, num_splits=No
     need = fa_split_workspace_bytes(B, Hq, Nq, D, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, need, q.device)
     out, lse = _outputs(q, out, lse)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
@@ -315,10 +364,16 @@ def merge(part_o, part_lse, dtype, *, out=None, lse=None, stream=None):
         raise ValueError("part_o must be part_lse's shape plus a trailing D axis")
     P, D = part_o.shape[0], part_o.shape[-1]
     rows = part_lse[0].numel() if P > 0 else math.prod(part_lse.shape[1:])
+    if part_lse.device != part_o.device:
+        raise ValueError("part_o and part_lse must be on one device")
     if out is None:
         out = torch.empty(tuple(part_o.shape[1:]), dtype=dtype, device=part_o.device)
+    else:
+        _check_buffer("out", out, part_o.shape[1:], dtype, part_o.device)
     if lse is None:
         lse = torch.empty(tuple(part_lse.shape[1:]), dtype=torch.float32, device=part_o.device)
+    else:
+        _check_buffer("lse", lse, part_lse.shape[1:], torch.float32, part_o.device)
     if stream is None:
         stream = torch.cuda.current_stream(part_o.device)
     st = lib.fa_merge(part_o.data_ptr() if P > 0 else None,
@@ -342,16 +397,21 @@ def backward(q, k, v, o, lse, dout, bias=None, *, causal=False, scale=None, dq=N
     lib = load_library()
     B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v, bias)
     for name, t in (("o", o), ("dout", dout)):
-        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor like q")
+        _check_buffer(name, t, q.shape, q.dtype, q.device)
+    _check_buffer("lse", lse, (B, Hq, Nq), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is not None:
+            _check_buffer(name, t, like.shape, like.dtype, like.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     need = fa_backward_workspace_bytes(B, Hq, Nq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, need, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(),
