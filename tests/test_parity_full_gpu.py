@@ -14,7 +14,7 @@ these cases can be reproduced without a GPU.  With bf16 outputs, rounding O
 alone moves an element by up to half a unit in the last place: 0.0078 for
 |O| in [2, 4), 0.0156 from 4 up.  Each case also reports, as a diagnostic,
 the largest distance in output units of the last place between the GPU's O and
-the oracle's O rounded to the output type.
+the oracle's O rounded to the output type, over the elements with |O| >= 1.
 """
 
 import time
@@ -77,11 +77,12 @@ def whole_tensor_stats(w, seed, dev):
             sum_abs += float(d.sum())
             n += d.size
             lse_max = max(lse_max, float(np.abs(lse_h[b, h].double().numpy() - l_ref).max()))
-            if w.dtype == "bf16":
-                r = torch.from_numpy(o_ref).to(torch.bfloat16).double().numpy()
-                max_ulps = max(max_ulps, float((np.abs(og - r) / _ulp_bf16(o_ref)).max()))
+            big = np.abs(o_ref) >= 1.0   # where output rounding sets the error
+            if w.dtype == "bf16" and big.any():
+                r = torch.from_numpy(o_ref[big]).to(torch.bfloat16).double().numpy()
+                max_ulps = max(max_ulps, float((np.abs(og[big] - r) / _ulp_bf16(o_ref[big])).max()))
     return {"max_abs": max_abs, "mean_abs": sum_abs / n, "lse_max": lse_max, "n": n,
-            "worst (b, h, row, col, ref, gpu)": worst, "max_ulps_vs_rounded_oracle": max_ulps,
+            "worst (b, h, row, col, ref, gpu)": worst, "max_ulps_vs_rounded_oracle_where_abs_ge_1": max_ulps,
             "seconds": round(time.time() - t0, 1)}
 
 
