@@ -30,8 +30,11 @@
  *    finite value, including 0 and negative values, is accepted.
  *  - A row that sees no key (Nk == 0) gets O = 0 and LSE = -inf.
  *  - B == 0, Hq == 0 or Nq == 0 is an empty problem: nothing is launched.
- *  - The library allocates no memory, keeps no state between calls, never
- *    synchronises and never copies between host and device.  It is reentrant.
+ *  - The library allocates no memory, never synchronises and never copies
+ *    between host and device.  It keeps no state between calls, except for
+ *    the one scratch array per GPU that fa_forward_split_noalloc uses (a
+ *    static device array, not an allocation).  Every other entry point is
+ *    reentrant.
  *  - Errors in the arguments are reported synchronously, as a nonzero status,
  *    before anything is launched.  A launch failure reported by the runtime is
  *    FA_ERR_HIP.  Faults during execution surface at the caller's next
@@ -84,7 +87,9 @@ typedef enum fa_status {
                            /* head's K (Nq*D or Nk*D elements) < 2^31 bytes; with a bias, */
                            /* 128*Nk elements < 2^31 bytes                               */
   FA_ERR_HIP = 10,         /* the HIP runtime rejected the launch                        */
-  FA_ERR_WORKSPACE = 11    /* key-split workspace is NULL, too small or misaligned       */
+  FA_ERR_WORKSPACE = 11,   /* key-split workspace is NULL, too small or misaligned       */
+  FA_ERR_SCRATCH_LIMIT = 12 /* fa_forward_split_noalloc: the partials need more than      */
+                            /* FA_SPLIT_SCRATCH_BYTES                                    */
 } fa_status;
 
 /*
@@ -193,6 +198,36 @@ int fa_forward_split(const void* q, const void* k, const void* v, const void* bi
                      float scale, int causal, int dtype,
                      int64_t num_splits, void* workspace, int64_t workspace_bytes,
                      void* stream);
+
+/*
+ * fa_forward_split for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The caller passes inputs and outputs only; the float32 partials that
+ * fa_forward_split keeps in the caller's workspace go instead to a scratch
+ * array of FA_SPLIT_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on, from the first call on that GPU until the process ends.  Nothing is
+ * allocated, freed or cleared per call (every partial row is written before
+ * the merge reads it).
+ *
+ * Arguments, results and errors are those of fa_forward_split without
+ * workspace / workspace_bytes, plus FA_ERR_SCRATCH_LIMIT when
+ * fa_split_workspace_bytes(B, Hq, Nq, D, num_splits) exceeds
+ * FA_SPLIT_SCRATCH_BYTES (32 MiB: with 16 splits at D = 128, up to 4064
+ * query rows B*Hq*Nq); nothing is launched then.  The work runs on
+ * the current device, so stream must belong to it; FA_ERR_HIP if the
+ * runtime cannot give the scratch array's address there.
+ *
+ * All calls on one GPU share its scratch array: two calls whose work can
+ * overlap on that GPU (different streams without ordering between them, or
+ * different host threads) race on it and may return wrong results.  Calls
+ * ordered on one stream are safe.
+ */
+#define FA_SPLIT_SCRATCH_BYTES ((int64_t)32 << 20)
+int fa_forward_split_noalloc(const void* q, const void* k, const void* v, const void* bias,
+                             void* o, float* lse,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                             int64_t D, float scale, int causal, int dtype, int64_t num_splits,
+                             void* stream);
 
 /*
  * Workspace size of fa_forward_split, in bytes, through *bytes:

@@ -46,7 +46,8 @@ def forward_status(**over):
 def test_library_loads_and_exports_every_declared_symbol():
     lib = binding.load_library()
     names = declared_functions()
-    assert set(names) == {"fa_check_args", "fa_forward", "fa_forward_split", "fa_merge",
+    assert set(names) == {"fa_check_args", "fa_forward", "fa_forward_split",
+                          "fa_forward_split_noalloc", "fa_merge",
                           "fa_split_count", "fa_split_workspace_bytes", "fa_backward",
                           "fa_backward_workspace_bytes", "fa_forward_window",
                           "fa_backward_window", "fa_forward_chain", "fa_status_string",
@@ -76,7 +77,7 @@ def test_library_imports_no_allocator():
 
 def test_version_and_status_strings():
     assert binding.fa_version().startswith("fa ") and "gfx950" in binding.fa_version()
-    for code in range(0, 12):
+    for code in range(0, 13):
         s = binding.fa_status_string(code)
         assert s and s != "unknown status", code
     assert binding.fa_status_string(99) == "unknown status"
@@ -218,6 +219,34 @@ def test_split_rejections_before_launch():
     assert split_status(Hq=64, Hkv=1, Nq=1 << 18, B=1, workspace_bytes=1 << 62) == 9
     # empty problem: nothing launched, no workspace needed
     assert split_status(B=0, workspace=None, workspace_bytes=0) == 0
+
+
+def noalloc_status(num_splits=4, **over):
+    a = dict(OK_ARGS, **over)
+    return binding.fa_forward_split_noalloc(a["q"], a["k"], a["v"], a["bias"], a["o"], a["lse"],
+                                            a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"],
+                                            a["scale"], a["causal"], a["dtype"], num_splits, None)
+
+
+def test_split_noalloc_rejections_before_launch():
+    """The allocation-free key split checks what fa_forward_split checks (except
+    the workspace), and refuses partials larger than its scratch array before
+    touching the GPU."""
+    assert noalloc_status(num_splits=0) == 2 and noalloc_status(num_splits=1025) == 2
+    assert noalloc_status(D=72) == 4 and noalloc_status(D=256) == 4
+    assert noalloc_status(q=None) == 1 and noalloc_status(o=O + 8) == 7
+    assert noalloc_status(o=Q) == 8
+    assert noalloc_status(dtype=binding.FA_DTYPE_FP8_E4M3) == 5
+    # just over the limit: rows * D * 4 * splits (plus the LSE part) > 32 MiB
+    limit = binding.FA_SPLIT_SCRATCH_BYTES
+    rows = 2 * 4 * 100
+    over = limit // (rows * 64 * 4) + 1
+    assert binding.fa_split_workspace_bytes(2, 4, 100, 64, over) > limit
+    assert noalloc_status(num_splits=over) == binding.FA_ERR_SCRATCH_LIMIT
+    assert noalloc_status(B=64, Hq=32, Hkv=32, Nq=4096, num_splits=1) == 12
+    assert "scratch" in binding.fa_status_string(12)
+    # empty problem: nothing launched
+    assert noalloc_status(B=0, q=None, o=None, lse=None) == 0
 
 
 def merge_status(part_o=WS, part_lse=WS + (1 << 30), num_parts=3, rows=10, D=64, o=O, lse=L,

@@ -1,15 +1,17 @@
 """ctypes binding of libfa.so (argument marshalling only).
 
-``fa_forward``, ``fa_forward_split``, ``fa_merge``, ``fa_backward``,
-``fa_split_count``, ``fa_split_workspace_bytes``, ``fa_backward_workspace_bytes``,
-``fa_check_args``, ``fa_status_string`` and ``fa_version`` take the same
-arguments as the C functions of ``include/fa.h`` (device pointers as Python
-ints; the size queries return their value).  ``forward``, ``forward_split``,
-``merge`` and ``backward`` are the tensor-level conveniences: they check the torch tensors, allocate outputs (and the
-key-split workspace) with torch, and call the library on the current stream.
-Every step of the attention runs in the library's kernels; if the library is
-missing or does not load, the call raises instead of computing anything some
-other way.
+``fa_forward``, ``fa_forward_split``, ``fa_forward_split_noalloc``, ``fa_merge``,
+``fa_backward``, ``fa_split_count``, ``fa_split_workspace_bytes``,
+``fa_backward_workspace_bytes``, ``fa_check_args``, ``fa_status_string`` and
+``fa_version`` take the same arguments as the C functions of
+``include/fa.h`` (device pointers as Python ints; the size queries return
+their value).  ``forward``, ``forward_split``, ``forward_split_noalloc``,
+``forward_chain``, ``merge`` and ``backward`` are the tensor-level
+conveniences: they check the torch tensors, allocate outputs (and the
+key-split workspace) with torch unless given, and call the library on the
+current stream.  Every step of the attention runs in the library's kernels;
+if the library is missing or does not load, the call raises instead of
+computing anything some other way.
 """
 
 from __future__ import annotations
@@ -26,7 +28,11 @@ STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_BAD_SIZE", 3: "FA_ERR_HEAD_GROUPS",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_DTYPE", 6: "FA_ERR_SCALE", 7: "FA_ERR_ALIGNMENT",
     8: "FA_ERR_OVERLAP", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP", 11: "FA_ERR_WORKSPACE",
+    12: "FA_ERR_SCRATCH_LIMIT",
 }
+FA_ERR_SCRATCH_LIMIT = 12
+# bytes of the library's per-GPU scratch array (fa_forward_split_noalloc)
+FA_SPLIT_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -67,6 +73,9 @@ def load_library():
     lib.fa_forward_split.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32, i32,
                                      i32, i64, p, i64, p]
     lib.fa_forward_split.restype = i32
+    lib.fa_forward_split_noalloc.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32,
+                                             i32, i32, i64, p]
+    lib.fa_forward_split_noalloc.restype = i32
     lib.fa_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(i64)]
     lib.fa_split_workspace_bytes.restype = i32
     lib.fa_split_count.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]
@@ -103,6 +112,13 @@ def fa_forward_split(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal
                                            float(scale), int(causal), int(dtype),
                                            int(num_splits), workspace, int(workspace_bytes),
                                            stream)
+
+
+def fa_forward_split_noalloc(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype,
+                             num_splits, stream) -> int:
+    return load_library().fa_forward_split_noalloc(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D,
+                                                   float(scale), int(causal), int(dtype),
+                                                   int(num_splits), stream)
 
 
 def fa_merge(part_o, part_lse, num_parts, rows, D, o, lse, dtype, stream) -> int:
@@ -342,6 +358,32 @@ def forward_split(q, k, v, bias=None, *, causal=False, scale=None, num_splits=No
                               float(scale), int(bool(causal)), _dtype_code(q), int(num_splits),
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                               stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+    return out, lse
+
+
+def forward_split_noalloc(q, k, v, bias=None, *, causal=False, scale=None, num_splits=None,
+                          out=None, lse=None, stream=None):
+    """``forward_split`` through fa_forward_split_noalloc: the partials go to
+    the library's per-GPU scratch array instead of a workspace, so with ``out``
+    and ``lse`` given nothing is allocated.  Calls that can overlap on one GPU
+    race on that array."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, Nq, Nk, D = _check_inputs(q, k, v, bias)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if num_splits is None:
+        num_splits = fa_split_count(B, Hq, Hkv, Nq, Nk, D)
+    out, lse = _outputs(q, out, lse)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = lib.fa_forward_split_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      bias.data_ptr() if bias is not None else None,
+                                      out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk, D,
+                                      float(scale), int(bool(causal)), _dtype_code(q),
+                                      int(num_splits), stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, fa_status_string(st))
     return out, lse

@@ -224,23 +224,61 @@ extern "C" int fa_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, in
   return FA_OK;
 }
 
+namespace {
+
+// Checks shared by the two key-split entry points (everything except the
+// partials' storage), and the launch arguments.  *need receives the bytes of
+// the partials.
+int split_common(const void* q, const void* k, const void* v, const void* bias, void* o,
+                 float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                 int64_t D, float scale, int causal, int dtype, int64_t num_splits,
+                 void* stream, fa::LaunchArgs* a, int64_t* need) {
+  if (dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_DTYPE;  // fused FP8 forward only
+  if (D == 256) return FA_ERR_HEAD_DIM;                 // fused forward only
+  int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  *need = 0;
+  if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
+  st = check_split_sizes(B, Hq, Hkv, Nq, D, elem_bytes(dtype), num_splits);
+  if (st != FA_OK) return st;
+  *need = fa::split_workspace_bytes(B * Hq * Nq, D, num_splits);
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->bias = bias;
+  a->o = o;
+  a->lse = lse;
+  a->B = int(B);
+  a->Hq = int(Hq);
+  a->Hkv = int(Hkv);
+  a->Nq = int(Nq);
+  a->Nk = int(Nk);
+  a->D = int(D);
+  a->scale = scale;
+  a->causal = causal != 0;
+  a->window = 0;
+  a->dtype = dtype;
+  a->stream = stream;
+  return FA_OK;
+}
+
+}  // namespace
+
 extern "C" int fa_forward_split(const void* q, const void* k, const void* v, const void* bias,
                                 void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
                                 int64_t Nq, int64_t Nk, int64_t D, float scale, int causal,
                                 int dtype, int64_t num_splits, void* workspace,
                                 int64_t workspace_bytes, void* stream) {
-  if (dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_DTYPE;  // fused FP8 forward only
-  if (D == 256) return FA_ERR_HEAD_DIM;                 // fused forward only
-  int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
+  fa::LaunchArgs a;
+  int64_t need = 0;
+  const int st = split_common(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype,
+                              num_splits, stream, &a, &need);
   if (st != FA_OK) return st;
   if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
-  const int esz = elem_bytes(dtype);
-  st = check_split_sizes(B, Hq, Hkv, Nq, D, esz, num_splits);
-  if (st != FA_OK) return st;
-  const int64_t rows = B * Hq * Nq;
-  const int64_t need = fa::split_workspace_bytes(rows, D, num_splits);
   if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)
     return FA_ERR_WORKSPACE;
+  const int esz = elem_bytes(dtype);
+  const int64_t rows = B * Hq * Nq;
   const uint64_t nq_b = uint64_t(rows) * D * esz;
   const uint64_t nkv_b = uint64_t(B) * Hkv * Nk * D * esz;
   const uint64_t nb_b = bias ? uint64_t(rows) * Nk * esz : 0;
@@ -249,25 +287,22 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, con
       overlap(workspace, need, v, nkv_b) || overlap(workspace, need, bias, nb_b) ||
       overlap(workspace, need, o, nq_b) || overlap(workspace, need, lse, nl_b))
     return FA_ERR_OVERLAP;
-  fa::LaunchArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.bias = bias;
-  a.o = o;
-  a.lse = lse;
-  a.B = int(B);
-  a.Hq = int(Hq);
-  a.Hkv = int(Hkv);
-  a.Nq = int(Nq);
-  a.Nk = int(Nk);
-  a.D = int(D);
-  a.scale = scale;
-  a.causal = causal != 0;
-  a.window = 0;
-  a.dtype = dtype;
-  a.stream = stream;
   return fa::launch_forward_split(a, int(num_splits), workspace);
+}
+
+extern "C" int fa_forward_split_noalloc(const void* q, const void* k, const void* v,
+                                        const void* bias, void* o, float* lse, int64_t B,
+                                        int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                        int64_t D, float scale, int causal, int dtype,
+                                        int64_t num_splits, void* stream) {
+  fa::LaunchArgs a;
+  int64_t need = 0;
+  const int st = split_common(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype,
+                              num_splits, stream, &a, &need);
+  if (st != FA_OK) return st;
+  if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
+  if (need > FA_SPLIT_SCRATCH_BYTES) return FA_ERR_SCRATCH_LIMIT;
+  return fa::launch_forward_split_noalloc(a, int(num_splits));
 }
 
 extern "C" int fa_merge(const float* part_o, const float* part_lse, int64_t num_parts,
@@ -416,6 +451,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_TOO_LARGE: return "a size exceeds the kernel's index range";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     case FA_ERR_WORKSPACE: return "the key-split workspace is NULL, too small or misaligned";
+    case FA_ERR_SCRATCH_LIMIT:
+      return "the key-split partials exceed the library's scratch array (FA_SPLIT_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

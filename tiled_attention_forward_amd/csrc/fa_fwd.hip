@@ -41,6 +41,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/fa.h"
@@ -1322,6 +1323,47 @@ int launch_forward_chain(const LaunchArgs& a, const void* const* q_layers,
                            ? launch_chain_t<__bf16>(p, grid, s, a.D, a.causal, n_layers)
                            : launch_chain_t<_Float16>(p, grid, s, a.D, a.causal, n_layers);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free key split: the partials live in a static device array of
+// FA_SPLIT_SCRATCH_BYTES (each GPU the library runs on holds its own copy for
+// the life of the process).  On the host the array's name is only a stand-in
+// for its device address, so the address is taken once per device with
+// hipGetSymbolAddress, with that device current, and the kernels receive it
+// as their workspace pointer.
+// ---------------------------------------------------------------------------
+}  // namespace fa
+
+static __device__ __attribute__((aligned(256))) unsigned char scratch[FA_SPLIT_SCRATCH_BYTES];
+
+namespace fa {
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device); nullptr if the runtime cannot give it.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+int launch_forward_split_noalloc(const LaunchArgs& a, int n_splits) {
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return FA_ERR_HIP;
+  return launch_forward_split(a, n_splits, ws);
 }
 
 int launch_merge(const float* part_o, const float* part_lse, int n_parts, int64_t rows, int D,

@@ -28,6 +28,11 @@ int launch_forward(const LaunchArgs& a);
 // into a.o / a.lse, both on a.stream.  Arguments are already validated.
 int launch_forward_split(const LaunchArgs& a, int n_splits, void* workspace);
 
+// The same, with the partials in the library's per-device scratch array
+// (FA_SPLIT_SCRATCH_BYTES); the caller has checked that they fit.  Returns
+// FA_OK or FA_ERR_HIP.
+int launch_forward_split_noalloc(const LaunchArgs& a, int n_splits);
+
 // Merge of n_parts normalised partials: part_o [n_parts][rows][D] fp32,
 // part_lse [n_parts][rows] -> o [rows][D] (dtype), lse [rows].  Validated.
 int launch_merge(const float* part_o, const float* part_lse, int n_parts, int64_t rows, int D,
