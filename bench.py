@@ -22,7 +22,13 @@ roofline  = the step's own rate against the chip's peak: useful flops
             is above the chip's ridge point (peak flops / peak HBM bandwidth),
             else algorithmic bytes (Q, K, V, visible bias, O, LSE) / step time;
 cpu_baseline = the fp64 oracle, timed on the host on a bounded sample of the
-            same workload (whole heads), scaled to the same metric.
+            same workload (whole heads), scaled to the same metric;
+            cpu_baseline_1thread the same with one BLAS thread, on a smaller
+            sample;
+error_vs_oracle = max / mean |O_gpu - O_oracle| and max |LSE_gpu - LSE_oracle|
+            over the heads the oracle ran, from this run's own output;
+env       = GPU, runtime, torch and library versions; peak_mem_gb the peak
+            device memory allocated (inputs, outputs, workspace).
 """
 
 from __future__ import annotations
@@ -145,8 +151,9 @@ def cpu_baseline_backward(w, q, k, v, dout, target_s: float):
                       f"fp64 NumPy, {t_used:.1f} s"}
 
 
-def cpu_baseline_chain(w, q_layers, k_layers, v, target_s: float):
-    """Time the oracle's chain on whole heads until about target_s."""
+def cpu_baseline_chain(w, q_layers, k_layers, v, target_s: float, o_gpu=None, lse_gpu=None):
+    """Time the oracle's chain on whole heads until about target_s (and the
+    error of the GPU output on those heads)."""
     import numpy as np
 
     from oracle import attention_chain_head_rows
@@ -155,6 +162,7 @@ def cpu_baseline_chain(w, q_layers, k_layers, v, target_s: float):
     rows = np.arange(w.Nq)
     f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     done, t_used = 0, 0.0
+    acc = _err_acc()
     for b in range(w.B):
         for h in range(w.Hq):
             hk = h // grp
@@ -162,30 +170,67 @@ def cpu_baseline_chain(w, q_layers, k_layers, v, target_s: float):
             ks = [f(t[b, hk]) for t in k_layers]
             vh = f(v[b, hk])
             t0 = time.perf_counter()
-            attention_chain_head_rows(qs, ks, vh, rows=rows, scale=w.scale, causal=w.causal)
+            o_ref, lse_ref = attention_chain_head_rows(qs, ks, vh, rows=rows, scale=w.scale,
+                                                       causal=w.causal)
             t_used += time.perf_counter() - t0
             done += 1
+            if o_gpu is not None:
+                _err_add(acc, o_gpu[b, h], lse_gpu[b, h], o_ref, lse_ref)
             if t_used >= target_s:
                 break
         if t_used >= target_s:
             break
     per_head = w.useful_flops() / (w.B * w.Hq)
-    return {"value": round(per_head * done / t_used / 1e12, 6), "unit": "TFLOPS",
+    base = {"value": round(per_head * done / t_used / 1e12, 6), "unit": "TFLOPS",
             "cores": blas_threads(), "kind": "oracle",
             "sample": f"{done} of {w.B * w.Hq} (batch, head) slices of {w.name}, fp64 NumPy, "
                       f"{t_used:.1f} s"}
+    return base, _err_report(acc, w, f"{done} of {w.B * w.Hq} whole (batch, head) slices")
 
 
-def cpu_baseline(w, q, k, v, bias, target_s: float):
-    """Time the oracle on whole heads of the same workload until about target_s."""
+def _err_acc():
+    return {"max_abs": 0.0, "sum_abs": 0.0, "n": 0, "lse_max": 0.0}
+
+
+def _err_add(acc, o_gpu, lse_gpu, o_ref, lse_ref):
     import numpy as np
-    import torch
+    d = np.abs(o_gpu.float().cpu().numpy().astype(np.float64) - o_ref)
+    acc["max_abs"] = max(acc["max_abs"], float(d.max(initial=0.0)))
+    acc["sum_abs"] += float(d.sum())
+    acc["n"] += d.size
+    dl = np.abs(lse_gpu.cpu().numpy().astype(np.float64) - lse_ref)
+    acc["lse_max"] = max(acc["lse_max"], float(dl.max(initial=0.0)))
+
+
+# Bars of the workloads (against the fp64 oracle): bf16/fp16 max |dO| <= 1e-2,
+# mean <= 1e-3; fp32 max <= 1e-5; LSE <= 1e-3.  FP8 inputs are held to a
+# derived rounding bound in the tests, not to a fixed bar.
+_BARS = {"bf16": (1e-2, 1e-3), "fp16": (1e-2, 1e-3), "fp32": (1e-5, 1e-5)}
+
+
+def _err_report(acc, w, what):
+    if acc["n"] == 0:
+        return None
+    rep = {"max_abs": acc["max_abs"], "mean_abs": acc["sum_abs"] / acc["n"],
+           "lse_max": acc["lse_max"], "elements": acc["n"], "compared": what}
+    bars = _BARS.get(w.dtype)
+    if bars is not None:
+        rep["within_bars"] = bool(acc["max_abs"] <= bars[0] and rep["mean_abs"] <= bars[1]
+                                  and acc["lse_max"] <= 1e-3)
+    return rep
+
+
+def cpu_baseline(w, q, k, v, bias, target_s: float, o_gpu=None, lse_gpu=None):
+    """Time the oracle on whole heads of the same workload until about target_s;
+    the same oracle results give the error of the GPU output on those heads."""
+    import numpy as np
 
     from oracle import attention_head_rows
 
     grp = w.Hq // w.Hkv
     rows = np.arange(w.Nq)
     done, t_used = 0, 0.0
+    acc = _err_acc()
     heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
     for b, h in heads:
         hk = h // grp
@@ -194,17 +239,43 @@ def cpu_baseline(w, q, k, v, bias, target_s: float):
         vh = v[b, hk].cpu().float().numpy().astype(np.float64)
         bh = None if bias is None else bias[b, h].cpu().float().numpy().astype(np.float64)
         t0 = time.perf_counter()
-        attention_head_rows(qh, kh, vh, rows=rows, scale=w.scale, causal=w.causal, bias_rows=bh,
-                            window=w.window or None)
+        o_ref, lse_ref = attention_head_rows(qh, kh, vh, rows=rows, scale=w.scale,
+                                             causal=w.causal, bias_rows=bh,
+                                             window=w.window or None)
         t_used += time.perf_counter() - t0
         done += 1
+        if o_gpu is not None:
+            _err_add(acc, o_gpu[b, h], lse_gpu[b, h], o_ref, lse_ref)
         if t_used >= target_s:
             break
     per_head_flops = (w.useful_flops() if w.window else w.metric_flops()) / (w.B * w.Hq)
-    return {"value": round(per_head_flops * done / t_used / 1e12, 6), "unit": "TFLOPS",
+    base = {"value": round(per_head_flops * done / t_used / 1e12, 6), "unit": "TFLOPS",
             "cores": blas_threads(), "kind": "oracle",
             "sample": f"{done} of {w.B * w.Hq} (batch, head) slices of {w.name}, fp64 NumPy, "
                       f"{t_used:.1f} s"}
+    return base, _err_report(acc, w, f"{done} of {w.B * w.Hq} whole (batch, head) slices")
+
+
+def cpu_baseline_one_thread(w, q, k, v, bias, target_s: float):
+    """The same oracle with its BLAS held to one thread, on whole heads until
+    about target_s (a smaller sample than the threaded run)."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        base, _ = cpu_baseline(w, q, k, v, bias, target_s)
+    base["cores"] = 1
+    return base
+
+
+def environment(lib_version: str):
+    """What the numbers were measured on (the Day 26 post's report header)."""
+    import platform
+
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hip_runtime": torch.version.hip,
+            "torch": torch.__version__, "library": lib_version,
+            "host_cpus": os.cpu_count(), "python": platform.python_version()}
 
 
 def main():
@@ -297,6 +368,13 @@ def main():
         if st != 0:
             raise binding.FaError(st, binding.fa_status_string(st))
 
+    # peak device memory of the run (the Day 26 report's peak-memory column):
+    # inputs, outputs and any workspace are allocated by now, so the steps
+    # themselves should add nothing
+    torch.cuda.synchronize()
+    mem_base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -316,6 +394,7 @@ def main():
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(K))
     ms_per_step = total_ms / K
     launch_ms = statistics.fmean(per)
+    mem_peak = torch.cuda.max_memory_allocated(dev)
     assert torch.isfinite(lse).all(), "non-finite LSE in the benchmark output"
 
     fl = BACKWARD_FLOP_FACTOR if backward else 1.0
@@ -366,19 +445,35 @@ def main():
                    "path": w.path, "splits": splits, "pass": args.pass_,
                    "window": w.window or None, "layers": w.layers or None,
                    "parallelism": "single GPU"},
-        "pct_of_bf16_peak": round(100.0 * value / metrics.MFMA_PEAK_TFLOPS["bf16"], 2),
+        # value / bf16 dense peak: the metric's own formula counts every
+        # (query, key) pair, so for causal workloads this is twice the share
+        # of the matrix cores' peak that the visible pairs use
+        "pct_of_bf16_peak_dense_formula": round(100.0 * value / metrics.MFMA_PEAK_TFLOPS["bf16"],
+                                                2),
         "useful_tflops": round(fl * w.useful_flops() / (ms_per_step / 1e3) / 1e12, 2),
+        # useful flops (visible pairs only) per step time / the dtype's peak
+        "pct_of_peak_useful": round(100.0 * fl * w.useful_flops() / (ms_per_step / 1e3) / 1e12
+                                    / peak, 2),
+        "peak_mem_gb": round(mem_peak / 1e9, 4),
+        "alloc_in_timed_steps_bytes": int(mem_peak - mem_base),
         "launch_ms": {"mean": round(launch_ms, 5), "median": round(statistics.median(per), 5),
                       "p90": round(per[int(len(per) * 0.9)], 5), "min": round(per[0], 5)},
         "roofline": roof,
     }
+    out["env"] = environment(binding.fa_version())
     if not args.no_cpu_baseline:
+        # the oracle on the host; for the forward its results on the heads it
+        # ran also give the error of this run's GPU output there
         if backward:
             out["cpu_baseline"] = cpu_baseline_backward(w, q, k, v, dout, args.cpu_seconds)
         elif w.layers:
-            out["cpu_baseline"] = cpu_baseline_chain(w, q_layers, k_layers, v, args.cpu_seconds)
+            out["cpu_baseline"], out["error_vs_oracle"] = cpu_baseline_chain(
+                w, q_layers, k_layers, v, args.cpu_seconds, o, lse)
         else:
-            out["cpu_baseline"] = cpu_baseline(w, q, k, v, bias, args.cpu_seconds)
+            out["cpu_baseline"], out["error_vs_oracle"] = cpu_baseline(
+                w, q, k, v, bias, args.cpu_seconds, o, lse)
+            out["cpu_baseline_1thread"] = cpu_baseline_one_thread(
+                w, q, k, v, bias, args.cpu_seconds / 4)
     print(json.dumps(out), flush=True)
 
 

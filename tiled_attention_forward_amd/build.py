@@ -10,6 +10,7 @@ switched off for all device code.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -65,6 +66,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
                 raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
             if verbose and res.stderr:
                 print(res.stderr, flush=True)
+            if src.endswith(".hip"):
+                check_device_code(obj, tmp)
             objs.append(obj)
         tmp_lib = LIB + ".tmp"
         cmd = [cc, *DEVICE, "-shared", "-fPIC", *objs, "-o", tmp_lib]
@@ -74,6 +77,125 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         check_no_undefined_kernels(tmp_lib)
         os.replace(tmp_lib, LIB)
     return LIB
+
+
+LLVM_BIN = "/opt/rocm/llvm/bin"
+DEVICE_TARGET = f"hipv4-amdgcn-amd-amdhsa--{ARCH}"
+
+
+def device_code(obj: str, tmp: str):
+    """Disassembly and kernel metadata of the gfx950 code object inside a hipcc
+    object file (our own build; AMD assembly only)."""
+    tools = {t: os.path.join(LLVM_BIN, t) for t in
+             ("llvm-objcopy", "clang-offload-bundler", "llvm-objdump", "llvm-readobj")}
+    missing = [t for t, path in tools.items() if not os.path.exists(path)]
+    if missing:
+        raise RuntimeError(f"cannot check the device code: {missing} not found in {LLVM_BIN}")
+    base = os.path.join(tmp, os.path.basename(obj))
+    fat, co = base + ".fatbin", base + ".co"
+    subprocess.run([tools["llvm-objcopy"], f"--dump-section=.hip_fatbin={fat}", obj],
+                   check=True)
+    subprocess.run([tools["clang-offload-bundler"], "--unbundle", "--type=o",
+                    f"--targets={DEVICE_TARGET}", f"--input={fat}", f"--output={co}"],
+                   check=True)
+    listing = subprocess.run([tools["llvm-objdump"], "-d", co], check=True, capture_output=True,
+                             text=True).stdout
+    notes = subprocess.run([tools["llvm-readobj"], "--notes", co], check=True,
+                           capture_output=True, text=True).stdout
+    return listing, notes
+
+
+# Instructions that read M0 without naming it: direct-to-LDS loads, message
+# sends, relative register moves, GWS and append/consume LDS operations,
+# interpolation.
+_M0_IMPLICIT = re.compile(r"^(buffer_load_\w+.*\blds\b|global_load_lds_\w+|s_sendmsg\w*|"
+                          r"[sv]_movrel\w*|ds_gws\w*|ds_append|ds_consume|ds_\w*addtid\w*|"
+                          r"v_interp\w*)")
+_BRANCH = re.compile(r"^(s_branch|s_cbranch_\w+|s_setpc_b64|s_swappc_b64|s_endpgm)\b")
+_LINE = re.compile(r"^\s+(\S+)\s*([^/]*?)\s*//\s*([0-9A-Fa-f]+):")
+_FUNC = re.compile(r"^[0-9A-Fa-f]+ <([^>]+)>:")
+
+
+def m0_discipline_problems(listing: str, window: int = 16):
+    """Check that no value lives in M0 across another instruction that touches it.
+
+    The forward's bias instances issue their direct-to-LDS loads from inline
+    assembly that writes M0 without the compiler saving it first; that is safe
+    only if the compiler never keeps a value in M0 across such a statement.
+    Rule checked, per kernel: M0 is never read by name, and every instruction
+    that reads it implicitly has, as the nearest earlier instruction touching M0
+    in its basic block (no branch or branch target in between, at most
+    ``window`` instructions back), a write of M0.  Returns a list of problems."""
+    problems = []
+    funcs = []
+    for line in listing.splitlines():
+        m = _FUNC.match(line)
+        if m:
+            funcs.append((m.group(1), []))
+            continue
+        m = _LINE.match(line)
+        if m and funcs:
+            ops = [o.strip() for o in m.group(2).split(",")] if m.group(2) else []
+            funcs[-1][1].append((m.group(1), ops, int(m.group(3), 16)))
+    for name, ins in funcs:
+        targets = set()
+        for mn, ops, addr in ins:
+            if mn.startswith(("s_branch", "s_cbranch_")) and ops:
+                try:
+                    targets.add(addr + 4 + 4 * int(ops[0], 0))
+                except ValueError:
+                    pass
+        for i, (mn, ops, addr) in enumerate(ins):
+            full = mn + (" " + " ".join(ops) if ops else "")
+            if any(o == "m0" or o.startswith("m0 ") for o in ops[1:]) or \
+                    (ops and ops[0] == "m0" and not mn.startswith("s_")):
+                problems.append(f"{name}+{addr:#x}: M0 read by name: {full}")
+            if not _M0_IMPLICIT.match(full):
+                continue
+            ok = False
+            for j in range(i - 1, max(i - 1 - window, -1), -1):
+                pmn, pops, paddr = ins[j]
+                if _BRANCH.match(pmn) or ins[j + 1][2] in targets:
+                    break
+                pfull = pmn + " " + " ".join(pops)
+                if pops and pops[0] == "m0" and pmn.startswith("s_"):
+                    ok = True
+                    break
+                if _M0_IMPLICIT.match(pfull):
+                    break
+            if not ok:
+                problems.append(f"{name}+{addr:#x}: M0 reader without its own write: {full}")
+    return problems
+
+
+# fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, ...>: 16-bit types with BIAS
+# (these issue the K/V loads from inline assembly)
+_ASM_INSTANCE = re.compile(r"fa_fwd_kernelI(DF16b|DF16_)Li\d+ELi\d+ELi\d+ELb[01]ELb1E")
+
+
+def asm_instance_scratch_problems(notes: str):
+    """The instances that issue loads from inline assembly must not spill: a
+    spill or scratch reload next to an M0-writing asm statement is where the
+    compiler would be most tempted to keep values in M0.  Returns problems."""
+    problems = []
+    name = None
+    for line in notes.splitlines():
+        line = line.strip()
+        if line.startswith(".name:"):
+            name = line.split(":", 1)[1].strip()
+        elif line.startswith(".private_segment_fixed_size:") and name:
+            size = int(line.split(":", 1)[1])
+            if size and _ASM_INSTANCE.search(name):
+                problems.append(f"{name}: {size} bytes of scratch")
+    return problems
+
+
+def check_device_code(obj: str, tmp: str) -> None:
+    listing, notes = device_code(obj, tmp)
+    problems = m0_discipline_problems(listing) + asm_instance_scratch_problems(notes)
+    if problems:
+        raise RuntimeError(f"device code of {os.path.basename(obj)} breaks the M0 / scratch "
+                           "rules:\n  " + "\n  ".join(problems[:20]))
 
 
 def check_no_undefined_kernels(path: str) -> None:
