@@ -47,11 +47,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfa.so)")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source and link libfa.so; returns its path.  Always rebuilds."""
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Compile every source and link libfa.so (or ``out``); returns its path.
+    Always rebuilds.  The three sources compile in parallel."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
-        objs = []
+        objs, procs = [], []
         for src in SOURCES:
             path = os.path.join(CSRC, src)
             obj = os.path.join(tmp, src + ".o")
@@ -59,24 +60,26 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             cmd = [cc, *COMMON, *DEVICE, *SOURCE_FLAGS.get(src, []), *extra_flags, *lang, "-c", path, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
-            res = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
-            if res.returncode != 0:
-                errs = "\n".join(l for l in res.stderr.splitlines()
+            procs.append((src, obj, subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True)))
+        for src, obj, proc in procs:
+            _, err = proc.communicate()
+            if proc.returncode != 0:
+                errs = "\n".join(l for l in err.splitlines()
                                  if "packed-fp32-ops' is not a recognized" not in l)
                 raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
-            if verbose and res.stderr:
-                print(res.stderr, flush=True)
+            if verbose and err:
+                print(err, flush=True)
             if src.endswith(".hip"):
                 check_device_code(obj, tmp)
             objs.append(obj)
-        tmp_lib = LIB + ".tmp"
+        tmp_lib = out + ".tmp"
         cmd = [cc, *DEVICE, "-shared", "-fPIC", *objs, "-o", tmp_lib]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         check_no_undefined_kernels(tmp_lib)
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, out)
+    return out
 
 
 LLVM_BIN = "/opt/rocm/llvm/bin"

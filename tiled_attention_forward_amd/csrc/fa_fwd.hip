@@ -85,6 +85,14 @@ constexpr int kPolicyNT = 2;  // buffer-load cache policy: non-temporal
 #ifndef FA_SPLIT_BN128
 #define FA_SPLIT_BN128 32
 #endif
+// Key halves per workgroup of the causal D = 64 fused instances (1 or 2)
+#ifndef FA_KH64
+#define FA_KH64 1
+#endif
+#ifndef FA_KH64_F8
+#define FA_KH64_F8 2
+#endif
+
 constexpr int kBN64 = FA_BN64;         // keys per K/V tile, D = 64
 constexpr int kBN128 = FA_BN128;       // keys per K/V tile, D = 128
 constexpr int kQB64 = FA_QB64;         // 32-row query blocks per wave, D = 64
@@ -159,12 +167,20 @@ __device__ __forceinline__ void dma16_asm(__amdgpu_buffer_rsrc_t rs, lds_void* d
 // NL > 1 (Block Attention Residual chain): the logits are the sum over NL
 // layers of Q_l K_l^T * scale, the K tiles of all layers sharing one LDS
 // buffer with the V tile; 16-bit types, no bias, no key split, no window.
+// KH = 2 (two key halves): 8 waves; waves w and w + 4 own the same 32 rows,
+// the first four stream the first half of the row block's key tiles through
+// their own pair of LDS buffers and the last four the second half; at the end
+// the second half hands its (max, sum, output) state to the first through
+// LDS, which merges the two with the online-softmax merge and writes O and
+// LSE.  Halving the longest workgroup's loop lets the grid run in two rounds
+// with the heaviest row blocks first (for causal grids the per-block work
+// ranges from 1 to Nk/64 tiles).  16-bit and FP8 fused instances only.
 template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT, bool WINDOW,
-          int NL, int KVPOL>
+          int NL, int KVPOL, int KH>
 // (waves per SIMD asked of the compiler: fp32 at D = 128 with 64-key tiles
 // holds 137 KB of LDS, so one workgroup per compute unit, and the D = 256
 // bias instances keep their accumulators in AGPRs at one)
-__global__ __launch_bounds__(kThreads,
+__global__ __launch_bounds__(kThreads * KH,
                              (D == 64                                                  ? FA_MINB64
                               : (D == 256 && BIAS)                                     ? 1
                               : (std::is_same<T, float>::value && D == 128 && BN == 64) ? 1
@@ -216,6 +232,7 @@ void fa_fwd_kernel(Params p) {
   static_assert(NL >= 1 && NL <= kMaxChainLayers, "chain length");
   static_assert(NL == 1 || (VTR && !BIAS && !SPLIT && !WINDOW), "chain instances");
   static_assert(!F8 || (NL == 1 && !BIAS && !SPLIT && !WINDOW && D == DL), "FP8 instances");
+  static_assert(KH == 1 || (KH == 2 && VTR && NL == 1 && !SPLIT && !BIAS), "key-half instances");
   // FP8: P is stored as e4m3 for the P.V product.  It is taken as
   // 2^(t - m_ref + 7) with the rescale threshold at 1, so every p lies in
   // (0, 2^8] (e4m3 reaches 448) and values down to 2^-13 of the row max stay
@@ -225,11 +242,20 @@ void fa_fwd_kernel(Params p) {
   constexpr int NKO = F8 ? NS / 2 : NS;   // K fragment reads per 32-key block
   constexpr int KTL = NL * KT;       // elements of the K tiles of all layers
   constexpr int BUF = KTL + VT;      // elements per LDS buffer
-  // two LDS buffers: tile j+1 loads while tile j is computed
-  __shared__ __attribute__((aligned(16))) T smem[2 * BUF];
+  // KH = 2: floats per lane of the state the second key half hands over
+  // (m, l, then the output accumulators), stored [row wave][value][lane]
+  constexpr int XN = QB * (2 + 16 * NDB);
+  constexpr int XBYTES = KH == 2 ? kWaves * XN * 64 * 4 : 0;
+  constexpr int SMEM_ELEMS = (KH * 2 * BUF * ESZ >= XBYTES) ? KH * 2 * BUF
+                                                            : (XBYTES + ESZ - 1) / ESZ;
+  // two LDS buffers per key half: tile j+1 loads while tile j is computed
+  __shared__ __attribute__((aligned(16))) T smem[SMEM_ELEMS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // wave: the row wave (0-3); half: which half of the key tiles (KH = 2)
+  const int wave = (tid >> 6) & (kWaves - 1);
+  const int half = KH == 2 ? tid >> 8 : 0;
   const int g = lane >> 5, ln = lane & 31;
 
   // Workgroup id -> (head, query block).
@@ -270,8 +296,14 @@ void fa_fwd_kernel(Params p) {
       const unsigned unit = um.unit, member = um.member;
       bh = int((unit % units_per_rank) * G + member);
       const int rank = int(unit / units_per_rank);
-      const int half = (p.n_qtiles + 1) / 2;
-      tile = rank < half ? p.n_qtiles - 1 - rank : rank - half;
+      if constexpr (KH == 2) {
+        // the grid runs in more than one round: heaviest row blocks first,
+        // so the last to start are the shortest
+        tile = p.n_qtiles - 1 - rank;
+      } else {
+        const int hr = (p.n_qtiles + 1) / 2;
+        tile = rank < hr ? p.n_qtiles - 1 - rank : rank - hr;
+      }
     } else {
       const unsigned logical = xcd_contiguous(blockIdx.x, gridDim.x);
       bh = int(logical / unsigned(p.n_qtiles));
@@ -550,9 +582,11 @@ void fa_fwd_kernel(Params p) {
   // wave index is taken as a scalar, so the destination (M0) is scalar work.
   // KVPOL is the loads' cache policy (see launch_one).
   const int wave_s = FA_SCALAR_WAVE ? __builtin_amdgcn_readfirstlane(wave) : wave;
+  const int half_s = KH == 2 ? __builtin_amdgcn_readfirstlane(half) : 0;
+  T* const smem_h = smem + half_s * 2 * BUF;   // this key half's two buffers
   auto dma_tile = [&](int j, int buf) {
     if constexpr (VTR) {
-      char* base = reinterpret_cast<char*>(smem + buf * BUF);
+      char* base = reinterpret_cast<char*>(smem_h + buf * BUF);
       const int soff = j * BN * D * ESZ;
 #pragma unroll
       for (int i = 0; i < DNI; ++i) {
@@ -661,7 +695,7 @@ void fa_fwd_kernel(Params p) {
   }
 
   auto compute = [&](int j, int buf) {
-    const T* sK = smem + buf * BUF;
+    const T* sK = smem_h + buf * BUF;
     const T* sV = sK + KTL;
     const int key0 = j * BN;
 
@@ -822,25 +856,37 @@ void fa_fwd_kernel(Params p) {
   // Tile j+1 is requested (into the other LDS buffer, or into registers for
   // fp32) before tile j is computed; one barrier per tile.  The buffer being
   // filled was last read in the previous iteration, before its barrier.
-  if (j_end > j_begin) {
-    dma_tile(j_begin, 0);
+  // KH = 2: the first half takes tiles [j_begin, j_begin + n/2), the second
+  // the rest; both run ceil(n/2) iterations so that every wave reaches every
+  // barrier (the first half idles through the last one when n is odd).
+  int t_begin = j_begin, t_end = j_end;
+  if constexpr (KH == 2) {
+    const int mid = j_begin + (j_end - j_begin) / 2;
+    if (half == 0) t_end = mid;
+    else t_begin = mid;
+  }
+  const int iters = KH == 2 ? (j_end - j_begin + 1) / 2 : j_end - j_begin;
+  if (iters > 0) {
+    if (t_begin < t_end) dma_tile(t_begin, 0);
     gload(j_begin);
     if constexpr (BIAS) load_bias(bcur, j_begin);
     sstore(0);
     if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
     __syncthreads();
   }
-  for (int j = j_begin; j < j_end; ++j) {
-    const int cur = (j - j_begin) & 1;
-    const bool has_next = j + 1 < j_end;
+  for (int it = 0; it < iters; ++it) {
+    const int j = t_begin + it;
+    const int cur = it & 1;
+    const bool has_tile = KH == 1 || j < t_end;
+    const bool has_next = j + 1 < t_end;
     if (has_next) {
       dma_tile(j + 1, cur ^ 1);
       gload(j + 1);
     }
     // a wave skips tiles above its rows' diagonal and, with a window, tiles
     // wholly left of its rows' windows
-    const bool active = wave_has_rows && (!CAUSAL || (j * BN <= wave_pos_max &&
-                                                      j * BN + BN - 1 >= wave_key_lo));
+    const bool active = has_tile && wave_has_rows &&
+                        (!CAUSAL || (j * BN <= wave_pos_max && j * BN + BN - 1 >= wave_key_lo));
     if constexpr (BIAS) {
       const bool next_active =
           has_next && wave_has_rows &&
@@ -860,6 +906,46 @@ void fa_fwd_kernel(Params p) {
     // the direct LDS loads of this wave are done before the barrier publishes them
     if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
     __syncthreads();
+  }
+
+  // ---- KH = 2: merge the second key half's state into the first ---------------
+  // Both halves hold the same rows in the same lanes, so the merge is per lane:
+  // with M = max(m0, m1), each side's sum and output are scaled by
+  // 2^(m_side - M) (0 for a side that saw no key) and added -- the merge of
+  // two partial states of the kwkr.cn tutorial, §2.2.  The LDS buffers are
+  // free: the last iteration's barrier followed every wave's last read, and
+  // no tile load is in flight.
+  if constexpr (KH == 2) {
+    float* xs = reinterpret_cast<float*>(smem) + wave * XN * 64 + lane;
+    if (half == 1) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float* x = xs + qb * (2 + 16 * NDB) * 64;
+        x[0] = m_ref[qb];
+        x[64] = l_run[qb];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[(2 + 16 * db + r) * 64] = acc[qb][db][r];
+      }
+    }
+    __syncthreads();
+    if (half == 1) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float* x = xs + qb * (2 + 16 * NDB) * 64;
+      const float m1 = x[0], l1 = x[64];
+      const float m = fmaxf(m_ref[qb], m1);
+      const float a0 = m_ref[qb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[qb] - m);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+      m_ref[qb] = m;
+      l_run[qb] = l_run[qb] * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[qb][db][r] = acc[qb][db][r] * a0 + x[(2 + 16 * db + r) * 64] * a1;
+    }
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 -----------------------------
@@ -1063,17 +1149,17 @@ __global__ __launch_bounds__(256) void fa_merge_few_kernel(
 // The choice is a template argument: a branch on it inside the tile loop cost
 // 1.3% on the split instances that do not take it.
 template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT,
-          bool WINDOW = false, int NL = 1>
+          bool WINDOW = false, int NL = 1, int KH = 1>
 hipError_t launch_one(const Params& p, unsigned grid, hipStream_t stream) {
   void* args[] = {const_cast<Params*>(&p)};
   const void* fn = reinterpret_cast<const void*>(
-      &fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT, WINDOW, NL, 0>);
+      &fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT, WINDOW, NL, 0, KH>);
   if constexpr (SPLIT && FA_SPLIT_KV_STREAM && !std::is_same<T, float>::value) {
     if (p.n_qtiles == 1)
       fn = reinterpret_cast<const void*>(
-          &fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT, WINDOW, NL, kPolicyNT>);
+          &fa_fwd_kernel<T, D, BN, QB, CAUSAL, BIAS, SPLIT, WINDOW, NL, kPolicyNT, KH>);
   }
-  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads * KH), args, 0, stream);
 }
 
 // Chain instances.  Keys per tile: the K tiles of all layers and the V tile
@@ -1148,8 +1234,10 @@ hipError_t launch_t(const Params& p, unsigned grid, hipStream_t s, int D, bool c
     if constexpr (!std::is_same<T, float>::value && !SPLIT) {
       if (!bias) {
         if (causal && p.window > 0)
-          return launch_one<T, 64, kBN64, kQB64, true, false, false, true>(p, grid, s);
-        return causal ? launch_one<T, 64, kBN64, kQB64, true, false, false>(p, grid, s)
+          return launch_one<T, 64, kBN64, kQB64, true, false, false, true, 1, FA_KH64>(p, grid,
+                                                                                       s);
+        return causal ? launch_one<T, 64, kBN64, kQB64, true, false, false, false, 1, FA_KH64>(
+                            p, grid, s)
                       : launch_one<T, 64, kBN64, kQB64, false, false, false>(p, grid, s);
       }
     }
@@ -1215,7 +1303,8 @@ Params make_params(const LaunchArgs& a, int rows_per_block, int n_rows) {
 hipError_t launch_f8(const Params& p, unsigned grid, hipStream_t s, int D, bool causal) {
   using F8 = fp8e4m3;
   if (D == 64)
-    return causal ? launch_one<F8, 64, 64, 1, true, false, false>(p, grid, s)
+    return causal ? launch_one<F8, 64, 64, 1, true, false, false, false, 1, FA_KH64_F8>(p, grid,
+                                                                                         s)
                   : launch_one<F8, 64, 64, 1, false, false, false>(p, grid, s);
   return causal ? launch_one<F8, 128, 64, 1, true, false, false>(p, grid, s)
                 : launch_one<F8, 128, 64, 1, false, false, false>(p, grid, s);

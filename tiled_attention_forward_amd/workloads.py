@@ -27,7 +27,9 @@ its 1024 most recent keys.  The chain shape is the same GQA setup at the last
 layer of a 4-layer Block Attention Residual block, whose logits sum the Q K^T
 products of all four layers (in place of the dense logit tensor); its Q and K
 are drawn layer by layer (Q_l, then K_l, oldest layer first), then V.  The
-FP8 shape is the benchmark report shape with Q, K and V rounded to E4M3.
+FP8 shape is the benchmark report shape with Q, K and V rounded to E4M3.  The
+report shape with a dense logit term (D = 64) measures the bias path at the
+head size where the softmax, not the matrix products, bounds the kernel.
 """
 
 from __future__ import annotations
@@ -113,6 +115,8 @@ WORKLOADS = {
         Workload("b8_h32_s2048_d128_bf16", 8, 32, 32, 2048, 2048, 128, "bf16", False, False),
         Workload("b1_hq20_hkv4_s8192_d128_bf16_causal_bias", 1, 20, 4, 8192, 8192, 128, "bf16",
                  True, True),
+        Workload("b2_h16_s4096_d64_bf16_causal_bias", 2, 16, 16, 4096, 4096, 64, "bf16", True,
+                 True),
         Workload("decode_b8_hq20_hkv4_nq1_nk32768_d128_bf16", 8, 20, 4, 1, 32768, 128, "bf16",
                  False, False, "split"),
         Workload("b1_h2_s16384_d64_bf16", 1, 2, 2, 16384, 16384, 64, "bf16", False, False,
