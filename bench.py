@@ -12,7 +12,9 @@ recomputed from the Q and K of all four layers).  The default workload is B=2, H
 D=64, bf16, causal.  Timing follows the CUDA-event method of the Day 26 post
 (blog.ans20xx.com/posts/ai/day26): W untimed warm-up steps, then K steps with
 one event recorded before each step and one after the last, on the stream the
-kernels run on.  Prints one JSON line.
+kernels run on.  Before the warm-up steps the device is kept busy for
+--settle-ms (default 60 ms) with plain bf16 matrix products, so that the timed
+steps do not catch the GPU clock ramping up from idle.  Prints one JSON line.
 
 value     = 4*B*H*S^2*D / t_step in TFLOP/s (the post's formula, not halved
             for causal), t_step = wall time of the K steps / K;
@@ -79,6 +81,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time for the oracle sample")
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="before the warm-up steps, keep the GPU busy this long with plain "
+                         "bf16 matrix products (not the attention kernel), so that the clock "
+                         "has left its idle state when the timed steps start; 0 = off")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before timing, run one plain device copy of MIB MiB (a reference "
                          "dispatch for scaling HBM byte counters); untimed")
@@ -266,6 +272,26 @@ def cpu_baseline_one_thread(w, q, k, v, bias, target_s: float):
     return base
 
 
+def settle_clock(dev, ms: float) -> float:
+    """Keep the device busy for about ``ms`` ms with dense bf16 products (a
+    torch matmul, not the attention kernel): the GPU clock ramps up over the
+    first tens of milliseconds of sustained load, and a benchmark of a few
+    milliseconds would otherwise time that ramp.  Untimed; returns the
+    milliseconds spent."""
+    import torch
+    if ms <= 0:
+        return 0.0
+    a = torch.full((4096, 4096), 1.0 / 4096, dtype=torch.bfloat16, device=dev)
+    c = torch.empty_like(a)
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(16):
+            torch.mm(a, a, out=c)
+        torch.cuda.synchronize(dev)
+    del a, c
+    return (time.perf_counter() - t0) * 1e3
+
+
 def environment(lib_version: str):
     """What the numbers were measured on (the Day 26 post's report header)."""
     import platform
@@ -368,6 +394,8 @@ def main():
         if st != 0:
             raise binding.FaError(st, binding.fa_status_string(st))
 
+    settled_ms = settle_clock(dev, args.settle_ms)
+
     # peak device memory of the run (the Day 26 report's peak-memory column):
     # inputs, outputs and any workspace are allocated by now, so the steps
     # themselves should add nothing
@@ -456,6 +484,7 @@ def main():
                                     / peak, 2),
         "peak_mem_gb": round(mem_peak / 1e9, 4),
         "alloc_in_timed_steps_bytes": int(mem_peak - mem_base),
+        "clock_settle_ms": round(settled_ms, 1),
         "launch_ms": {"mean": round(launch_ms, 5), "median": round(statistics.median(per), 5),
                       "p90": round(per[int(len(per) * 0.9)], 5), "min": round(per[0], 5)},
         "roofline": roof,
