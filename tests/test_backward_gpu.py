@@ -74,6 +74,9 @@ CASES = [
     (1, 3, 3, 65, 63, 128, "fp16", True, True),
     (1, 2, 2, 1000, 1000, 64, "bf16", True, False),
     (1, 6, 2, 7, 40, 64, "bf16", True, True),        # group 3, fewer rows than a tile
+    # non-causal D = 128 without a logit term: 32-row query tiles, V in LDS
+    (1, 4, 2, 97, 200, 128, "bf16", False, False),   # group 2: row tiles cross heads
+    (1, 3, 1, 31, 33, 128, "bf16", False, False),    # group 3, rows < one tile, key tail
 ]
 
 

@@ -109,6 +109,7 @@ BWD_CASES = [
     (1, 4, 2, 130, 170, 128, "fp16", False, True, None),
     (1, 6, 2, 77, 129, 128, "bf16", True, False, None),
     (1, 4, 2, 300, 333, 64, "bf16", True, False, 100),
+    (1, 4, 2, 131, 170, 128, "bf16", False, False, None),
 ]
 
 

@@ -52,15 +52,38 @@ constexpr int kBwdThreads = 256;  // 4 waves
 #ifndef FA_DKDV_MINB64
 #define FA_DKDV_MINB64 3
 #endif
-// dK/dV kernel at D = 128: the key block's K and V sit in LDS (64 KB, one
-// workgroup per compute unit), except in the non-causal instance without a
-// logit term, where they sit in registers and two workgroups share a compute
-// unit (256 VGPRs and a 120-byte spill: B8 H32 S2048 backward 2.47 -> 2.38 ms;
-// the causal instances spill twice as much there and ran 18% slower).
-constexpr bool dkdv_kv_in_registers(int D, bool causal, bool bias) {
-  return D == 64 || (D == 128 && !causal && !bias);
+// Where the dK/dV kernel keeps its key block's K and V, and the height of the
+// query tiles it streams:
+//  * D = 64: K and V in registers, 64-row query tiles;
+//  * D = 128, non-causal, no logit term: K in registers, V in LDS (32 KB) and
+//    32-row query tiles (two 16.3 KB stages), 66 KB in all: two workgroups per
+//    compute unit at 256 VGPRs without spilling (with V in registers too and
+//    64-row tiles the kernel spilled 140 bytes per lane, and the spill
+//    reloads, 147 MB of scratch writes and reads per B8 H32 S2048 backward,
+//    waited in the tile loop: that backward took 2.26 ms, 1.88 ms now);
+//  * other D = 128: K and V in LDS (64 KB) and 64-row tiles, one workgroup per
+//    compute unit (with K and V in registers the causal instances spilled
+//    twice as much and ran 18% slower).
+#ifndef FA_DKDV128_VLDS
+#define FA_DKDV128_VLDS 1
+#endif
+constexpr bool dkdv_pair(int D, bool causal, bool bias) {  // two workgroups per CU at D = 128
+  return D == 128 && !causal && !bias;
 }
-constexpr int kQTile = 64;        // query rows per tile in the dK/dV kernel
+constexpr bool dkdv_k_in_lds(int D, bool causal, bool bias) {
+  return D == 128 && !dkdv_pair(D, causal, bias);
+}
+constexpr bool dkdv_v_in_lds(int D, bool causal, bool bias) {
+  return D == 128 && (!dkdv_pair(D, causal, bias) || FA_DKDV128_VLDS);
+}
+// The instance that runs at 256 VGPRs takes its LDS offsets from two
+// registers (OffsetsLean) rather than from 24: with the table it spilled.
+constexpr bool dkdv_lean_offsets(int D, bool causal, bool bias) {
+  return dkdv_pair(D, causal, bias) && FA_DKDV128_VLDS;
+}
+constexpr int dkdv_qtile(int D, bool causal, bool bias) {
+  return (dkdv_pair(D, causal, bias) && FA_DKDV128_VLDS) ? 32 : 64;
+}
 constexpr int kKTile = 64;        // keys per tile in the dQ kernel
 
 struct BwdParams {
@@ -145,6 +168,39 @@ struct Offsets {
         const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
         tr_off[t][db] = r * RB + ((c ^ lds_swizzle<D>(r)) * 16) + 8 * (lane & 1);
       }
+  }
+  __device__ __forceinline__ int row(int st) const { return row_off[st]; }
+  __device__ __forceinline__ int tr(int t, int db) const { return tr_off[t][db]; }
+  __device__ __forceinline__ Offsets fresh() const { return *this; }
+};
+
+// The same offsets from two registers: chunk 2*st + g differs from chunk g in
+// bits 1-3 only, which the swizzle's XOR leaves alone, so the row offset of
+// step st is that of step 0 XOR 32*st; column block db likewise XORs 64*db
+// into the transposed offset, and rows +8 flip bit 1 of the swizzle (XOR 32)
+// and add 8 rows.  For kernels that run short of registers.
+template <int D>
+struct OffsetsLean {
+  static constexpr int RB = D * 2;
+  int row0, tr0;
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 5, ln = lane & 31;
+    row0 = ln * RB + ((g ^ lds_swizzle<D>(ln)) * 16);
+    const int r = 4 * g + ((lane >> 2) & 3);
+    const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    tr0 = r * RB + ((c ^ lds_swizzle<D>(r)) * 16) + 8 * (lane & 1);
+  }
+  __device__ __forceinline__ int row(int st) const { return row0 ^ (32 * st); }
+  __device__ __forceinline__ int tr(int t, int db) const {
+    return (tr0 ^ (64 * db + 32 * t)) + t * 8 * RB;
+  }
+  // A copy whose registers the compiler must treat as new values, so that the
+  // XORs above are redone where they are used instead of being hoisted out of
+  // the tile loop into registers of their own.
+  __device__ __forceinline__ OffsetsLean fresh() const {
+    OffsetsLean o = *this;
+    asm volatile("" : "+v"(o.row0), "+v"(o.tr0));
+    return o;
   }
 };
 
@@ -425,19 +481,21 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW>
 __global__ __launch_bounds__(kBwdThreads, (D == 64 ? (BIAS ? 2 : FA_DKDV_MINB64)
-                                                   : dkdv_kv_in_registers(D, CAUSAL, BIAS) ? 2 : 1))
+                                                   : dkdv_pair(D, CAUSAL, BIAS) ? 2 : 1))
 void fa_bwd_dkdv_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
-  constexpr int BQ = kQTile;
+  constexpr int BQ = dkdv_qtile(D, CAUSAL, BIAS);
   constexpr int NS = D / 16, NDB = D / 32, NQB = BQ / 32;
   constexpr int RB = D * 2;
   constexpr int TILE = BQ * RB;               // bytes per Q (or dO) tile
-  constexpr bool KV_LDS = !dkdv_kv_in_registers(D, CAUSAL, BIAS);  // K/V of the block in LDS, else registers
-  constexpr int KVB = KV_LDS ? 128 * RB : 16; // bytes per K (or V) block in LDS
+  constexpr bool K_LDS = dkdv_k_in_lds(D, CAUSAL, BIAS);  // the block's K in LDS, else registers
+  constexpr bool V_LDS = dkdv_v_in_lds(D, CAUSAL, BIAS);  // the block's V in LDS, else registers
+  constexpr int KB_BYTES = 128 * RB;                        // bytes of the block's K (or V)
   // per stage: Q tile, dO tile, lse2[BQ], delta[BQ]
   constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + 2 * KVB];
+  constexpr int KV_BYTES = (K_LDS ? KB_BYTES : 0) + (V_LDS ? KB_BYTES : 0);
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + (KV_BYTES ? KV_BYTES : 16)];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, ln = lane & 31;
@@ -478,24 +536,27 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 
   TileLoad<BQ, D> tl;
   tl.init(wave, lane);
-  Offsets<D> of;
+  std::conditional_t<dkdv_lean_offsets(D, CAUSAL, BIAS), OffsetsLean<D>, Offsets<D>> of;
   of.init(lane);
 
-  // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T
-  Frag kf[KV_LDS ? 1 : NS], vf[KV_LDS ? 1 : NS];
-  char* sKV = smem + 2 * STAGE;
-  if constexpr (KV_LDS) {
+  // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T,
+  // held in registers or read from the block's copy in LDS
+  Frag kf[K_LDS ? 1 : NS], vf[V_LDS ? 1 : NS];
+  char* sK = smem + 2 * STAGE;
+  char* sV = sK + (K_LDS ? KB_BYTES : 0);
+  if constexpr (K_LDS || V_LDS) {
     TileLoad<128, D> kl;
     kl.init(wave, lane);
-    kl.issue(k_rs, sKV, wave, uint32_t(k_blk) * RB);
-    kl.issue(v_rs, sKV + KVB, wave, uint32_t(k_blk) * RB);
-  } else {
+    if constexpr (K_LDS) kl.issue(k_rs, sK, wave, uint32_t(k_blk) * RB);
+    if constexpr (V_LDS) kl.issue(v_rs, sV, wave, uint32_t(k_blk) * RB);
+  }
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      const int off = kj * RB + (16 * st + 8 * g) * 2;
+  for (int st = 0; st < NS; ++st) {
+    const int off = kj * RB + (16 * st + 8 * g) * 2;
+    if constexpr (!K_LDS)
       kf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(k_rs, off, 0, 0));
+    if constexpr (!V_LDS)
       vf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(v_rs, off, 0, 0));
-    }
   }
 
   f32x16 dka[NDB], dva[NDB];
@@ -524,19 +585,20 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const uint32_t soff = uint32_t(r0) * RB;
     tl.issue(q_rs, st, wave, soff);
     tl.issue(g_rs, st + TILE, wave, soff);
-    // lse2 and delta: 64 floats each, by 16 lanes of waves 0 and 1
+    // lse2 and delta: BQ floats each, 16 bytes per lane of waves 0 and 1
     if (wave == 0) {
-      if (lane < 16)
+      if (lane < BQ / 4)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(l_rs, (lds_void*)(st + 2 * TILE), 16,
                                                  unsigned(lane * 16), uint32_t(r0) * 4, 0, 0);
     } else if (wave == 1) {
-      if (lane < 16)
+      if (lane < BQ / 4)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d_rs, (lds_void*)(st + 2 * TILE + BQ * 4), 16,
                                                  unsigned(lane * 16), uint32_t(r0) * 4, 0, 0);
     }
   };
 
   auto compute = [&](int r0, int i0, int buf) {
+    const auto ofs = of.fresh();
     const char* sQ = smem + buf * STAGE;
     const char* sG = sQ + TILE;
     const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
@@ -556,15 +618,14 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       f32x16 s, dp;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const Frag qa = lds_frag<T>(sQ + qb * 32 * RB + of.row_off[st]);
-        const Frag kb = KV_LDS ? lds_frag<T>(sKV + wave * 32 * RB + of.row_off[st]) : kf[st];
+        const Frag qa = lds_frag<T>(sQ + qb * 32 * RB + ofs.row(st));
+        const Frag kb = K_LDS ? lds_frag<T>(sK + wave * 32 * RB + ofs.row(st)) : kf[st];
         s = E::mma(qa, kb, st == 0 ? f32x16{} : s);
       }
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const Frag ga = lds_frag<T>(sG + qb * 32 * RB + of.row_off[st]);
-        const Frag vb =
-            KV_LDS ? lds_frag<T>(sKV + KVB + wave * 32 * RB + of.row_off[st]) : vf[st];
+        const Frag ga = lds_frag<T>(sG + qb * 32 * RB + ofs.row(st));
+        const Frag vb = V_LDS ? lds_frag<T>(sV + wave * 32 * RB + ofs.row(st)) : vf[st];
         dp = E::mma(ga, vb, st == 0 ? f32x16{} : dp);
       }
       // register r: query row qb*32 + 8*(r/4) + 4*g + r%4 of the tile, key kj
@@ -616,9 +677,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         const Frag dsf = pack_half<T>(dp, h);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const Frag gt = lds_frag_tr<T>(sG + (qb * 32 + 16 * h) * RB, of.tr_off[0][db], of.tr_off[1][db]);
+          const Frag gt = lds_frag_tr<T>(sG + (qb * 32 + 16 * h) * RB, ofs.tr(0, db), ofs.tr(1, db));
           dva[db] = E::mma(gt, pf, dva[db]);
-          const Frag qt = lds_frag_tr<T>(sQ + (qb * 32 + 16 * h) * RB, of.tr_off[0][db], of.tr_off[1][db]);
+          const Frag qt = lds_frag_tr<T>(sQ + (qb * 32 + 16 * h) * RB, ofs.tr(0, db), ofs.tr(1, db));
           dka[db] = E::mma(qt, dsf, dka[db]);
         }
       }
