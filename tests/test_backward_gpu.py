@@ -125,7 +125,8 @@ def test_backward_deterministic(gpu_device):
     assert all(torch.equal(x, y) for x, y in zip(a, c))
 
 
-@pytest.mark.parametrize("name", ["b2_h16_s4096_d64_bf16_causal", "b8_h32_s2048_d128_bf16"])
+@pytest.mark.parametrize("name", ["b2_h16_s4096_d64_bf16_causal", "b8_h32_s2048_d128_bf16",
+                                  "b8_h32_s2048_d128_bf16_causal"])
 def test_backward_full_size_heads(gpu_device, name):
     """Full-size run; the oracle differentiates two whole heads (MHA: a head's
     dQ, dK and dV depend only on that head's Q, K, V and dO)."""

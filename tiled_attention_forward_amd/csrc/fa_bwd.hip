@@ -55,20 +55,21 @@ constexpr int kBwdThreads = 256;  // 4 waves
 // Where the dK/dV kernel keeps its key block's K and V, and the height of the
 // query tiles it streams:
 //  * D = 64: K and V in registers, 64-row query tiles;
-//  * D = 128, non-causal, no logit term: K in registers, V in LDS (32 KB) and
-//    32-row query tiles (two 16.3 KB stages), 66 KB in all: two workgroups per
-//    compute unit at 256 VGPRs without spilling (with V in registers too and
-//    64-row tiles the kernel spilled 140 bytes per lane, and the spill
-//    reloads, 147 MB of scratch writes and reads per B8 H32 S2048 backward,
-//    waited in the tile loop: that backward took 2.26 ms, 1.88 ms now);
-//  * other D = 128: K and V in LDS (64 KB) and 64-row tiles, one workgroup per
-//    compute unit (with K and V in registers the causal instances spilled
-//    twice as much and ran 18% slower).
+//  * D = 128 without a logit term: K in registers, V in LDS (32 KB) and 32-row
+//    query tiles (two 16.3 KB stages), 66 KB in all: two workgroups per compute
+//    unit at 256 VGPRs without spilling.  Before, the non-causal instance kept
+//    V in registers too, with 64-row tiles, and spilled 140 bytes per lane
+//    (147 MB of scratch writes per B8 H32 S2048 backward, their reloads
+//    waited in the tile loop): that backward took 2.26 ms, 1.88 ms now; the
+//    causal instances kept K and V in LDS, one workgroup per compute unit:
+//    1.30 ms, 1.11 ms now;
+//  * D = 128 with a logit term: K and V in LDS (64 KB) and 64-row tiles, one
+//    workgroup per compute unit (the layout above spilled 188 bytes there).
 #ifndef FA_DKDV128_VLDS
 #define FA_DKDV128_VLDS 1
 #endif
 constexpr bool dkdv_pair(int D, bool causal, bool bias) {  // two workgroups per CU at D = 128
-  return D == 128 && !causal && !bias;
+  return D == 128 && !bias;
 }
 constexpr bool dkdv_k_in_lds(int D, bool causal, bool bias) {
   return D == 128 && !dkdv_pair(D, causal, bias);

@@ -29,7 +29,9 @@ products of all four layers (in place of the dense logit tensor); its Q and K
 are drawn layer by layer (Q_l, then K_l, oldest layer first), then V.  The
 FP8 shape is the benchmark report shape with Q, K and V rounded to E4M3.  The
 report shape with a dense logit term (D = 64) measures the bias path at the
-head size where the softmax, not the matrix products, bounds the kernel.
+head size where the softmax, not the matrix products, bounds the kernel.  The
+causal variant of the tutorial's shape is the common training case at D = 128
+(causal, no logit term), timed for the backward.
 """
 
 from __future__ import annotations
@@ -113,6 +115,7 @@ WORKLOADS = {
         Workload("b2_h16_s512_d64_fp16_causal", 2, 16, 16, 512, 512, 64, "fp16", True, False),
         Workload("b2_h16_s4096_d64_bf16_causal", 2, 16, 16, 4096, 4096, 64, "bf16", True, False),
         Workload("b8_h32_s2048_d128_bf16", 8, 32, 32, 2048, 2048, 128, "bf16", False, False),
+        Workload("b8_h32_s2048_d128_bf16_causal", 8, 32, 32, 2048, 2048, 128, "bf16", True, False),
         Workload("b1_hq20_hkv4_s8192_d128_bf16_causal_bias", 1, 20, 4, 8192, 8192, 128, "bf16",
                  True, True),
         Workload("b2_h16_s4096_d64_bf16_causal_bias", 2, 16, 16, 4096, 4096, 64, "bf16", True,
