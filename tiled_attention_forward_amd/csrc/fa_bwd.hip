@@ -12,18 +12,18 @@
 // tiles), so no atomics are needed and the results are deterministic, at the
 // price of computing S and dP twice.
 //
-// Kernels (16-bit types, D in {64, 128}):
-//  * fa_bwd_prep_kernel: delta_i = sum_d dO_id O_id and lse2_i = LSE_i log2(e)
-//    (+inf for rows with LSE = -inf, so that their P is exactly 0), fp32;
+// Kernels (16-bit types, D in {64, 128}), launched in this order:
 //  * fa_bwd_dq_kernel: the forward's layout -- each wave owns 32 query rows,
 //    one per lane; S^T = K Q^T and dP^T = V dO^T on 32x32x16 MFMAs with Q and
 //    dO rows held in registers and K/V tiles streamed through LDS; then
-//    dQ^T += K^T dS^T with K read transposed from LDS;
+//    dQ^T += K^T dS^T with K read transposed from LDS.  Its prologue forms
+//    delta_i = sum_d dO_id O_id and lse2_i = LSE_i log2(e) (+inf for rows
+//    with LSE = -inf, so that their P is exactly 0), fp32, and stores both;
 //  * fa_bwd_dkdv_kernel: the roles swapped -- each wave owns 32 keys, one per
 //    lane, and the query rows of the KV head's group (packed as the key-split
-//    forward packs them) stream through LDS in 64-row tiles: S = Q K^T and
-//    dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS with Q and dO read
-//    transposed from LDS.
+//    forward packs them) stream through LDS in 32- or 64-row tiles with their
+//    delta and lse2: S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
+//    dK^T += Q^T dS with Q and dO read transposed from LDS.
 // P and dS are rounded to the input type for the MFMAs (as P is in the
 // forward); all sums are fp32.
 //
@@ -260,38 +260,9 @@ __device__ __forceinline__ void store_rows(T* dst_row, const f32x16 (&acc)[NDB],
 }
 
 // ---------------------------------------------------------------------------
-// delta = rowsum(dO o O) and lse2 = LSE * log2(e), one row per D/8 lanes.
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;  // lanes per row (8 elements, 16 bytes each)
-  constexpr int RPB = 256 / LPR;
-  const int tid = threadIdx.x;
-  const int sub = tid % LPR;
-  const T* o = static_cast<const T*>(p.o);
-  const T* dout = static_cast<const T*>(p.dout);
-  for (int64_t row = int64_t(blockIdx.x) * RPB + tid / LPR; row < p.rows;
-       row += int64_t(gridDim.x) * RPB) {
-    const u32x4 ow = *reinterpret_cast<const u32x4*>(o + row * D + sub * 8);
-    const u32x4 gw = *reinterpret_cast<const u32x4*>(dout + row * D + sub * 8);
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc = fmaf(Elem<T>::widen(ow[w] & 0xffffu), Elem<T>::widen(gw[w] & 0xffffu), acc);
-      acc = fmaf(Elem<T>::widen(ow[w] >> 16), Elem<T>::widen(gw[w] >> 16), acc);
-    }
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-    if (sub == 0) {
-      p.delta[row] = acc;
-      const float l = p.lse[row];
-      p.lse2[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dQ: one workgroup per (b, hq, 128-row query block), 64-key tiles.
+// dQ: one workgroup per (b, hq, 128-row query block), 64-key tiles.  It also
+// forms each row's delta = rowsum(dO o O) and lse2 = LSE log2(e) and leaves
+// them in the workspace for the dK/dV kernel, which runs after it.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW>
 __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) {
@@ -351,8 +322,34 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
     gf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(g_rs, off, 0, 0));
   }
   const bool row_ok = qi < p.Nq;
-  const float lse2 = row_ok ? p.lse2[row_base + qi] : INFINITY;
-  const float dlt = row_ok ? p.delta[row_base + qi] : 0.f;
+  // delta of this lane's row: the lane holds half of the row's dO (chunks
+  // 2*st + g), reads the same half of O and adds its partner's (lane ^ 32).
+  // lse2 = +inf for rows with LSE = -inf (no visible key), so their P is 0.
+  float dlt, lse2;
+  {
+    const T* Oh = static_cast<const T*>(p.o) + row_base * D;
+    const __amdgpu_buffer_rsrc_t o_rs = make_rsrc(Oh, uint32_t(p.Nq) * RB);
+    float acc = 0.f;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const u32x4 ow =
+          __builtin_amdgcn_raw_buffer_load_b128(o_rs, qi * RB + (16 * st + 8 * g) * 2, 0, 0);
+      const u32x4 gw = __builtin_bit_cast(u32x4, gf[st]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = fmaf(E::widen(ow[w] & 0xffffu), E::widen(gw[w] & 0xffffu), acc);
+        acc = fmaf(E::widen(ow[w] >> 16), E::widen(gw[w] >> 16), acc);
+      }
+    }
+    acc += __shfl_xor(acc, 32, 64);
+    const float l = row_ok ? p.lse[row_base + qi] : -INFINITY;
+    lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    dlt = row_ok ? acc : 0.f;
+    if (row_ok && g == 0) {
+      p.delta[row_base + qi] = dlt;
+      p.lse2[row_base + qi] = lse2;
+    }
+  }
 
   // bias rows of this block (resource over the block's rows)
   const T* bblk = BIAS ? static_cast<const T*>(p.bias) + (row_base + q_blk) * p.Nk
@@ -717,15 +714,10 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 }
 
 template <typename T, int D>
-hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool bias, hipStream_t s, unsigned g_prep,
-                        unsigned g_dq, unsigned g_kv) {
+hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool bias, hipStream_t s, unsigned g_dq,
+                        unsigned g_kv) {
   void* args[] = {const_cast<BwdParams*>(&p)};
   hipError_t e = hipSuccess;
-  if (g_prep) {
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_prep_kernel<T, D>), dim3(g_prep),
-                        dim3(256), args, 0, s);
-    if (e != hipSuccess) return e;
-  }
   const void* dq;
   const void* kv;
   if (causal && p.window > 0) {
@@ -782,20 +774,16 @@ int launch_backward(const BwdArgs& a) {
   p.scale = a.scale;
   p.bias_vec = (a.Nk % 4) == 0;
   p.window = a.window;
-  const int64_t lpr = a.D / 8;
-  const int64_t rows_per_block = 256 / lpr;
-  const int64_t want = (p.rows + rows_per_block - 1) / rows_per_block;
-  const unsigned g_prep = unsigned(want < 16384 ? want : 16384);
   const unsigned g_dq = unsigned(p.n_qblk) * unsigned(p.BH);
   const unsigned g_kv = unsigned(p.n_kblk) * unsigned(p.BHkv);
   hipStream_t s = static_cast<hipStream_t>(a.stream);
   hipError_t e;
   if (a.dtype == FA_DTYPE_BF16) {
-    e = a.D == 64 ? launch_bwd_d<__bf16, 64>(p, a.causal, a.bias, s, g_prep, g_dq, g_kv)
-                  : launch_bwd_d<__bf16, 128>(p, a.causal, a.bias, s, g_prep, g_dq, g_kv);
+    e = a.D == 64 ? launch_bwd_d<__bf16, 64>(p, a.causal, a.bias, s, g_dq, g_kv)
+                  : launch_bwd_d<__bf16, 128>(p, a.causal, a.bias, s, g_dq, g_kv);
   } else {
-    e = a.D == 64 ? launch_bwd_d<_Float16, 64>(p, a.causal, a.bias, s, g_prep, g_dq, g_kv)
-                  : launch_bwd_d<_Float16, 128>(p, a.causal, a.bias, s, g_prep, g_dq, g_kv);
+    e = a.D == 64 ? launch_bwd_d<_Float16, 64>(p, a.causal, a.bias, s, g_dq, g_kv)
+                  : launch_bwd_d<_Float16, 128>(p, a.causal, a.bias, s, g_dq, g_kv);
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
