@@ -68,6 +68,11 @@ def _setup(case, group_checked, dev, seed=5):
 FWD_CASES = [
     # path, B, Hq, Hkv, Nq, Nk, D, dtype, causal, bias, extra (splits / window)
     ("fused", 1, 4, 2, 200, 333, 64, "bf16", True, True, None),
+    # bias rows that allow 16-byte loads (Nk % 8 == 0) go through LDS; the last
+    # key tile runs past Nk
+    ("fused", 1, 4, 2, 200, 264, 64, "bf16", True, True, None),
+    ("fused", 1, 4, 2, 130, 200, 128, "bf16", False, True, None),
+    ("fused", 1, 4, 2, 97, 136, 96, "fp16", True, True, None),
     ("fused", 1, 4, 2, 130, 70, 128, "fp16", False, True, None),
     ("fused", 1, 4, 2, 97, 161, 80, "bf16", True, False, None),
     ("fused", 1, 4, 2, 75, 100, 64, "fp32", True, True, None),
@@ -76,6 +81,7 @@ FWD_CASES = [
     ("split", 1, 4, 2, 150, 333, 64, "fp16", True, True, 4),
     ("split", 1, 4, 2, 70, 201, 96, "bf16", False, False, 2),
     ("window", 1, 4, 2, 300, 333, 64, "bf16", True, True, 100),
+    ("window", 1, 4, 2, 300, 336, 64, "bf16", True, True, 100),
     ("window", 1, 4, 2, 200, 260, 128, "bf16", True, False, 64),
 ]
 

@@ -30,6 +30,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // memory counter bits [3:0] and [15:14] zero, expcnt [6:4] and lgkmcnt [11:8]
 // at their maxima (no wait).
 constexpr int kWaitVmem0 = 0x0F70;
+// waiting for lgkmcnt = 0 only (LDS reads): vmcnt and expcnt at their maxima
+constexpr int kWaitLgkm0 = 0xC07F;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------

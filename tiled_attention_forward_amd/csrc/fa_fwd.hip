@@ -86,6 +86,9 @@ constexpr int kPolicyNT = 2;  // buffer-load cache policy: non-temporal
 #define FA_SPLIT_BN128 32
 #endif
 // Key halves per workgroup of the causal D = 64 fused instances (1 or 2)
+#ifndef FA_BIAS_LDS
+#define FA_BIAS_LDS 1
+#endif
 #ifndef FA_KH64
 #define FA_KH64 1
 #endif
@@ -246,8 +249,19 @@ void fa_fwd_kernel(Params p) {
   // (m, l, then the output accumulators), stored [row wave][value][lane]
   constexpr int XN = QB * (2 + 16 * NDB);
   constexpr int XBYTES = KH == 2 ? kWaves * XN * 64 * 4 : 0;
-  constexpr int SMEM_ELEMS = (KH * 2 * BUF * ESZ >= XBYTES) ? KH * 2 * BUF
-                                                            : (XBYTES + ESZ - 1) / ESZ;
+  // 16-bit logit tiles (64 keys, rows whose length allows 16-byte loads) go
+  // HBM -> LDS by direct loads into a 4 KB region of each wave's own, 8 lanes
+  // per 128-byte row so that each load covers whole rows, and are read back
+  // in the score layout.  One tile per wave: D = 64 then takes 48 KB of LDS
+  // and 148 VGPRs, three workgroups per compute unit (two tiles per wave
+  // allowed only two: B2 H16 S4096 D64 causal + bias 160.3 vs 143.4 us).
+  // (not the D = 128 window instance: it spilled 232 bytes that way)
+  constexpr bool BLDS = BIAS && VTR && QB == 1 && BN == 64 && !(WINDOW && D == 128) && FA_BIAS_LDS;
+  constexpr int BTILE = 32 * BN * 2;                  // bytes of one wave's logit tile
+  constexpr int BLDS_BYTES = BLDS ? kWaves * BTILE : 0;
+  constexpr int KV_ELEMS = (KH * 2 * BUF * ESZ >= XBYTES) ? KH * 2 * BUF
+                                                          : (XBYTES + ESZ - 1) / ESZ;
+  constexpr int SMEM_ELEMS = KV_ELEMS + BLDS_BYTES / ESZ;
   // two LDS buffers per key half: tile j+1 loads while tile j is computed
   __shared__ __attribute__((aligned(16))) T smem[SMEM_ELEMS];
 
@@ -612,6 +626,47 @@ void fa_fwd_kernel(Params p) {
     }
   };
 
+  // Logit tiles through LDS (BLDS).  Load t (0..3) of a tile brings rows
+  // 8t .. 8t+7 of the wave's 32, lane l the 16-byte chunk (l & 7) of row
+  // 8t + (l >> 3), stored at chunk (l & 7) ^ ((row >> 1) & 7) of that row in
+  // LDS: 16 lanes reading one chunk of 16 consecutive rows then hit 16
+  // distinct bank groups.
+  char* const bias_lds = reinterpret_cast<char*>(smem + KV_ELEMS) + (BLDS ? wave_s * BTILE : 0);
+  int bdma_off[BLDS ? 4 : 1];
+  if constexpr (BLDS) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = 8 * t + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+      bdma_off[t] = ((wq0 - q_blk + r) * p.Nk + chunk * 8) * ESZ;
+    }
+  }
+  auto dma_bias = [&](int j) {
+    if constexpr (BLDS) {
+      char* dst = bias_lds;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        dma16_asm<0>(b_rs, (lds_void*)(dst + t * 1024), unsigned(bdma_off[t]),
+                                  unsigned(j * BN * ESZ));
+    }
+  };
+  // the lane's keys of the tile, as the 16-byte global loads give them:
+  // keys 32kb + 16h + 8g + 0..7 of row ln (chunk 4kb + 2h + g)
+  auto read_bias = [&](BiasVec (&dst)[QB][NKB][4]) {
+    if constexpr (BLDS) {
+      const char* src = bias_lds + ln * (BN * 2);
+      const int sw = (ln >> 1) & 7;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(src + (((4 * kb + 2 * h + g) ^ sw) * 16));
+          dst[0][kb][2 * h] = u32x2{raw[0], raw[1]};
+          dst[0][kb][2 * h + 1] = u32x2{raw[2], raw[3]};
+        }
+    }
+  };
+
   // fp32: global -> registers (the LDS store follows the compute of the tile)
   auto gload = [&](int j) {
     if constexpr (!VTR) {
@@ -694,7 +749,8 @@ void fa_fwd_kernel(Params p) {
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x16{};
   }
 
-  auto compute = [&](int j, int buf) {
+  // (called from two loops in the BLDS instances; inlined at both)
+  auto compute = [&](int j, int buf) __attribute__((always_inline)) {
     const T* sK = smem_h + buf * BUF;
     const T* sV = sK + KTL;
     const int key0 = j * BN;
@@ -866,46 +922,89 @@ void fa_fwd_kernel(Params p) {
     else t_begin = mid;
   }
   const int iters = KH == 2 ? (j_end - j_begin + 1) / 2 : j_end - j_begin;
-  if (iters > 0) {
-    if (t_begin < t_end) dma_tile(t_begin, 0);
-    gload(j_begin);
-    if constexpr (BIAS) load_bias(bcur, j_begin);
-    sstore(0);
-    if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-    __syncthreads();
-  }
-  for (int it = 0; it < iters; ++it) {
-    const int j = t_begin + it;
-    const int cur = it & 1;
-    const bool has_tile = KH == 1 || j < t_end;
-    const bool has_next = j + 1 < t_end;
-    if (has_next) {
-      dma_tile(j + 1, cur ^ 1);
-      gload(j + 1);
+  // Logits.  BLDS instances, rows that allow 16-byte loads: tile j+1's go
+  // HBM -> LDS as soon as tile j's are in registers; each wave reads only its
+  // own region, so the tile barrier is not needed for them, and the wait
+  // before it covers them.  BLDS instances, other rows: each tile's are
+  // loaded when it is computed (one register set).  Other instances: tile
+  // j+1's are loaded into registers while tile j is computed.
+  // (whether a wave works on a tile is the same in all its lanes; read from
+  // lane 0 so that the branches on it are scalar)
+  auto active_s = [&](int jj) {
+    const bool a = jj < t_end && wave_has_rows &&
+                   (!CAUSAL || (jj * BN <= wave_pos_max && jj * BN + BN - 1 >= wave_key_lo));
+    return __builtin_amdgcn_readfirstlane(int(a)) != 0;
+  };
+  if (BLDS && p.bias_vec) {
+    if (iters > 0) {
+      dma_tile(t_begin, 0);
+      if (active_s(t_begin)) dma_bias(t_begin);
+      __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+      __syncthreads();
     }
-    // a wave skips tiles above its rows' diagonal and, with a window, tiles
-    // wholly left of its rows' windows
-    const bool active = has_tile && wave_has_rows &&
-                        (!CAUSAL || (j * BN <= wave_pos_max && j * BN + BN - 1 >= wave_key_lo));
-    if constexpr (BIAS) {
-      const bool next_active =
-          has_next && wave_has_rows &&
-          (!CAUSAL || ((j + 1) * BN <= wave_pos_max && (j + 1) * BN + BN - 1 >= wave_key_lo));
-      if (next_active) load_bias(bnext, j + 1);
+    for (int it = 0; it < iters; ++it) {
+      const int j = t_begin + it;
+      const int cur = it & 1;
+      if (j + 1 < t_end) dma_tile(j + 1, cur ^ 1);
+      const bool act = active_s(j);
+      if (act) {
+        read_bias(bcur);
+        // the reads are done before the region is refilled
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      }
+      if (active_s(j + 1)) dma_bias(j + 1);
+      if (act) compute(j, cur);
+      __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+      __syncthreads();
     }
-    if (active) compute(j, cur);
-    if constexpr (BIAS) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) bcur[qb][kb][q4] = bnext[qb][kb][q4];
+  } else {
+    if (iters > 0) {
+      if (t_begin < t_end) dma_tile(t_begin, 0);
+      gload(j_begin);
+      if constexpr (BIAS && !BLDS) load_bias(bcur, j_begin);
+      sstore(0);
+      if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+      __syncthreads();
     }
-    if (has_next) sstore(cur ^ 1);
-    // the direct LDS loads of this wave are done before the barrier publishes them
-    if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-    __syncthreads();
+    for (int it = 0; it < iters; ++it) {
+      const int j = t_begin + it;
+      const int cur = it & 1;
+      const bool has_tile = KH == 1 || j < t_end;
+      const bool has_next = j + 1 < t_end;
+      if (has_next) {
+        dma_tile(j + 1, cur ^ 1);
+        gload(j + 1);
+      }
+      // a wave skips tiles above its rows' diagonal and, with a window, tiles
+      // wholly left of its rows' windows
+      const bool active = has_tile && wave_has_rows &&
+                          (!CAUSAL || (j * BN <= wave_pos_max && j * BN + BN - 1 >= wave_key_lo));
+      if constexpr (BLDS) {
+        if (active) load_bias(bcur, j);
+      } else if constexpr (BIAS) {
+        {
+          const bool next_active =
+              has_next && wave_has_rows &&
+              (!CAUSAL || ((j + 1) * BN <= wave_pos_max && (j + 1) * BN + BN - 1 >= wave_key_lo));
+          if (next_active) load_bias(bnext, j + 1);
+        }
+      }
+      if (active) compute(j, cur);
+      if constexpr (BIAS && !BLDS) {
+        {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) bcur[qb][kb][q4] = bnext[qb][kb][q4];
+        }
+      }
+      if (has_next) sstore(cur ^ 1);
+      // the direct LDS loads of this wave are done before the barrier publishes them
+      if constexpr (VTR) __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+      __syncthreads();
+    }
   }
 
   // ---- KH = 2: merge the second key half's state into the first ---------------
