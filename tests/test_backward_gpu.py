@@ -77,6 +77,11 @@ CASES = [
     # non-causal D = 128 without a logit term: 32-row query tiles, V in LDS
     (1, 4, 2, 97, 200, 128, "bf16", False, False),   # group 2: row tiles cross heads
     (1, 3, 1, 31, 33, 128, "bf16", False, False),    # group 3, rows < one tile, key tail
+    # head sizes 80 and 96 (128-wide LDS rows, last column block partly stored)
+    (1, 2, 2, 150, 170, 80, "bf16", True, False),
+    (1, 4, 2, 97, 200, 96, "fp16", False, False),    # group 2
+    (1, 2, 1, 130, 129, 80, "bf16", False, True),
+    (1, 3, 1, 77, 64, 96, "bf16", True, True),       # group 3, bias
 ]
 
 
@@ -151,6 +156,8 @@ WINDOW_CASES = [
     (2, 2, 2, 513, 513, 64, "fp16", False, 129),
     (1, 5, 1, 64, 64, 64, "bf16", False, 5),          # group 5: row tiles cross heads
     (1, 3, 1, 20, 20, 128, "bf16", False, 6),         # group 3, fewer rows than a tile
+    (1, 2, 2, 200, 200, 96, "bf16", False, 50),
+    (1, 4, 2, 150, 180, 80, "fp16", True, 64),
 ]
 
 

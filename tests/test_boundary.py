@@ -291,8 +291,9 @@ def test_backward_workspace_bytes():
 def test_backward_rejections_before_launch():
     assert bwd_status(dtype=binding.FA_DTYPE_FP32) == 5       # 16-bit types only
     assert bwd_status(D=72) == 4 and bwd_status(q=None) == 1   # the forward's checks first
-    assert bwd_status(D=96) == 4 and bwd_status(D=80) == 4      # forward-only head dims
-    assert bwd_status(D=256) == 4
+    assert bwd_status(D=256) == 4                              # forward-only head dim
+    # 80 and 96 pass the head-size check (the workspace check after it fails)
+    assert bwd_status(D=96, workspace=None) == 11 and bwd_status(D=80, workspace=None) == 11
     assert bwd_status(dout=None) == 1 and bwd_status(dq=None) == 1
     assert bwd_status(dk=None) == 1 and bwd_status(dv=None) == 1
     assert bwd_status(dq=DQ + 8) == 7 and bwd_status(dout=GO + 4) == 7

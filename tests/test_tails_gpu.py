@@ -116,6 +116,8 @@ BWD_CASES = [
     (1, 6, 2, 77, 129, 128, "bf16", True, False, None),
     (1, 4, 2, 300, 333, 64, "bf16", True, False, 100),
     (1, 4, 2, 131, 170, 128, "bf16", False, False, None),
+    (1, 4, 2, 130, 170, 80, "bf16", False, False, None),
+    (1, 4, 2, 77, 129, 96, "fp16", True, True, None),
 ]
 
 

@@ -347,7 +347,7 @@ int backward_common(const void* q, const void* k, const void* v, const void* bia
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;  // 16-bit only
   int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
   if (st != FA_OK) return st;
-  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;   // the backward kernels' tiles
+  if (D != 64 && D != 80 && D != 96 && D != 128) return FA_ERR_HEAD_DIM;  // the backward kernels' tiles
   const int esz = elem_bytes(dtype);
   const bool no_rows = (B == 0 || Hq == 0 || Nq == 0);
   const bool no_keys = (B == 0 || Hkv == 0 || Nk == 0);

@@ -46,6 +46,12 @@ namespace fa {
 namespace {
 
 constexpr int kBwdThreads = 256;  // 4 waves
+// Head sizes 80 and 96 keep the 128-wide LDS row layout of D = 128: the
+// 16-byte chunks past the real row are loaded from an offset past every
+// resource, which reads 0, so they add nothing to the products; the kernels
+// run ceil(D/16) contraction steps and ceil(D/32) output column blocks and
+// store only the real columns.
+constexpr int lds_width(int D) { return (D == 80 || D == 96) ? 128 : D; }
 // dK/dV kernel at D = 64 without a logit term: 3 workgroups per compute unit
 // (168 VGPRs, a small spill) measured 11% faster than 2 (180 VGPRs) on the
 // B2 H16 S4096 causal backward; with a logit term the spill grows, so 2.
@@ -68,14 +74,15 @@ constexpr int kBwdThreads = 256;  // 4 waves
 #ifndef FA_DKDV128_VLDS
 #define FA_DKDV128_VLDS 1
 #endif
+// (D = 80 and 96 take the D = 128 layouts: their LDS rows are 128 wide)
 constexpr bool dkdv_pair(int D, bool causal, bool bias) {  // two workgroups per CU at D = 128
-  return D == 128 && !bias;
+  return D > 64 && !bias;
 }
 constexpr bool dkdv_k_in_lds(int D, bool causal, bool bias) {
-  return D == 128 && !dkdv_pair(D, causal, bias);
+  return D > 64 && !dkdv_pair(D, causal, bias);
 }
 constexpr bool dkdv_v_in_lds(int D, bool causal, bool bias) {
-  return D == 128 && (!dkdv_pair(D, causal, bias) || FA_DKDV128_VLDS);
+  return D > 64 && (!dkdv_pair(D, causal, bias) || FA_DKDV128_VLDS);
 }
 // The instance that runs at 256 VGPRs takes its LDS offsets from two
 // registers (OffsetsLean) rather than from 24: with the table it spilled.
@@ -118,8 +125,9 @@ struct BwdParams {
 // 16 bytes at l*16; off[i] is the lane's source offset within the tile.
 template <int R, int D>
 struct TileLoad {
-  static constexpr int RB = D * 2;
-  static constexpr int CPR = RB / 16;
+  static constexpr int DL = lds_width(D);
+  static constexpr int RB = D * 2;         // bytes per row in HBM
+  static constexpr int CPR = DL * 2 / 16;  // 16-byte chunks per LDS row
   static constexpr int NI = R * CPR / kBwdThreads;
   static_assert(NI * kBwdThreads == R * CPR, "tile must split into whole wave loads");
   int off[NI];
@@ -128,7 +136,8 @@ struct TileLoad {
     for (int i = 0; i < NI; ++i) {
       const int q = (wave * NI + i) * 64 + lane;
       const int row = q / CPR, pc = q % CPR;
-      off[i] = row * RB + ((pc ^ lds_swizzle<D>(row)) * 16);
+      const int c = pc ^ lds_swizzle<DL>(row);  // the HBM chunk this LDS chunk holds
+      off[i] = c < D / 8 ? row * RB + c * 16 : int(0x80000000u);
     }
   }
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* lds, int wave,
@@ -151,23 +160,24 @@ struct TileLoad {
 //    a+8, a+12); t = 0 and t = 1 give the two halves of one MFMA fragment.
 template <int D>
 struct Offsets {
-  static constexpr int RB = D * 2;
-  static constexpr int NS = D / 16;
-  static constexpr int NDB = D / 32;
+  static constexpr int DL = lds_width(D);
+  static constexpr int RB = DL * 2;  // bytes per LDS row
+  static constexpr int NS = (D + 15) / 16;
+  static constexpr int NDB = (D + 31) / 32;
   int row_off[NS];
   int tr_off[2][NDB];
   __device__ __forceinline__ void init(int lane) {
     const int g = lane >> 5, ln = lane & 31;
 #pragma unroll
     for (int st = 0; st < NS; ++st)
-      row_off[st] = ln * RB + (((2 * st + g) ^ lds_swizzle<D>(ln)) * 16);
+      row_off[st] = ln * RB + (((2 * st + g) ^ lds_swizzle<DL>(ln)) * 16);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int r = 8 * t + 4 * g + ((lane >> 2) & 3);
         const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-        tr_off[t][db] = r * RB + ((c ^ lds_swizzle<D>(r)) * 16) + 8 * (lane & 1);
+        tr_off[t][db] = r * RB + ((c ^ lds_swizzle<DL>(r)) * 16) + 8 * (lane & 1);
       }
   }
   __device__ __forceinline__ int row(int st) const { return row_off[st]; }
@@ -182,14 +192,15 @@ struct Offsets {
 // and add 8 rows.  For kernels that run short of registers.
 template <int D>
 struct OffsetsLean {
-  static constexpr int RB = D * 2;
+  static constexpr int DL = lds_width(D);
+  static constexpr int RB = DL * 2;  // bytes per LDS row
   int row0, tr0;
   __device__ __forceinline__ void init(int lane) {
     const int g = lane >> 5, ln = lane & 31;
-    row0 = ln * RB + ((g ^ lds_swizzle<D>(ln)) * 16);
+    row0 = ln * RB + ((g ^ lds_swizzle<DL>(ln)) * 16);
     const int r = 4 * g + ((lane >> 2) & 3);
     const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    tr0 = r * RB + ((c ^ lds_swizzle<D>(r)) * 16) + 8 * (lane & 1);
+    tr0 = r * RB + ((c ^ lds_swizzle<DL>(r)) * 16) + 8 * (lane & 1);
   }
   __device__ __forceinline__ int row(int st) const { return row0 ^ (32 * st); }
   __device__ __forceinline__ int tr(int t, int db) const {
@@ -233,7 +244,7 @@ __device__ __forceinline__ typename Elem<T>::Frag pack_half(const f32x16& x, int
 // of block db = column 32*db + 8*(r/4) + 4*g + r%4) times `mul` as row `row`
 // of a row-major [.., D] tensor: one v_permlane32_swap per word pair gives each
 // lane 8 consecutive columns, written as one 16-byte store.
-template <typename T, int NDB>
+template <typename T, int NDB, int D>
 __device__ __forceinline__ void store_rows(T* dst_row, const f32x16 (&acc)[NDB], float mul,
                                            int g, bool ok) {
 #pragma unroll
@@ -255,7 +266,9 @@ __device__ __forceinline__ void store_rows(T* dst_row, const f32x16 (&acc)[NDB],
         out[e] = r0;
         out[2 + e] = r1;
       }
-      if (ok) *reinterpret_cast<u32x4*>(dst_row + db * 32 + 16 * pr + 8 * g) = out;
+      // (D = 80, 96: the last block's columns past D are not stored)
+      if (ok && (D % 32 == 0 || db * 32 + 16 * pr + 8 * g < D))
+        *reinterpret_cast<u32x4*>(dst_row + db * 32 + 16 * pr + 8 * g) = out;
     }
 }
 
@@ -269,9 +282,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
   using E = Elem<T>;
   using Frag = typename E::Frag;
   constexpr int BN = kKTile;
-  constexpr int NS = D / 16, NDB = D / 32, NKB = BN / 32;
-  constexpr int RB = D * 2;
-  constexpr int TILE = BN * RB;  // bytes per K (or V) tile
+  constexpr int NS = (D + 15) / 16, NDB = (D + 31) / 32, NKB = BN / 32;
+  constexpr int RB = D * 2;                // bytes per row in HBM
+  constexpr int LRB = lds_width(D) * 2;    // bytes per row in LDS
+  constexpr int TILE = BN * LRB;  // bytes per K (or V) tile
   __shared__ __attribute__((aligned(16))) char smem[2][2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -387,12 +401,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const Frag kf = lds_frag<T>(sK + kb * 32 * RB + of.row_off[st]);
+        const Frag kf = lds_frag<T>(sK + kb * 32 * LRB + of.row_off[st]);
         s[kb] = E::mma(kf, qf[st], st == 0 ? f32x16{} : s[kb]);
       }
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const Frag vf = lds_frag<T>(sV + kb * 32 * RB + of.row_off[st]);
+        const Frag vf = lds_frag<T>(sV + kb * 32 * LRB + of.row_off[st]);
         dp[kb] = E::mma(vf, gf[st], st == 0 ? f32x16{} : dp[kb]);
       }
     }
@@ -448,7 +462,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
         const Frag dsf = pack_half<T>(s[kb], h);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const Frag kt = lds_frag_tr<T>(sK + (kb * 32 + 16 * h) * RB, of.tr_off[0][db], of.tr_off[1][db]);
+          const Frag kt = lds_frag_tr<T>(sK + (kb * 32 + 16 * h) * LRB, of.tr_off[0][db], of.tr_off[1][db]);
           acc[db] = E::mma(kt, dsf, acc[db]);
         }
       }
@@ -470,7 +484,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) 
   }
 
   T* dst = static_cast<T*>(p.dq) + (row_base + qi) * D;
-  store_rows<T, NDB>(dst, acc, p.scale, g, row_ok);
+  store_rows<T, NDB, D>(dst, acc, p.scale, g, row_ok);
 }
 
 // ---------------------------------------------------------------------------
@@ -484,12 +498,13 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
   constexpr int BQ = dkdv_qtile(D, CAUSAL, BIAS);
-  constexpr int NS = D / 16, NDB = D / 32, NQB = BQ / 32;
-  constexpr int RB = D * 2;
-  constexpr int TILE = BQ * RB;               // bytes per Q (or dO) tile
+  constexpr int NS = (D + 15) / 16, NDB = (D + 31) / 32, NQB = BQ / 32;
+  constexpr int RB = D * 2;                   // bytes per row in HBM
+  constexpr int LRB = lds_width(D) * 2;       // bytes per row in LDS
+  constexpr int TILE = BQ * LRB;              // bytes per Q (or dO) tile
   constexpr bool K_LDS = dkdv_k_in_lds(D, CAUSAL, BIAS);  // the block's K in LDS, else registers
   constexpr bool V_LDS = dkdv_v_in_lds(D, CAUSAL, BIAS);  // the block's V in LDS, else registers
-  constexpr int KB_BYTES = 128 * RB;                        // bytes of the block's K (or V)
+  constexpr int KB_BYTES = 128 * LRB;                       // bytes of the block's K (or V)
   // per stage: Q tile, dO tile, lse2[BQ], delta[BQ]
   constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
   constexpr int KV_BYTES = (K_LDS ? KB_BYTES : 0) + (V_LDS ? KB_BYTES : 0);
@@ -616,14 +631,14 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       f32x16 s, dp;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const Frag qa = lds_frag<T>(sQ + qb * 32 * RB + ofs.row(st));
-        const Frag kb = K_LDS ? lds_frag<T>(sK + wave * 32 * RB + ofs.row(st)) : kf[st];
+        const Frag qa = lds_frag<T>(sQ + qb * 32 * LRB + ofs.row(st));
+        const Frag kb = K_LDS ? lds_frag<T>(sK + wave * 32 * LRB + ofs.row(st)) : kf[st];
         s = E::mma(qa, kb, st == 0 ? f32x16{} : s);
       }
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const Frag ga = lds_frag<T>(sG + qb * 32 * RB + ofs.row(st));
-        const Frag vb = V_LDS ? lds_frag<T>(sV + wave * 32 * RB + ofs.row(st)) : vf[st];
+        const Frag ga = lds_frag<T>(sG + qb * 32 * LRB + ofs.row(st));
+        const Frag vb = V_LDS ? lds_frag<T>(sV + wave * 32 * LRB + ofs.row(st)) : vf[st];
         dp = E::mma(ga, vb, st == 0 ? f32x16{} : dp);
       }
       // register r: query row qb*32 + 8*(r/4) + 4*g + r%4 of the tile, key kj
@@ -675,9 +690,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         const Frag dsf = pack_half<T>(dp, h);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const Frag gt = lds_frag_tr<T>(sG + (qb * 32 + 16 * h) * RB, ofs.tr(0, db), ofs.tr(1, db));
+          const Frag gt = lds_frag_tr<T>(sG + (qb * 32 + 16 * h) * LRB, ofs.tr(0, db), ofs.tr(1, db));
           dva[db] = E::mma(gt, pf, dva[db]);
-          const Frag qt = lds_frag_tr<T>(sQ + (qb * 32 + 16 * h) * RB, ofs.tr(0, db), ofs.tr(1, db));
+          const Frag qt = lds_frag_tr<T>(sQ + (qb * 32 + 16 * h) * LRB, ofs.tr(0, db), ofs.tr(1, db));
           dka[db] = E::mma(qt, dsf, dka[db]);
         }
       }
@@ -709,8 +724,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const bool key_ok = kj < p.Nk;
   T* dk_row = static_cast<T*>(p.dk) + (kv_head * p.Nk + kj) * D;
   T* dv_row = static_cast<T*>(p.dv) + (kv_head * p.Nk + kj) * D;
-  store_rows<T, NDB>(dk_row, dka, p.scale, g, key_ok);
-  store_rows<T, NDB>(dv_row, dva, 1.f, g, key_ok);
+  store_rows<T, NDB, D>(dk_row, dka, p.scale, g, key_ok);
+  store_rows<T, NDB, D>(dv_row, dva, 1.f, g, key_ok);
 }
 
 template <typename T, int D>
@@ -778,12 +793,19 @@ int launch_backward(const BwdArgs& a) {
   const unsigned g_kv = unsigned(p.n_kblk) * unsigned(p.BHkv);
   hipStream_t s = static_cast<hipStream_t>(a.stream);
   hipError_t e;
+  auto launch = [&](auto tag) {
+    using T = decltype(tag);
+    switch (a.D) {
+      case 64: return launch_bwd_d<T, 64>(p, a.causal, a.bias, s, g_dq, g_kv);
+      case 80: return launch_bwd_d<T, 80>(p, a.causal, a.bias, s, g_dq, g_kv);
+      case 96: return launch_bwd_d<T, 96>(p, a.causal, a.bias, s, g_dq, g_kv);
+      default: return launch_bwd_d<T, 128>(p, a.causal, a.bias, s, g_dq, g_kv);
+    }
+  };
   if (a.dtype == FA_DTYPE_BF16) {
-    e = a.D == 64 ? launch_bwd_d<__bf16, 64>(p, a.causal, a.bias, s, g_dq, g_kv)
-                  : launch_bwd_d<__bf16, 128>(p, a.causal, a.bias, s, g_dq, g_kv);
+    e = launch(__bf16{});
   } else {
-    e = a.D == 64 ? launch_bwd_d<_Float16, 64>(p, a.causal, a.bias, s, g_dq, g_kv)
-                  : launch_bwd_d<_Float16, 128>(p, a.causal, a.bias, s, g_dq, g_kv);
+    e = launch(_Float16{});
   }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
