@@ -43,7 +43,14 @@ def run_backward(q, k, v, bias, dout, scale, causal):
     return dq, dk, dv
 
 
-def compare(got, ref, dtype, what):
+def compare(got, ref, dtype, what, atol=0.0):
+    """Relative bars of the module docstring.  A gradient tensor that the
+    definition makes zero by cancellation (every row sees one key: P = 1 and
+    O = v, so dP - D_i = dO.v - dO.O is exactly 0 in the oracle) is instead
+    held to the absolute bound ``atol``: the kernel forms dP (matrix cores) and
+    D_i (from the rounded O) as two fp32 sums of D products, each off by up to
+    about D 2^-24 sum_d |dO_d v_d|, and dQ and dK carry that times scale |K| or
+    scale |Q|.  That applies only when the whole reference lies within atol."""
     mx_tol, mean_tol = TOL[dtype]
     out = {}
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
@@ -54,10 +61,22 @@ def compare(got, ref, dtype, what):
         scale_mean = max(np.abs(r).mean() if r.size else 0.0, 1e-30)
         out[name] = (float(err.max(initial=0.0) / scale_max),
                      float(err.mean() / scale_mean) if r.size else 0.0)
+        if np.abs(r).max(initial=0.0) <= atol:
+            assert err.max(initial=0.0) <= atol, f"{what} {name} max abs {err.max()} > {atol}"
+            continue
         assert err.max(initial=0.0) <= mx_tol * scale_max, f"{what} {name} max {out[name]}"
         if r.size:
             assert err.mean() <= mean_tol * scale_mean, f"{what} {name} mean {out[name]}"
     return out
+
+
+def cancellation_floor(q, k, v, dout, scale):
+    """The absolute floor of ``compare`` for these inputs: 2 D 2^-24 max|dO|
+    max|V| D (the two sums' rounding, with |sum| <= D max|dO| max|V|) times
+    scale max(|K|, |Q|)."""
+    D = q.shape[-1]
+    m = lambda t: float(t.abs().max()) if t.numel() else 0.0
+    return 2.0 * D * 2.0 ** -24 * D * m(dout) * m(v) * abs(scale) * max(m(k), m(q))
 
 
 CASES = [

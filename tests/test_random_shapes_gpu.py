@@ -1,4 +1,5 @@
-"""Seeded random sweep of the forward entry points against the oracle.
+"""Seeded random sweep of the forward entry points, and of the backward,
+against the oracle.
 
 Each case draws a shape (batch, query heads, KV-head group, query and key
 counts with ragged tails), an element type, a head dimension, the causal flag,
@@ -62,3 +63,44 @@ def test_random_case(gpu_device, case):
         assert_within(errors(f64(o), lse.cpu().numpy(), o_ref, l_ref), dt, str(case))
     else:
         full_check(q, k, v, b, w.scale, causal, dt, str(case))
+
+
+def _backward_cases(n=24, seed=4048):
+    r = random.Random(seed)
+    out = []
+    while len(out) < n:
+        dtype = r.choice(["bf16", "bf16", "fp16"])
+        D = r.choice([64, 80, 96, 128])
+        window = r.choice([None, None, None, 1, 16, 100])
+        causal = window is not None or r.random() < 0.5
+        bias = r.random() < 0.3
+        hkv = r.choice([1, 2, 3])
+        group = r.choice([1, 2, 5])
+        nq = r.choice([1, 7, 64, 127, 200, 333])
+        nk = r.choice([1, 63, 64, 65, 190, 400]) if not causal else r.choice([nq, nq + 17, 300])
+        out.append((r.choice([1, 2]), hkv * group, hkv, nq, nk, D, dtype, causal, bias, window))
+    return out
+
+
+@pytest.mark.parametrize("case", _backward_cases(), ids=lambda c: "-".join(map(str, c)))
+def test_random_backward_case(gpu_device, case):
+    """The same kind of sweep for fa_backward (and its window form): dQ, dK and
+    dV against the oracle's gradients at the bars of test_backward_gpu."""
+    from oracle import attention_backward
+    from tests.parity import f64
+    from tests.test_backward_gpu import cancellation_floor, compare
+    B, Hq, Hkv, Nq, Nk, D, dt, causal, bias, window = case
+    print(f"random backward case {case}", flush=True)
+    w = custom(B, Hq, Hkv, Nq, Nk, D, dt, causal, bias)
+    seed = zlib.crc32(repr(case).encode()) % 100000
+    q, k, v, b = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=seed))
+    g = torch.Generator().manual_seed(seed + 1)
+    dout = torch.randn(q.shape, generator=g).to(q.dtype).to(gpu_device)
+    o, lse = binding.forward(q, k, v, b, causal=causal, scale=w.scale, window=window)
+    dq, dk, dv = binding.backward(q, k, v, o, lse, dout, b, causal=causal, scale=w.scale,
+                                  window=window)
+    torch.cuda.synchronize()
+    refs = attention_backward(f64(q), f64(k), f64(v), f64(dout), None if b is None else f64(b),
+                              scale=w.scale, causal=causal, window=window)
+    atol = cancellation_floor(q, k, v, dout, w.scale)
+    print(compare((dq, dk, dv), refs, dt, str(case), atol=atol), flush=True)
