@@ -918,7 +918,7 @@ void fa_fwd_kernel(Params p) {
   int t_begin = j_begin, t_end = j_end;
   if constexpr (KH == 2) {
     const int mid = j_begin + (j_end - j_begin) / 2;
-    if (half == 0) t_end = mid;
+    if (half_s == 0) t_end = mid;
     else t_begin = mid;
   }
   const int iters = KH == 2 ? (j_end - j_begin + 1) / 2 : j_end - j_begin;
