@@ -55,8 +55,10 @@ extern "C" {
  * of "FlashAttention principles and Triton practice" (xnwp.cn/news/15505), §7,
  * which asks for its precision loss to be evaluated: the probabilities are
  * rounded to E4M3 for the P.V product (the other arithmetic as for 16-bit
- * inputs).  fa_forward only (fused, with or without the causal mask), D = 64
- * or 128; the other entry points return FA_ERR_DTYPE for it. */
+ * inputs).  fa_forward (fused) and the key-split entry points (fa_forward_split,
+ * fa_forward_split_noalloc: the decode step over an FP8 KV cache), with or
+ * without the causal mask, D = 64 or 128; the other entry points return
+ * FA_ERR_DTYPE for it. */
 typedef enum fa_dtype {
   FA_DTYPE_BF16 = 0,
   FA_DTYPE_FP16 = 1,
@@ -173,7 +175,8 @@ int fa_forward_chain(const void* const* q_layers, const void* const* k_layers,
  *     heads that share a KV head are packed into one row space of
  *     (Hq/Hkv)*Nq rows, so a decode step with Nq = 1 still fills row blocks;
  *  2. fa_merge's kernel combines the num_splits partials of every row into o
- *     (dtype) and lse with the merge of the kwkr.cn/news/592482 tutorial,
+ *     (dtype; bf16 for FP8 inputs) and lse with the merge of the
+ *     kwkr.cn/news/592482 tutorial,
  *     §2.2 (closing remarks there name flash decode as an extension of the
  *     fused kernel).
  * Results equal fa_forward's up to float32 rounding order.  All conventions of

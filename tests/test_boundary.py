@@ -236,13 +236,17 @@ def test_split_noalloc_rejections_before_launch():
     assert noalloc_status(D=72) == 4 and noalloc_status(D=256) == 4
     assert noalloc_status(q=None) == 1 and noalloc_status(o=O + 8) == 7
     assert noalloc_status(o=Q) == 8
-    assert noalloc_status(dtype=binding.FA_DTYPE_FP8_E4M3) == 5
+    # FP8 is accepted (the decode step over an FP8 KV cache): the scratch
+    # limit is what stops this call, not the type; FP8 with a bias is refused
+    fp8 = binding.FA_DTYPE_FP8_E4M3
+    assert noalloc_status(dtype=fp8, bias=BIAS) == 5 and noalloc_status(dtype=fp8, D=80) == 4
     # just over the limit: rows * D * 4 * splits (plus the LSE part) > 32 MiB
     limit = binding.FA_SPLIT_SCRATCH_BYTES
     rows = 2 * 4 * 100
     over = limit // (rows * 64 * 4) + 1
     assert binding.fa_split_workspace_bytes(2, 4, 100, 64, over) > limit
     assert noalloc_status(num_splits=over) == binding.FA_ERR_SCRATCH_LIMIT
+    assert noalloc_status(num_splits=over, dtype=fp8) == binding.FA_ERR_SCRATCH_LIMIT
     assert noalloc_status(B=64, Hq=32, Hkv=32, Nq=4096, num_splits=1) == 12
     assert "scratch" in binding.fa_status_string(12)
     # empty problem: nothing launched
@@ -362,7 +366,11 @@ def test_fp8_rejections_before_launch():
     args = (a["q"], a["k"], a["v"], None, a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
             a["Nq"], a["Nk"], a["D"], a["scale"])
     assert lib.fa_forward_window(*args, 16, fp8, None) == 5
-    assert lib.fa_forward_split(*args, 1, fp8, 2, WS, 1 << 40, None) == 5
+    # the key split takes FP8 (no bias): past the type check, a missing
+    # workspace is what fails
+    assert lib.fa_forward_split(*args, 1, fp8, 2, None, 0, None) == 11
+    bias_args = args[:3] + (BIAS,) + args[4:]
+    assert lib.fa_forward_split(*bias_args, 1, fp8, 2, WS, 1 << 40, None) == 5
     bargs = (a["q"], a["k"], a["v"], None, a["o"], a["lse"], GO, DQ, DK, DV, a["B"], a["Hq"],
              a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"])
     assert lib.fa_backward(*bargs, 1, fp8, WS, 1 << 40, None) == 5

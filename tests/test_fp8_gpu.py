@@ -68,8 +68,10 @@ def test_fp8_rejections(gpu_device):
     q, k, v, b = (t.to(gpu_device) for t in make_inputs(w, seed=53))
     with pytest.raises(binding.FaError):          # no logit term with FP8
         binding.forward(q, k, v, b)
-    with pytest.raises(binding.FaError):          # fused forward only
-        binding.forward_split(q, k, v, None, num_splits=2)
+    with pytest.raises(binding.FaError):          # nor on the key-split path
+        binding.forward_split(q, k, v, b, num_splits=2)
+    with pytest.raises(binding.FaError):          # no window with FP8
+        binding.forward(q, k, v, None, causal=True, window=16)
 
 
 def test_fp8_full_size_sampled(gpu_device):
@@ -94,5 +96,52 @@ def test_fp8_full_size_sampled(gpu_device):
              f"worst err/bound {(err / bound).max():.2f}")
         assert np.all(err <= bound)
         assert np.abs(lse[b, h, rows_t].cpu().numpy() - l_ref).max() <= 1e-3
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
+SPLIT_CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, causal, splits
+    (1, 8, 2, 1, 1000, 128, False, 4),     # a decode step, 4 query heads per KV head
+    (2, 4, 1, 1, 333, 64, False, 3),
+    (1, 4, 2, 150, 333, 64, True, 3),
+    (1, 2, 2, 200, 517, 128, True, 5),
+    (1, 2, 2, 64, 64, 64, False, 16),      # more splits than key tiles
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_fp8_key_split_within_bound(gpu_device, case):
+    """The key-split path with FP8 inputs (the decode step over an FP8 KV cache):
+    each split rounds its own P to E4M3 against its own reference max, so the
+    bound of the fused FP8 check applies to every split's part of the row, and
+    the merge of the fp32 partials adds only float32 rounding."""
+    B, Hq, Hkv, Nq, Nk, D, causal, splits = case
+    w = custom(B, Hq, Hkv, Nq, Nk, D, "fp8", causal, False)
+    _log(f"fp8 split case {case}")
+    q, k, v, _ = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=54))
+    o, lse = binding.forward_split(q, k, v, None, causal=causal, scale=w.scale,
+                                   num_splits=splits)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    mx, mean, ratio = fp8_bound_check(q, k, v, w.scale, causal, o, lse, str(case))
+    _log(f"  max {mx:.2e} mean {mean:.2e} worst err/bound {ratio:.2f}")
+    on, ln = binding.forward_split_noalloc(q, k, v, None, causal=causal, scale=w.scale,
+                                           num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(on, o) and torch.equal(ln, lse)   # same kernels, same partials
+
+
+def test_fp8_decode_full_size(gpu_device):
+    """The decode workload with an FP8 KV cache (B8, 20/4 heads, Nq 1, Nk 32768,
+    D 128), every row against the oracle within the FP8 bound."""
+    from tiled_attention_forward_amd.workloads import WORKLOADS
+    w = WORKLOADS["decode_b8_hq20_hkv4_nq1_nk32768_d128_fp8"]
+    _log("full-size fp8 decode")
+    q, k, v, _ = make_inputs(w, seed=0, device=gpu_device)
+    o, lse = binding.forward_split(q, k, v, None, causal=False, scale=w.scale)
+    torch.cuda.synchronize()
+    mx, mean, ratio = fp8_bound_check(q, k, v, w.scale, False, o, lse, w.name)
+    _log(f"  max {mx:.2e} mean {mean:.2e} worst err/bound {ratio:.2f}")
     del q, k, v, o, lse
     torch.cuda.empty_cache()

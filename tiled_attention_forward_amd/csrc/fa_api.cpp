@@ -233,7 +233,6 @@ int split_common(const void* q, const void* k, const void* v, const void* bias, 
                  float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                  int64_t D, float scale, int causal, int dtype, int64_t num_splits,
                  void* stream, fa::LaunchArgs* a, int64_t* need) {
-  if (dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_DTYPE;  // fused FP8 forward only
   if (D == 256) return FA_ERR_HEAD_DIM;                 // fused forward only
   int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
   if (st != FA_OK) return st;
@@ -278,14 +277,16 @@ extern "C" int fa_forward_split(const void* q, const void* k, const void* v, con
   if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need)
     return FA_ERR_WORKSPACE;
   const int esz = elem_bytes(dtype);
+  const int oesz = dtype == FA_DTYPE_FP8_E4M3 ? 2 : esz;  // FP8 inputs give a bf16 o
   const int64_t rows = B * Hq * Nq;
   const uint64_t nq_b = uint64_t(rows) * D * esz;
+  const uint64_t no_b = uint64_t(rows) * D * oesz;
   const uint64_t nkv_b = uint64_t(B) * Hkv * Nk * D * esz;
   const uint64_t nb_b = bias ? uint64_t(rows) * Nk * esz : 0;
   const uint64_t nl_b = uint64_t(rows) * 4;
   if (overlap(workspace, need, q, nq_b) || overlap(workspace, need, k, nkv_b) ||
       overlap(workspace, need, v, nkv_b) || overlap(workspace, need, bias, nb_b) ||
-      overlap(workspace, need, o, nq_b) || overlap(workspace, need, lse, nl_b))
+      overlap(workspace, need, o, no_b) || overlap(workspace, need, lse, nl_b))
     return FA_ERR_OVERLAP;
   return fa::launch_forward_split(a, int(num_splits), workspace);
 }

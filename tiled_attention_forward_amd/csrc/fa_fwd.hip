@@ -234,7 +234,7 @@ void fa_fwd_kernel(Params p) {
   static_assert(VTR || KCH * kThreads * VEC == BN * D, "K tile must split evenly");
   static_assert(NL >= 1 && NL <= kMaxChainLayers, "chain length");
   static_assert(NL == 1 || (VTR && !BIAS && !SPLIT && !WINDOW), "chain instances");
-  static_assert(!F8 || (NL == 1 && !BIAS && !SPLIT && !WINDOW && D == DL), "FP8 instances");
+  static_assert(!F8 || (NL == 1 && !BIAS && !WINDOW && D == DL && BN == 64), "FP8 instances");
   static_assert(KH == 1 || (KH == 2 && VTR && NL == 1 && !SPLIT && !BIAS), "key-half instances");
   // FP8: P is stored as e4m3 for the P.V product.  It is taken as
   // 2^(t - m_ref + 7) with the rescale threshold at 1, so every p lies in
@@ -1409,13 +1409,23 @@ hipError_t launch_f8(const Params& p, unsigned grid, hipStream_t s, int D, bool 
                 : launch_one<F8, 128, 64, 1, false, false, false>(p, grid, s);
 }
 
+// FP8 key split (the decode step over an FP8 KV cache): 64-key tiles, fp32
+// partials like the 16-bit instances; the merge writes a bf16 O.
+hipError_t launch_f8_split(const Params& p, unsigned grid, hipStream_t s, int D, bool causal) {
+  using F8 = fp8e4m3;
+  if (D == 64)
+    return causal ? launch_one<F8, 64, 64, 1, true, false, true>(p, grid, s)
+                  : launch_one<F8, 64, 64, 1, false, false, true>(p, grid, s);
+  return causal ? launch_one<F8, 128, 64, 1, true, false, true>(p, grid, s)
+                : launch_one<F8, 128, 64, 1, false, false, true>(p, grid, s);
+}
+
 template <bool SPLIT>
 hipError_t dispatch(const Params& p, unsigned grid, const LaunchArgs& a) {
   hipStream_t s = static_cast<hipStream_t>(a.stream);
   const bool bias = a.bias != nullptr;
-  if constexpr (!SPLIT) {
-    if (a.dtype == FA_DTYPE_FP8_E4M3) return launch_f8(p, grid, s, a.D, a.causal);
-  }
+  if (a.dtype == FA_DTYPE_FP8_E4M3)
+    return SPLIT ? launch_f8_split(p, grid, s, a.D, a.causal) : launch_f8(p, grid, s, a.D, a.causal);
   switch (a.dtype) {
     case FA_DTYPE_BF16: return launch_t<__bf16, SPLIT>(p, grid, s, a.D, a.causal, bias);
     case FA_DTYPE_FP16: return launch_t<_Float16, SPLIT>(p, grid, s, a.D, a.causal, bias);
@@ -1491,7 +1501,9 @@ int launch_forward_split(const LaunchArgs& a, int n_splits, void* workspace) {
   p.part_rows = part_rows;
   const unsigned grid = unsigned(p.n_qtiles) * unsigned(n_splits) * unsigned(a.B * a.Hkv);
   if (dispatch<true>(p, grid, pa) != hipSuccess) return FA_ERR_HIP;
-  return merge(part_o, part_lse, n_splits, part_rows, a.D, a.o, a.lse, a.dtype,
+  // (FP8 inputs give a bf16 O)
+  const int out_dtype = a.dtype == FA_DTYPE_FP8_E4M3 ? int(FA_DTYPE_BF16) : a.dtype;
+  return merge(part_o, part_lse, n_splits, part_rows, a.D, a.o, a.lse, out_dtype,
                static_cast<hipStream_t>(a.stream)) == hipSuccess
              ? FA_OK
              : FA_ERR_HIP;

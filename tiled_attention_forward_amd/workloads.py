@@ -30,6 +30,7 @@ are drawn layer by layer (Q_l, then K_l, oldest layer first), then V.  The
 FP8 shape is the benchmark report shape with Q, K and V rounded to E4M3.  The
 report shape with a dense logit term (D = 64) measures the bias path at the
 head size where the softmax, not the matrix products, bounds the kernel.  The
+decode shape also runs with an FP8 (E4M3) KV cache: half the bytes to stream.  The
 causal variant of the tutorial's shape is the common training case at D = 128
 (causal, no logit term), timed for the backward.
 """
@@ -121,6 +122,8 @@ WORKLOADS = {
         Workload("b2_h16_s4096_d64_bf16_causal_bias", 2, 16, 16, 4096, 4096, 64, "bf16", True,
                  True),
         Workload("decode_b8_hq20_hkv4_nq1_nk32768_d128_bf16", 8, 20, 4, 1, 32768, 128, "bf16",
+                 False, False, "split"),
+        Workload("decode_b8_hq20_hkv4_nq1_nk32768_d128_fp8", 8, 20, 4, 1, 32768, 128, "fp8",
                  False, False, "split"),
         Workload("b1_h2_s16384_d64_bf16", 1, 2, 2, 16384, 16384, 64, "bf16", False, False,
                  "split"),
