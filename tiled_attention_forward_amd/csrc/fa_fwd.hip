@@ -100,6 +100,19 @@ constexpr int kBN64 = FA_BN64;         // keys per K/V tile, D = 64
 constexpr int kBN128 = FA_BN128;       // keys per K/V tile, D = 128
 constexpr int kQB64 = FA_QB64;         // 32-row query blocks per wave, D = 64
 constexpr int kQB128 = FA_QB128;       // 32-row query blocks per wave, D = 128
+// 16-bit fused non-causal instances at D = 128 without a bias: two 32-row
+// query blocks per wave over 32-key tiles (256 VGPRs; the 24-byte spill is
+// the prologue's and the epilogue's, none in the loop), which halves the LDS
+// operand reads per MFMA.  The causal instance would spill inside its loop
+// and keeps one block over 64-key tiles.
+#ifndef FA_QB128N
+#define FA_QB128N 2
+#endif
+#ifndef FA_BN128N
+#define FA_BN128N 32
+#endif
+constexpr int kQB128N = FA_QB128N;
+constexpr int kBN128N = FA_BN128N;
 constexpr float kTau = 8.f;            // lazy-rescale threshold (log2 units)
 static_assert(kWaves * 32 >= kRowsPerBlock,
               "grid-size validation assumes at least this block height");
@@ -1318,12 +1331,14 @@ hipError_t launch_d256(const Params& p, unsigned grid, hipStream_t s, bool causa
 }
 
 // 32-row query blocks per wave.  Two blocks (64 rows) halve the K/V operand
-// reads per MFMA, but only fit in registers for 16-bit inputs with D = 64 and
-// no bias tile; every other instance keeps one.  The key-split path keeps one.
-constexpr int query_blocks(int dtype, int D, bool bias, bool split) {
+// reads per MFMA; they fit in registers only for 16-bit inputs without a bias
+// tile, at D = 64 and (non-causal, 32-key tiles) at D = 128.  Every other
+// instance keeps one, and so does the key-split path.
+constexpr int query_blocks(int dtype, int D, bool bias, bool split, bool causal) {
   return split ? 1
                : dtype == FA_DTYPE_FP8_E4M3                   ? 1
                : (dtype != FA_DTYPE_FP32 && D == 64 && !bias) ? kQB64
+               : (dtype != FA_DTYPE_FP32 && D == 128 && !bias && !causal) ? kQB128N
                : (D == 128) ? kQB128 : 1;
 }
 
@@ -1358,6 +1373,9 @@ hipError_t launch_t(const Params& p, unsigned grid, hipStream_t s, int D, bool c
     return bias ? launch_one<T, 128, kBN128, 1, false, true, true>(p, grid, s)
                 : launch_one<T, 128, BS, 1, false, false, true>(p, grid, s);
   } else {
+    if constexpr (!std::is_same<T, float>::value) {
+      if (!bias && !causal) return launch_one<T, 128, kBN128N, kQB128N, false, false, false>(p, grid, s);
+    }
     return launch_d<T, 128, kBN128, kQB128, SPLIT>(p, grid, s, causal, bias);
   }
 }
@@ -1481,7 +1499,7 @@ hipError_t merge(const float* part_o, const float* part_lse, int n_parts, int64_
 }  // namespace
 
 int launch_forward(const LaunchArgs& a) {
-  const int bm = kWaves * 32 * query_blocks(a.dtype, a.D, a.bias != nullptr, false);
+  const int bm = kWaves * 32 * query_blocks(a.dtype, a.D, a.bias != nullptr, false, a.causal);
   const Params p = make_params(a, bm, a.Nq);
   const unsigned grid = unsigned(p.n_qtiles) * unsigned(p.BH);
   return dispatch<false>(p, grid, a) == hipSuccess ? FA_OK : FA_ERR_HIP;
