@@ -61,6 +61,16 @@ EDGE = [
     (1, 2, 1, 517, 333, 96, "bf16", True, False),
     (1, 1, 1, 1, 1, 80, "bf16", False, False),
     (1, 2, 2, 130, 70, 96, "bf16", False, False),
+    # D = 128, non-causal, no bias: two 32-row query blocks per wave (256 rows
+    # per workgroup) over 32-key tiles; row counts around the 32-, 64- and
+    # 256-row boundaries, key counts around the 32-key tile
+    (1, 2, 2, 1, 33, 128, "bf16", False, False),
+    (1, 2, 1, 33, 31, 128, "fp16", False, False),
+    (1, 4, 2, 65, 200, 128, "bf16", False, False),
+    (2, 3, 3, 255, 257, 128, "bf16", False, False),
+    (1, 2, 2, 257, 1, 128, "fp16", False, False),
+    (1, 5, 1, 300, 333, 128, "bf16", False, False),
+    (1, 2, 2, 513, 64, 128, "bf16", False, False),
     # head dim 256: 32-key tiles
     (1, 2, 2, 300, 300, 256, "bf16", True, False),
     (1, 4, 2, 257, 190, 256, "fp16", False, False),

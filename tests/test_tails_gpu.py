@@ -74,6 +74,9 @@ FWD_CASES = [
     ("fused", 1, 4, 2, 130, 200, 128, "bf16", False, True, None),
     ("fused", 1, 4, 2, 97, 136, 96, "fp16", True, True, None),
     ("fused", 1, 4, 2, 130, 70, 128, "fp16", False, True, None),
+    # two 32-row query blocks per wave (D = 128, non-causal, no bias)
+    ("fused", 1, 4, 2, 300, 333, 128, "bf16", False, False, None),
+    ("fused", 1, 4, 2, 65, 31, 128, "fp16", False, False, None),
     ("fused", 1, 4, 2, 97, 161, 80, "bf16", True, False, None),
     ("fused", 1, 4, 2, 75, 100, 64, "fp32", True, True, None),
     ("fused", 1, 4, 2, 100, 90, 256, "bf16", True, False, None),
