@@ -77,9 +77,9 @@ typedef enum fa_status {
                            /* forward-only sizes run in 128-wide tiles, per the xnwp.cn  */
                            /* post, §5.1 and §6.4: a block narrower than the head drops  */
                            /* or misreads columns), nor 256 with bf16/fp16 in fa_forward */
-                           /* (fused, no window); the backward and the residual chain    */
-                           /* take 64 and 128.  Other sizes are rejected, never silently  */
-                           /* truncated                                                  */
+                           /* (fused, no window); the residual chain takes 64 and 128,   */
+                           /* the backward 64, 80, 96, 128 and 256 (256 without a logit  */
+                           /* term).  Other sizes are rejected, never silently truncated */
   FA_ERR_DTYPE = 5,        /* dtype is not one of fa_dtype                               */
   FA_ERR_SCALE = 6,        /* scale is NaN or infinite                                   */
   FA_ERR_ALIGNMENT = 7,    /* a tensor pointer is not aligned as required above          */
@@ -295,8 +295,8 @@ int fa_merge(const float* part_o, const float* part_lse, int64_t num_parts, int6
  *   workspace: device scratch owned by the caller, 16-byte aligned, at least
  *     fa_backward_workspace_bytes(B, Hq, Nq) bytes; holds D_i and LSE_i*log2(e)
  *     (float32) on return.  NULL is allowed when B*Hq*Nq == 0.
- * bf16 and fp16 only (FA_ERR_DTYPE for fp32); head sizes 64, 80, 96 and 128
- * (FA_ERR_HEAD_DIM for 256).  Products run on the matrix
+ * bf16 and fp16 only (FA_ERR_DTYPE for fp32); head sizes 64, 80, 96, 128, and
+ * 256 without a logit term (FA_ERR_HEAD_DIM for 256 with one).  Products run on the matrix
  * cores with float32 accumulation; P and dS are rounded to the input type
  * before their products, as P is in the forward.  Results are deterministic
  * (no atomics: dQ has its own kernel).  Errors as for fa_forward, plus
@@ -316,7 +316,8 @@ int fa_backward(const void* q, const void* k, const void* v, const void* bias,
 
 /*
  * Backward of fa_forward_window: as fa_backward, with causal = 1 and the same
- * window (window >= 1, FA_ERR_BAD_SIZE otherwise).
+ * window (window >= 1, FA_ERR_BAD_SIZE otherwise); no D = 256
+ * (FA_ERR_HEAD_DIM), as for fa_forward_window.
  */
 int fa_backward_window(const void* q, const void* k, const void* v, const void* bias,
                        const void* o, const float* lse, const void* dout,

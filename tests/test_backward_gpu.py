@@ -101,6 +101,11 @@ CASES = [
     (1, 4, 2, 97, 200, 96, "fp16", False, False),    # group 2
     (1, 2, 1, 130, 129, 80, "bf16", False, True),
     (1, 3, 1, 77, 64, 96, "bf16", True, True),       # group 3, bias
+    # head size 256 (no logit term): 32-key dQ tiles, dK/dV in two column passes
+    (1, 2, 2, 150, 170, 256, "bf16", True, False),
+    (1, 4, 2, 97, 200, 256, "fp16", False, False),   # group 2: row tiles cross heads
+    (1, 3, 1, 33, 31, 256, "bf16", True, False),     # group 3, rows < one tile, key tail
+    (1, 2, 2, 300, 129, 256, "bf16", False, False),
 ]
 
 

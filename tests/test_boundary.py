@@ -295,7 +295,8 @@ def test_backward_workspace_bytes():
 def test_backward_rejections_before_launch():
     assert bwd_status(dtype=binding.FA_DTYPE_FP32) == 5       # 16-bit types only
     assert bwd_status(D=72) == 4 and bwd_status(q=None) == 1   # the forward's checks first
-    assert bwd_status(D=256) == 4                              # forward-only head dim
+    assert bwd_status(D=256, bias=BIAS) == 4                   # D = 256 takes no logit term
+    assert bwd_status(D=256, workspace=None) == 11             # D = 256 passes the head check
     # 80 and 96 pass the head-size check (the workspace check after it fails)
     assert bwd_status(D=96, workspace=None) == 11 and bwd_status(D=80, workspace=None) == 11
     assert bwd_status(dout=None) == 1 and bwd_status(dq=None) == 1
@@ -327,6 +328,8 @@ def test_window_rejections_before_launch():
              a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"])
     assert lib.fa_backward_window(*bargs, 0, a["dtype"], WS, 1 << 40, None) == 2
     assert lib.fa_backward_window(*bargs, 8, binding.FA_DTYPE_FP32, WS, 1 << 40, None) == 5
+    assert lib.fa_backward_window(*bargs[:15], 256, a["scale"], 8, a["dtype"], WS, 1 << 40,
+                                  None) == 4   # no window at D = 256, as in the forward
 
 
 def test_chain_rejections_before_launch():

@@ -121,6 +121,7 @@ BWD_CASES = [
     (1, 4, 2, 131, 170, 128, "bf16", False, False, None),
     (1, 4, 2, 130, 170, 80, "bf16", False, False, None),
     (1, 4, 2, 77, 129, 96, "fp16", True, True, None),
+    (1, 4, 2, 131, 170, 256, "bf16", True, False, None),
 ]
 
 

@@ -348,7 +348,8 @@ int backward_common(const void* q, const void* k, const void* v, const void* bia
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;  // 16-bit only
   int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
   if (st != FA_OK) return st;
-  if (D != 64 && D != 80 && D != 96 && D != 128) return FA_ERR_HEAD_DIM;  // the backward kernels' tiles
+  if (D != 64 && D != 80 && D != 96 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;  // the backward kernels' tiles
+  if (D == 256 && bias != nullptr) return FA_ERR_HEAD_DIM;  // D = 256: no logit term
   const int esz = elem_bytes(dtype);
   const bool no_rows = (B == 0 || Hq == 0 || Nq == 0);
   const bool no_keys = (B == 0 || Hkv == 0 || Nk == 0);
@@ -432,6 +433,7 @@ extern "C" int fa_backward_window(const void* q, const void* k, const void* v, c
                                   void* stream) {
   if (window < 1) return FA_ERR_BAD_SIZE;
   if (window >= (int64_t(1) << 30)) return FA_ERR_TOO_LARGE;
+  if (D == 256) return FA_ERR_HEAD_DIM;  // as fa_forward_window
   return backward_common(q, k, v, bias, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, D, scale,
                          1, int(window), dtype, workspace, workspace_bytes, stream);
 }
@@ -443,8 +445,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_BAD_SIZE: return "a size is negative, or Hkv < 1";
     case FA_ERR_HEAD_GROUPS: return "Hq is not a multiple of Hkv";
     case FA_ERR_HEAD_DIM:
-      return "head dimension D must be 64 or 128 (80, 96: bf16/fp16 forward, window and key "
-             "split; 256: bf16/fp16 fused forward)";
+      return "head dimension D must be 64 or 128 (80, 96: bf16/fp16 forward, window, key split "
+             "and backward; 256: bf16/fp16 fused forward, and backward without a logit term)";
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_SCALE: return "scale is not finite";
     case FA_ERR_ALIGNMENT: return "a tensor pointer is misaligned (16 bytes; lse 4 bytes)";

@@ -74,15 +74,20 @@ constexpr int lds_width(int D) { return (D == 80 || D == 96) ? 128 : D; }
 #ifndef FA_DKDV128_VLDS
 #define FA_DKDV128_VLDS 1
 #endif
+//  * D = 256: K in registers, V in LDS (64 KB), 32-row query tiles (two
+//    32.3 KB stages), one workgroup per compute unit.  The dK and dV
+//    accumulators of all 256 columns (256 registers) do not fit beside the
+//    rest, so the kernel runs its query tiles twice, for columns 0-127 and
+//    then 128-255, recomputing S and dP in each pass.
 // (D = 80 and 96 take the D = 128 layouts: their LDS rows are 128 wide)
 constexpr bool dkdv_pair(int D, bool causal, bool bias) {  // two workgroups per CU at D = 128
-  return D > 64 && !bias;
+  return D > 64 && D < 256 && !bias;
 }
 constexpr bool dkdv_k_in_lds(int D, bool causal, bool bias) {
-  return D > 64 && !dkdv_pair(D, causal, bias);
+  return D > 64 && D < 256 && !dkdv_pair(D, causal, bias);
 }
 constexpr bool dkdv_v_in_lds(int D, bool causal, bool bias) {
-  return D > 64 && (!dkdv_pair(D, causal, bias) || FA_DKDV128_VLDS);
+  return D == 256 || (D > 64 && (!dkdv_pair(D, causal, bias) || FA_DKDV128_VLDS));
 }
 // The instance that runs at 256 VGPRs takes its LDS offsets from two
 // registers (OffsetsLean) rather than from 24: with the table it spilled.
@@ -90,9 +95,12 @@ constexpr bool dkdv_lean_offsets(int D, bool causal, bool bias) {
   return dkdv_pair(D, causal, bias) && FA_DKDV128_VLDS;
 }
 constexpr int dkdv_qtile(int D, bool causal, bool bias) {
-  return (dkdv_pair(D, causal, bias) && FA_DKDV128_VLDS) ? 32 : 64;
+  return (D == 256 || (dkdv_pair(D, causal, bias) && FA_DKDV128_VLDS)) ? 32 : 64;
 }
-constexpr int kKTile = 64;        // keys per tile in the dQ kernel
+// Keys per tile in the dQ kernel: 64, and 32 at D = 256, whose Q and dO
+// fragments (128 VGPRs) and dQ accumulator (128) take one workgroup per
+// compute unit already.
+constexpr int dq_ktile(int D) { return D == 256 ? 32 : 64; }
 
 struct BwdParams {
   const void* q;
@@ -278,10 +286,10 @@ __device__ __forceinline__ void store_rows(T* dst_row, const f32x16 (&acc)[NDB],
 // them in the workspace for the dK/dV kernel, which runs after it.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW>
-__global__ __launch_bounds__(kBwdThreads, 2) void fa_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads, D == 256 ? 1 : 2) void fa_bwd_dq_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
-  constexpr int BN = kKTile;
+  constexpr int BN = dq_ktile(D);
   constexpr int NS = (D + 15) / 16, NDB = (D + 31) / 32, NKB = BN / 32;
   constexpr int RB = D * 2;                // bytes per row in HBM
   constexpr int LRB = lds_width(D) * 2;    // bytes per row in LDS
@@ -572,12 +580,11 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       vf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(v_rs, off, 0, 0));
   }
 
-  f32x16 dka[NDB], dva[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dka[db] = f32x16{};
-    dva[db] = f32x16{};
-  }
+  // column passes (D = 256: two of 128 columns) and the accumulator blocks
+  // of one pass
+  constexpr int NH = D == 256 ? 2 : 1, NDH = NDB / NH;
+  int colh = 0;
+  f32x16 dka[NDH], dva[NDH];
 
   // Query tiles: BQ rows i0 .. i0+BQ-1 of one query head h of the group
   // (packed row r0 = h*Nq + i0), so a row's query position is i0 plus its
@@ -689,43 +696,50 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         const Frag pf = pack_half<T>(s, h);
         const Frag dsf = pack_half<T>(dp, h);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int dh = 0; dh < NDH; ++dh) {
+          const int db = colh * NDH + dh;
           const Frag gt = lds_frag_tr<T>(sG + (qb * 32 + 16 * h) * LRB, ofs.tr(0, db), ofs.tr(1, db));
-          dva[db] = E::mma(gt, pf, dva[db]);
+          dva[dh] = E::mma(gt, pf, dva[dh]);
           const Frag qt = lds_frag_tr<T>(sQ + (qb * 32 + 16 * h) * LRB, ofs.tr(0, db), ofs.tr(1, db));
-          dka[db] = E::mma(qt, dsf, dka[db]);
+          dka[dh] = E::mma(qt, dsf, dka[dh]);
         }
       }
     }
   };
 
-  // the visible tiles in order: head h, tile ti (i0 = ti * BQ)
-  const int n_tiles = n_vis > 0 ? p.group * n_vis : 0;
-  int h = 0, ti = ti_lo;
-  if (n_tiles > 0) issue(ti * BQ, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-  __syncthreads();
-  int buf = 0;
-  for (int u = 0; u < n_tiles; ++u) {
-    int hn = h, tn = ti + 1;  // the next visible tile
-    if (tn == ti_end) {
-      tn = ti_lo;
-      ++hn;
-    }
-    if (u + 1 < n_tiles) issue(hn * p.Nq + tn * BQ, buf ^ 1);
-    compute(h * p.Nq + ti * BQ, ti * BQ, buf);
-    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-    __syncthreads();
-    h = hn;
-    ti = tn;
-    buf ^= 1;
-  }
-
   const bool key_ok = kj < p.Nk;
   T* dk_row = static_cast<T*>(p.dk) + (kv_head * p.Nk + kj) * D;
   T* dv_row = static_cast<T*>(p.dv) + (kv_head * p.Nk + kj) * D;
-  store_rows<T, NDB, D>(dk_row, dka, p.scale, g, key_ok);
-  store_rows<T, NDB, D>(dv_row, dva, 1.f, g, key_ok);
+  // the visible tiles in order: head h, tile ti (i0 = ti * BQ)
+  const int n_tiles = n_vis > 0 ? p.group * n_vis : 0;
+  for (colh = 0; colh < NH; ++colh) {
+#pragma unroll
+    for (int dh = 0; dh < NDH; ++dh) {
+      dka[dh] = f32x16{};
+      dva[dh] = f32x16{};
+    }
+    int h = 0, ti = ti_lo;
+    if (n_tiles > 0) issue(ti * BQ, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    __syncthreads();
+    int buf = 0;
+    for (int u = 0; u < n_tiles; ++u) {
+      int hn = h, tn = ti + 1;  // the next visible tile
+      if (tn == ti_end) {
+        tn = ti_lo;
+        ++hn;
+      }
+      if (u + 1 < n_tiles) issue(hn * p.Nq + tn * BQ, buf ^ 1);
+      compute(h * p.Nq + ti * BQ, ti * BQ, buf);
+      __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+      __syncthreads();
+      h = hn;
+      ti = tn;
+      buf ^= 1;
+    }
+    store_rows<T, NDH, D>(dk_row + colh * NDH * 32, dka, p.scale, g, key_ok);
+    store_rows<T, NDH, D>(dv_row + colh * NDH * 32, dva, 1.f, g, key_ok);
+  }
 }
 
 template <typename T, int D>
@@ -735,7 +749,16 @@ hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool bias, hipStream_t 
   hipError_t e = hipSuccess;
   const void* dq;
   const void* kv;
-  if (causal && p.window > 0) {
+  if constexpr (D == 256) {
+    // (no logit term and no window at D = 256: the API refuses both)
+    if (causal) {
+      dq = reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, false, false>);
+      kv = reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, false, false>);
+    } else {
+      dq = reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, false, false, false>);
+      kv = reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, false, false, false>);
+    }
+  } else if (causal && p.window > 0) {
     dq = bias ? reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, true, true>)
               : reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, false, true>);
     kv = bias ? reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, true, true>)
@@ -799,6 +822,7 @@ int launch_backward(const BwdArgs& a) {
       case 64: return launch_bwd_d<T, 64>(p, a.causal, a.bias, s, g_dq, g_kv);
       case 80: return launch_bwd_d<T, 80>(p, a.causal, a.bias, s, g_dq, g_kv);
       case 96: return launch_bwd_d<T, 96>(p, a.causal, a.bias, s, g_dq, g_kv);
+      case 256: return launch_bwd_d<T, 256>(p, a.causal, a.bias, s, g_dq, g_kv);
       default: return launch_bwd_d<T, 128>(p, a.causal, a.bias, s, g_dq, g_kv);
     }
   };
