@@ -1,9 +1,9 @@
 """The build's device-code checks, on synthetic disassembly (CPU only).
 
 build.py disassembles the gfx950 code it has just compiled and refuses a
-library in which a value could live in M0 across another instruction that
-touches M0 (the forward's bias instances write M0 from inline assembly without
-the compiler saving it), or in which one of those instances uses scratch.
+library in which, in a forward bias instance (these write M0 from inline
+assembly without the compiler saving it), a value could live in M0 across
+another instruction that touches M0, or one of those instances uses scratch.
 These tests plant each violation in a small listing in llvm-objdump's format
 and require the checker to report it, so that a clean build means something.
 """
@@ -44,6 +44,19 @@ def test_load_without_write_in_its_block_is_caught():
     # the write before a branch target does not reach a load after it
     lst = _listing("s_mov_b32 m0, s3", "s_branch 0", LOAD, "s_endpgm")
     assert len(build.m0_discipline_problems(lst)) == 1
+
+
+def test_rule_applies_to_the_inline_assembly_instances():
+    # one M0 value kept for two loads: a violation in a bias instance (whose
+    # asm writes M0 unseen by the compiler), the compiler's own business in
+    # any other kernel
+    body = ("s_mov_b32 m0, s3", LOAD, LOAD, "s_endpgm")
+    asm_kernel = "_ZN2fa12_GLOBAL__N_113fa_fwd_kernelIDF16bLi128ELi64ELi1ELb1ELb1ELb0ELb0ELi1ELi0ELi1EEEvNS0_6ParamsE"
+    other = "_ZN2fa12_GLOBAL__N_118fa_bwd_dkdv_kernelIDF16_Li256ELb0ELb0ELb0EEEvNS0_9BwdParamsE"
+    assert len(build.m0_discipline_problems(_listing(*body, name=asm_kernel),
+                                            only=build._ASM_INSTANCE)) == 1
+    assert build.m0_discipline_problems(_listing(*body, name=other), only=build._ASM_INSTANCE) == []
+    assert len(build.m0_discipline_problems(_listing(*body, name=other))) == 1
 
 
 def test_read_by_name_is_caught():

@@ -119,16 +119,17 @@ _LINE = re.compile(r"^\s+(\S+)\s*([^/]*?)\s*//\s*([0-9A-Fa-f]+):")
 _FUNC = re.compile(r"^[0-9A-Fa-f]+ <([^>]+)>:")
 
 
-def m0_discipline_problems(listing: str, window: int = 16):
+def m0_discipline_problems(listing: str, window: int = 16, only=None):
     """Check that no value lives in M0 across another instruction that touches it.
 
     The forward's bias instances issue their direct-to-LDS loads from inline
     assembly that writes M0 without the compiler saving it first; that is safe
     only if the compiler never keeps a value in M0 across such a statement.
-    Rule checked, per kernel: M0 is never read by name, and every instruction
-    that reads it implicitly has, as the nearest earlier instruction touching M0
-    in its basic block (no branch or branch target in between, at most
-    ``window`` instructions back), a write of M0.  Returns a list of problems."""
+    Rule checked, per kernel (those whose name ``only`` matches, if given): M0
+    is never read by name, and every instruction that reads it implicitly has,
+    as the nearest earlier instruction touching M0 in its basic block (no
+    branch or branch target in between, at most ``window`` instructions back),
+    a write of M0.  Returns a list of problems."""
     problems = []
     funcs = []
     for line in listing.splitlines():
@@ -141,6 +142,8 @@ def m0_discipline_problems(listing: str, window: int = 16):
             ops = [o.strip() for o in m.group(2).split(",")] if m.group(2) else []
             funcs[-1][1].append((m.group(1), ops, int(m.group(3), 16)))
     for name, ins in funcs:
+        if only is not None and not only.search(name):
+            continue
         targets = set()
         for mn, ops, addr in ins:
             if mn.startswith(("s_branch", "s_cbranch_")) and ops:
@@ -194,8 +197,11 @@ def asm_instance_scratch_problems(notes: str):
 
 
 def check_device_code(obj: str, tmp: str) -> None:
+    # Only the kernels with M0-writing inline assembly need the M0 rule: in the
+    # others the compiler owns M0 and may keep one value for several loads.
     listing, notes = device_code(obj, tmp)
-    problems = m0_discipline_problems(listing) + asm_instance_scratch_problems(notes)
+    problems = (m0_discipline_problems(listing, only=_ASM_INSTANCE) +
+                asm_instance_scratch_problems(notes))
     if problems:
         raise RuntimeError(f"device code of {os.path.basename(obj)} breaks the M0 / scratch "
                            "rules:\n  " + "\n  ".join(problems[:20]))

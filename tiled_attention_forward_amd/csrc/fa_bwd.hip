@@ -76,9 +76,9 @@ constexpr int lds_width(int D) { return (D == 80 || D == 96) ? 128 : D; }
 #endif
 //  * D = 256: K in registers, V in LDS (64 KB), 32-row query tiles (two
 //    32.3 KB stages), one workgroup per compute unit.  The dK and dV
-//    accumulators of all 256 columns (256 registers) do not fit beside the
-//    rest, so the kernel runs its query tiles twice, for columns 0-127 and
-//    then 128-255, recomputing S and dP in each pass.
+//    accumulators together (256 registers) do not fit beside the rest, so
+//    the kernel runs its query tiles twice: first for dV (S and P only), then
+//    for dK (S, P, dP and dS), with one accumulator set.
 // (D = 80 and 96 take the D = 128 layouts: their LDS rows are 128 wide)
 constexpr bool dkdv_pair(int D, bool causal, bool bias) {  // two workgroups per CU at D = 128
   return D > 64 && D < 256 && !bias;
@@ -580,11 +580,11 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       vf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(v_rs, off, 0, 0));
   }
 
-  // column passes (D = 256: two of 128 columns) and the accumulator blocks
-  // of one pass
-  constexpr int NH = D == 256 ? 2 : 1, NDH = NDB / NH;
-  int colh = 0;
-  f32x16 dka[NDH], dva[NDH];
+  // TWO (D = 256): a dV pass, then a dK pass, both accumulating into dva;
+  // otherwise one pass with both accumulators
+  constexpr bool TWO = D == 256;
+  int pass = 0;
+  f32x16 dva[NDB], dka[TWO ? 1 : NDB];
 
   // Query tiles: BQ rows i0 .. i0+BQ-1 of one query head h of the group
   // (packed row r0 = h*Nq + i0), so a row's query position is i0 plus its
@@ -635,18 +635,21 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       const int ib1 = min(ib0 + 31, p.Nq - 1);  // and of its last valid row
       if (CAUSAL && ib1 < kw0) continue;  // all masked
       if (W > 0 && ib0 > kw0 + 31 + W - 1) continue;
-      f32x16 s, dp;
+      const bool want_dv = !TWO || pass == 0, want_dk = !TWO || pass == 1;
+      f32x16 s, dp = f32x16{};
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         const Frag qa = lds_frag<T>(sQ + qb * 32 * LRB + ofs.row(st));
         const Frag kb = K_LDS ? lds_frag<T>(sK + wave * 32 * LRB + ofs.row(st)) : kf[st];
         s = E::mma(qa, kb, st == 0 ? f32x16{} : s);
       }
+      if (want_dk) {
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const Frag ga = lds_frag<T>(sG + qb * 32 * LRB + ofs.row(st));
-        const Frag vb = V_LDS ? lds_frag<T>(sV + wave * 32 * LRB + ofs.row(st)) : vf[st];
-        dp = E::mma(ga, vb, st == 0 ? f32x16{} : dp);
+        for (int st = 0; st < NS; ++st) {
+          const Frag ga = lds_frag<T>(sG + qb * 32 * LRB + ofs.row(st));
+          const Frag vb = V_LDS ? lds_frag<T>(sV + wave * 32 * LRB + ofs.row(st)) : vf[st];
+          dp = E::mma(ga, vb, st == 0 ? f32x16{} : dp);
+        }
       }
       // register r: query row qb*32 + 8*(r/4) + 4*g + r%4 of the tile, key kj
       const bool tail = ib0 + 32 > p.Nq;
@@ -696,12 +699,16 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         const Frag pf = pack_half<T>(s, h);
         const Frag dsf = pack_half<T>(dp, h);
 #pragma unroll
-        for (int dh = 0; dh < NDH; ++dh) {
-          const int db = colh * NDH + dh;
-          const Frag gt = lds_frag_tr<T>(sG + (qb * 32 + 16 * h) * LRB, ofs.tr(0, db), ofs.tr(1, db));
-          dva[dh] = E::mma(gt, pf, dva[dh]);
-          const Frag qt = lds_frag_tr<T>(sQ + (qb * 32 + 16 * h) * LRB, ofs.tr(0, db), ofs.tr(1, db));
-          dka[dh] = E::mma(qt, dsf, dka[dh]);
+        for (int db = 0; db < NDB; ++db) {
+          if (want_dv) {
+            const Frag gt = lds_frag_tr<T>(sG + (qb * 32 + 16 * h) * LRB, ofs.tr(0, db), ofs.tr(1, db));
+            dva[db] = E::mma(gt, pf, dva[db]);
+          }
+          if (want_dk) {
+            const Frag qt = lds_frag_tr<T>(sQ + (qb * 32 + 16 * h) * LRB, ofs.tr(0, db), ofs.tr(1, db));
+            if constexpr (TWO) dva[db] = E::mma(qt, dsf, dva[db]);
+            else dka[db] = E::mma(qt, dsf, dka[db]);
+          }
         }
       }
     }
@@ -712,11 +719,11 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   T* dv_row = static_cast<T*>(p.dv) + (kv_head * p.Nk + kj) * D;
   // the visible tiles in order: head h, tile ti (i0 = ti * BQ)
   const int n_tiles = n_vis > 0 ? p.group * n_vis : 0;
-  for (colh = 0; colh < NH; ++colh) {
+  for (pass = 0; pass < (TWO ? 2 : 1); ++pass) {
 #pragma unroll
-    for (int dh = 0; dh < NDH; ++dh) {
-      dka[dh] = f32x16{};
-      dva[dh] = f32x16{};
+    for (int db = 0; db < NDB; ++db) {
+      dva[db] = f32x16{};
+      if constexpr (!TWO) dka[db] = f32x16{};
     }
     int h = 0, ti = ti_lo;
     if (n_tiles > 0) issue(ti * BQ, 0);
@@ -737,8 +744,13 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       ti = tn;
       buf ^= 1;
     }
-    store_rows<T, NDH, D>(dk_row + colh * NDH * 32, dka, p.scale, g, key_ok);
-    store_rows<T, NDH, D>(dv_row + colh * NDH * 32, dva, 1.f, g, key_ok);
+    if constexpr (TWO) {
+      if (pass == 0) store_rows<T, NDB, D>(dv_row, dva, 1.f, g, key_ok);
+      else store_rows<T, NDB, D>(dk_row, dva, p.scale, g, key_ok);
+    } else {
+      store_rows<T, NDB, D>(dk_row, dka, p.scale, g, key_ok);
+      store_rows<T, NDB, D>(dv_row, dva, 1.f, g, key_ok);
+    }
   }
 }
 
