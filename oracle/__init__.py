@@ -8,6 +8,7 @@ It shares no code with the HIP path and imports nothing from it.
 from .attention import (  # noqa: F401
     attention_backward,
     attention_chain,
+    attention_chain_backward,
     attention_chain_head_rows,
     attention_forward,
     attention_head_rows,

@@ -60,6 +60,7 @@ __all__ = [
     "attention_backward",
     "attention_chain",
     "attention_chain_head_rows",
+    "attention_chain_backward",
 ]
 
 
@@ -412,3 +413,61 @@ def attention_chain_head_rows(q_rows_layers, k_layers, v, *, rows, scale, causal
         residual = logits if residual is None else logits + residual
     return attention_head_rows(q_rows_layers[-1], k_layers[-1], v, rows=rows, scale=scale,
                                causal=causal, bias_rows=residual)
+
+
+def attention_chain_backward(q_layers, k_layers, v, dout, *, scale=None, causal=False):
+    """Gradients of ``attention_chain`` with respect to every Q and K layer and V.
+
+    The "Block Attention Residual" post trains through the fused chain: its
+    first kernel version keeps the softmax statistic for the backward, which
+    recomputes the logits.  The chain rule through the recursion of
+    ``attention_chain``: the current layer's logits are S = sum over the
+    block's layers l of Q_l K_l^T * scale (the residual is that sum over the
+    earlier layers), so per (b, hq) with hk = hq // group
+
+        P     = softmax(S)                 (causal entries -inf, as in the forward)
+        dV    = P^T dO                     (summed over the query heads of a group)
+        dP    = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P o (dP - D)
+        dQ_l  = scale * dS K_l             for every layer l
+        dK_l  = scale * dS^T Q_l           (summed over the query heads of a group)
+
+    The earlier layers' own outputs are not part of this function: their
+    gradients reach Q_l and K_l through their own attention, which the caller
+    adds.  Returns ``(dq_layers, dk_layers, dv)``, lists of float64 arrays with
+    the layers' shapes, and dV with v's.
+    """
+    n = len(q_layers)
+    if n < 1 or len(k_layers) != n:
+        raise ValueError("need as many K layers as Q layers, at least one")
+    b_, hq_, hkv, nq, nk, d = _check_shapes(q_layers[-1], k_layers[-1], v, None)
+    for ql, kl in zip(q_layers, k_layers):
+        if tuple(ql.shape) != tuple(q_layers[-1].shape) or tuple(kl.shape) != tuple(k_layers[-1].shape):
+            raise ValueError("every layer of the chain has the same Q and K shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    qs = [_f64(x) for x in q_layers]
+    ks = [_f64(x) for x in k_layers]
+    v, dout = _f64(v), _f64(dout)
+    if dout.shape != qs[-1].shape:
+        raise ValueError("dout must have the Q layers' shape")
+    group = hq_ // hkv
+    dqs = [np.zeros_like(x) for x in qs]
+    dks = [np.zeros_like(x) for x in ks]
+    dv = np.zeros_like(v)
+    for b in range(b_):
+        for h in range(hq_):
+            hk = h // group
+            s = sum(qs[l][b, h] @ ks[l][b, hk].T for l in range(n)) * float(scale)
+            if causal:
+                i = np.arange(nq)[:, None]
+                j = np.arange(nk)[None, :]
+                s = np.where(j > i, -np.inf, s)
+            p, _, _ = softmax_two_pass(s)
+            do = dout[b, h]
+            dv[b, hk] += p.T @ do
+            dp = do @ v[b, hk].T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            for l in range(n):
+                dqs[l][b, h] = float(scale) * (ds @ ks[l][b, hk])
+                dks[l][b, hk] += float(scale) * (ds.T @ qs[l][b, h])
+    return dqs, dks, dv
