@@ -326,6 +326,39 @@ int fa_backward_window(const void* q, const void* k, const void* v, const void* 
                        float scale, int64_t window, int dtype,
                        void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * Backward of fa_forward_chain.  The Block Attention Residual post
+ * (iqiancheng.github.io, "v1") trains through its fused chain, with the
+ * softmax statistic kept for the backward.  With S = sum over the block's
+ * layers l of Q_l K_l^T * scale (the current layer's logits), P = softmax(S)
+ * and dS = P o (dP - D_i) as in fa_backward:
+ *   dq_layers[l] = scale * dS K_l,
+ *   dk_layers[l] = scale * dS^T Q_l  (summed over the query heads of a KV head),
+ *   dv           = P^T dO.
+ * These are the gradients through this layer's attention only: what the
+ * earlier layers receive through their own attention is the caller's to add.
+ *   q_layers, k_layers, num_layers, v, scale, causal: as passed to
+ *     fa_forward_chain (oldest layer first); o, lse: its outputs;
+ *   dout: gradient of the loss w.r.t. o, [B, Hq, Nq, D], dtype;
+ *   dq_layers[l]: out, [B, Hq, Nq, D]; dk_layers[l]: out, [B, Hkv, Nk, D];
+ *   dv: out, [B, Hkv, Nk, D]; all dtype;
+ *   workspace, workspace_bytes: as for fa_backward.
+ * bf16 and fp16, D = 64 or 128 (FA_ERR_HEAD_DIM), 1 to 4 layers
+ * (FA_ERR_BAD_SIZE); NULL layer arrays give FA_ERR_NULL_POINTER.  Every
+ * layer's arguments are checked as fa_backward checks its own, and
+ * FA_ERR_OVERLAP is returned if an output overlaps any layer's input or
+ * another output.  One layer is fa_backward.  Otherwise two kernels per layer
+ * l are enqueued on stream in layer order (dQ of layer l, then dK of layer l,
+ * with dV formed alongside layer 0's), each recomputing the summed logits; the
+ * call returns without waiting.  Deterministic (no atomics).
+ */
+int fa_backward_chain(const void* const* q_layers, const void* const* k_layers,
+                      int64_t num_layers, const void* v, const void* o, const float* lse,
+                      const void* dout, void* const* dq_layers, void* const* dk_layers, void* dv,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                      float scale, int causal, int dtype,
+                      void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Workspace bytes of fa_backward through *bytes: float32 [B*Hq*Nq] twice,
  * the second part from the next 256-byte boundary.  Pure host code. */
 int fa_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t* bytes);

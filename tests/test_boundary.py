@@ -50,8 +50,8 @@ def test_library_loads_and_exports_every_declared_symbol():
                           "fa_forward_split_noalloc", "fa_merge",
                           "fa_split_count", "fa_split_workspace_bytes", "fa_backward",
                           "fa_backward_workspace_bytes", "fa_forward_window",
-                          "fa_backward_window", "fa_forward_chain", "fa_status_string",
-                          "fa_version"}
+                          "fa_backward_window", "fa_forward_chain", "fa_backward_chain",
+                          "fa_status_string", "fa_version"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
@@ -355,6 +355,37 @@ def test_chain_rejections_before_launch():
     assert chain([Q0, Q], [K0 + 8, K]) == 7                   # a layer's K misaligned
     assert chain([Q0, Q], [K0, K], o=Q0) == 8                 # output over an earlier Q
     assert chain([Q0, Q], [K0, K], B=0) == 0                  # empty: nothing launched
+
+
+def test_chain_backward_rejections_before_launch():
+    Q0, K0, DQ0, DK0 = 0x1000000000, 0x1100000000, 0x1200000000, 0x1300000000
+    a = dict(OK_ARGS)
+
+    def bchain(qs, ks, dqs, dks, workspace=WS, dv=DV, dout=GO, **over):
+        b = dict(a, **over)
+        return binding.fa_backward_chain(qs, ks, b["v"], b["o"], b["lse"], dout, dqs, dks, dv,
+                                         b["B"], b["Hq"], b["Hkv"], b["Nq"], b["Nk"], b["D"],
+                                         b["scale"], b["causal"], b["dtype"], workspace, 1 << 40,
+                                         None)
+    lib = binding.load_library()
+    assert lib.fa_backward_chain(None, None, 2, V, O, L, GO, None, None, DV, 2, 4, 2, 100, 77,
+                                 64, 0.125, 1, a["dtype"], WS, 1 << 40, None) == 1
+    ok = ([Q0, Q], [K0, K], [DQ0, DQ], [DK0, DK])
+    assert bchain([], [], [], []) == 2                                     # no layer
+    assert bchain([Q0, Q] * 2 + [Q], [K0, K] * 2 + [K], [DQ0, DQ] * 2 + [DQ],
+                  [DK0, DK] * 2 + [DK]) == 2                               # five layers
+    assert bchain(*ok, dtype=binding.FA_DTYPE_FP32) == 5                   # 16-bit only
+    assert bchain(*ok, D=96) == 4 and bchain(*ok, D=256) == 4              # 64 and 128 only
+    assert bchain(*ok, Hq=3) == 3
+    assert bchain([None, Q], [K0, K], [DQ0, DQ], [DK0, DK]) == 1           # a layer's Q missing
+    assert bchain([Q0, Q], [K0, K], [None, DQ], [DK0, DK]) == 1            # a layer's dQ missing
+    assert bchain([Q0, Q], [K0 + 8, K], [DQ0, DQ], [DK0, DK]) == 7         # a layer's K misaligned
+    assert bchain(*ok, workspace=None) == 11
+    assert bchain([Q0, Q], [K0, K], [Q, DQ], [DK0, DK]) == 8               # dQ_0 over the last Q
+    assert bchain([Q0, Q], [K0, K], [DQ0, DQ], [DK0, K0]) == 8             # dK_1 over K_0
+    assert bchain([Q0, Q], [K0, K], [DQ0, DQ0], [DK0, DK]) == 8            # two dQ on one buffer
+    assert bchain(*ok, dv=DK0) == 8                                        # dV over dK_0
+    assert bchain(*ok, B=0) == 0                                           # empty: nothing launched
 
 
 def test_fp8_rejections_before_launch():

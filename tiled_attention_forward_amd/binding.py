@@ -85,6 +85,10 @@ def load_library():
     lib.fa_backward.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, f32,
                                 i32, i32, p, i64, p]
     lib.fa_backward.restype = i32
+    lib.fa_backward_chain.argtypes = [ctypes.POINTER(p), ctypes.POINTER(p), i64, p, p, p, p,
+                                      ctypes.POINTER(p), ctypes.POINTER(p), p, i64, i64, i64,
+                                      i64, i64, i64, f32, i32, i32, p, i64, p]
+    lib.fa_backward_chain.restype = i32
     lib.fa_backward_workspace_bytes.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
     lib.fa_backward_workspace_bytes.restype = i32
     lib.fa_status_string.argtypes = [i32]
@@ -471,3 +475,71 @@ def backward(q, k, v, o, lse, dout, bias=None, *, causal=False, scale=None, dq=N
     if st != FA_OK:
         raise FaError(st, fa_status_string(st))
     return dq, dk, dv
+
+
+def fa_backward_chain(q_ptrs, k_ptrs, v, o, lse, dout, dq_ptrs, dk_ptrs, dv, B, Hq, Hkv, Nq,
+                      Nk, D, scale, causal, dtype, workspace, workspace_bytes, stream) -> int:
+    """fa_backward_chain with Python lists of device addresses for the layers."""
+    arr = lambda xs: (ctypes.c_void_p * max(len(xs), 1))(*xs)
+    return load_library().fa_backward_chain(arr(q_ptrs), arr(k_ptrs), len(q_ptrs), v, o, lse,
+                                            dout, arr(dq_ptrs), arr(dk_ptrs), dv, B, Hq, Hkv, Nq,
+                                            Nk, D, scale, causal, dtype, workspace,
+                                            workspace_bytes, stream)
+
+
+def backward_chain(q_layers, k_layers, v, o, lse, dout, *, causal=False, scale=None,
+                   dq_layers=None, dk_layers=None, dv=None, workspace=None, stream=None):
+    """Gradients of ``forward_chain`` through fa_backward_chain.
+
+    Returns ``(dq_layers, dk_layers, dv)``: the gradients of every Q and K
+    layer of the chain (oldest first) and of v, for ``o`` and ``lse`` from
+    ``forward_chain`` on the same arguments and ``dout`` the gradient with
+    respect to ``o``.  bf16/fp16, D = 64 or 128; outputs and the workspace are
+    allocated with torch unless given.
+    """
+    import torch
+    lib = load_library()
+    if len(q_layers) != len(k_layers) or not q_layers:
+        raise ValueError("need as many K layers as Q layers, at least one")
+    B, Hq, Hkv, Nq, Nk, D = _check_inputs(q_layers[-1], k_layers[-1], v, None)
+    for ql, kl in zip(q_layers, k_layers):
+        _check_inputs(ql, kl, v, None)
+        if ql.shape != q_layers[-1].shape or ql.dtype != v.dtype or kl.dtype != v.dtype:
+            raise ValueError("every layer needs the shapes and dtype of the last one")
+    q = q_layers[-1]
+    for name, t in (("o", o), ("dout", dout)):
+        _check_buffer(name, t, q.shape, q.dtype, q.device)
+    _check_buffer("lse", lse, (B, Hq, Nq), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    n = len(q_layers)
+    if dq_layers is None:
+        dq_layers = [torch.empty_like(t) for t in q_layers]
+    if dk_layers is None:
+        dk_layers = [torch.empty_like(t) for t in k_layers]
+    if len(dq_layers) != n or len(dk_layers) != n:
+        raise ValueError("need one dQ and one dK buffer per layer")
+    for t in dq_layers:
+        _check_buffer("dq", t, q.shape, q.dtype, q.device)
+    for t in dk_layers:
+        _check_buffer("dk", t, v.shape, v.dtype, v.device)
+    if dv is None:
+        dv = torch.empty_like(v)
+    else:
+        _check_buffer("dv", dv, v.shape, v.dtype, v.device)
+    need = fa_backward_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, need, q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_backward_chain([t.data_ptr() for t in q_layers], [t.data_ptr() for t in k_layers],
+                           v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                           [t.data_ptr() for t in dq_layers], [t.data_ptr() for t in dk_layers],
+                           dv.data_ptr(), B, Hq, Hkv, Nq, Nk, D, float(scale), int(bool(causal)),
+                           _dtype_code(v), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, fa_status_string(st))
+    return dq_layers, dk_layers, dv

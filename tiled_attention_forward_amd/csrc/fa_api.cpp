@@ -340,11 +340,14 @@ extern "C" int fa_backward_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, in
 
 namespace {
 
-int backward_common(const void* q, const void* k, const void* v, const void* bias, const void* o,
-                    const float* lse, const void* dout, void* dq, void* dk, void* dv, int64_t B,
-                    int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, float scale,
-                    int causal, int window, int dtype, void* workspace, int64_t workspace_bytes,
-                    void* stream) {
+// The backward's checks; fills *a for the launch, or sets *empty when there is
+// nothing to compute.
+int backward_prepare(const void* q, const void* k, const void* v, const void* bias,
+                     const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                     void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                     int64_t D, float scale, int causal, int window, int dtype, void* workspace,
+                     int64_t workspace_bytes, void* stream, fa::BwdArgs* a, bool* empty) {
+  *empty = false;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;  // 16-bit only
   int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
   if (st != FA_OK) return st;
@@ -353,7 +356,10 @@ int backward_common(const void* q, const void* k, const void* v, const void* bia
   const int esz = elem_bytes(dtype);
   const bool no_rows = (B == 0 || Hq == 0 || Nq == 0);
   const bool no_keys = (B == 0 || Hkv == 0 || Nk == 0);
-  if (no_rows && no_keys) return FA_OK;
+  if (no_rows && no_keys) {
+    *empty = true;
+    return FA_OK;
+  }
   // pointers fa_check_args does not cover, or skipped for an empty row space
   if (!no_rows && (dout == nullptr || dq == nullptr)) return FA_ERR_NULL_POINTER;
   if (!no_keys && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
@@ -388,29 +394,42 @@ int backward_common(const void* q, const void* k, const void* v, const void* bia
     for (const Buf& b : outs)
       if (&a != &b && overlap(a.p, a.n, b.p, b.n)) return FA_ERR_OVERLAP;
   }
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->bias = bias;
+  a->o = o;
+  a->dout = dout;
+  a->lse = lse;
+  a->dq = dq;
+  a->dk = dk;
+  a->dv = dv;
+  a->workspace = workspace;
+  a->B = int(B);
+  a->Hq = int(Hq);
+  a->Hkv = int(Hkv);
+  a->Nq = int(Nq);
+  a->Nk = int(Nk);
+  a->D = int(D);
+  a->scale = scale;
+  a->causal = causal != 0;
+  a->window = window;
+  a->dtype = dtype;
+  a->stream = stream;
+  return FA_OK;
+}
+
+int backward_common(const void* q, const void* k, const void* v, const void* bias, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv, int64_t B,
+                    int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, float scale,
+                    int causal, int window, int dtype, void* workspace, int64_t workspace_bytes,
+                    void* stream) {
   fa::BwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.bias = bias;
-  a.o = o;
-  a.dout = dout;
-  a.lse = lse;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.workspace = workspace;
-  a.B = int(B);
-  a.Hq = int(Hq);
-  a.Hkv = int(Hkv);
-  a.Nq = int(Nq);
-  a.Nk = int(Nk);
-  a.D = int(D);
-  a.scale = scale;
-  a.causal = causal != 0;
-  a.window = window;
-  a.dtype = dtype;
-  a.stream = stream;
+  bool empty;
+  const int st = backward_prepare(q, k, v, bias, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, D,
+                                  scale, causal, window, dtype, workspace, workspace_bytes,
+                                  stream, &a, &empty);
+  if (st != FA_OK || empty) return st;
   return fa::launch_backward(a);
 }
 
@@ -436,6 +455,58 @@ extern "C" int fa_backward_window(const void* q, const void* k, const void* v, c
   if (D == 256) return FA_ERR_HEAD_DIM;  // as fa_forward_window
   return backward_common(q, k, v, bias, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, D, scale,
                          1, int(window), dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa_backward_chain(const void* const* q_layers, const void* const* k_layers,
+                                 int64_t num_layers, const void* v, const void* o,
+                                 const float* lse, const void* dout, void* const* dq_layers,
+                                 void* const* dk_layers, void* dv, int64_t B, int64_t Hq,
+                                 int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, float scale,
+                                 int causal, int dtype, void* workspace, int64_t workspace_bytes,
+                                 void* stream) {
+  if (q_layers == nullptr || k_layers == nullptr || dq_layers == nullptr || dk_layers == nullptr)
+    return FA_ERR_NULL_POINTER;
+  if (num_layers < 1 || num_layers > fa::kMaxChainLayers) return FA_ERR_BAD_SIZE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;  // as fa_forward_chain
+  const int n = int(num_layers);
+  fa::BwdArgs a;
+  bool empty = false;
+  for (int l = 0; l < n; ++l) {
+    const int st = backward_prepare(q_layers[l], k_layers[l], v, nullptr, o, lse, dout,
+                                    dq_layers[l], dk_layers[l], dv, B, Hq, Hkv, Nq, Nk, D, scale,
+                                    causal, 0, dtype, workspace, workspace_bytes, stream, &a,
+                                    &empty);
+    if (st != FA_OK) return st;
+  }
+  if (empty) return FA_OK;
+  // across layers: no output may overlap any layer's input or another output
+  const int esz = elem_bytes(dtype);
+  const int64_t rows = B * Hq * Nq;
+  const uint64_t nq_b = uint64_t(rows) * D * esz;
+  const uint64_t nkv_b = uint64_t(B) * Hkv * Nk * D * esz;
+  const uint64_t ws_b = rows > 0 ? uint64_t(fa::backward_workspace_bytes(rows)) : 0;
+  struct Buf { const void* p; uint64_t n; };
+  Buf ins[2 * fa::kMaxChainLayers + 4], outs[2 * fa::kMaxChainLayers + 2];
+  int ni = 0, no = 0;
+  for (int l = 0; l < n; ++l) {
+    ins[ni++] = {q_layers[l], nq_b};
+    ins[ni++] = {k_layers[l], nkv_b};
+    outs[no++] = {dq_layers[l], nq_b};
+    outs[no++] = {dk_layers[l], nkv_b};
+  }
+  ins[ni++] = {v, nkv_b};
+  ins[ni++] = {o, nq_b};
+  ins[ni++] = {lse, uint64_t(rows) * 4};
+  ins[ni++] = {dout, nq_b};
+  outs[no++] = {dv, nkv_b};
+  outs[no++] = {workspace, ws_b};
+  for (int i = 0; i < no; ++i) {
+    for (int j = 0; j < ni; ++j)
+      if (overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return FA_ERR_OVERLAP;
+    for (int j = 0; j < no; ++j)
+      if (i != j && overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return FA_ERR_OVERLAP;
+  }
+  return fa::launch_backward_chain(a, q_layers, k_layers, dq_layers, dk_layers, n);
 }
 
 extern "C" const char* fa_status_string(int status) {

@@ -100,7 +100,7 @@ constexpr int dkdv_qtile(int D, bool causal, bool bias) {
 // Keys per tile in the dQ kernel: 64, and 32 at D = 256, whose Q and dO
 // fragments (128 VGPRs) and dQ accumulator (128) take one workgroup per
 // compute unit already.
-constexpr int dq_ktile(int D) { return D == 256 ? 32 : 64; }
+constexpr int dq_ktile(int D, int NL) { return (D == 256 || (D == 128 && NL > 1)) ? 32 : 64; }
 
 struct BwdParams {
   const void* q;
@@ -125,6 +125,13 @@ struct BwdParams {
   int bias_vec;  // bias rows allow 8-byte loads (Nk % 4 == 0)
   int window;    // causal sliding window (keys i-window+1 .. i), 0 = none
   int64_t rows;  // B * Hq * Nq
+  // Block Attention Residual chain (NL > 1 instances): every layer's Q and K,
+  // oldest first (the logits are the sum of their products), and the layer
+  // whose dQ (dQ kernel) and dK (dK/dV kernel) this launch forms; dq and dk
+  // point at that layer's gradients, and dV is formed with target 0 only.
+  const void* chain_q[kMaxChainLayers];
+  const void* chain_k[kMaxChainLayers];
+  int target;
 };
 
 // Direct LDS loads of an R x D tile (16-bit, row-major in HBM at a buffer
@@ -285,16 +292,19 @@ __device__ __forceinline__ void store_rows(T* dst_row, const f32x16 (&acc)[NDB],
 // forms each row's delta = rowsum(dO o O) and lse2 = LSE log2(e) and leaves
 // them in the workspace for the dK/dV kernel, which runs after it.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW>
-__global__ __launch_bounds__(kBwdThreads, D == 256 ? 1 : 2) void fa_bwd_dq_kernel(BwdParams p) {
+template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW, int NL = 1>
+__global__ __launch_bounds__(kBwdThreads, (D == 256 || (D == 128 && NL > 1)) ? 1 : 2)
+void fa_bwd_dq_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
-  constexpr int BN = dq_ktile(D);
+  static_assert(NL == 1 || (!BIAS && !WINDOW && D <= 128), "chain instances");
+  constexpr int BN = dq_ktile(D, NL);
   constexpr int NS = (D + 15) / 16, NDB = (D + 31) / 32, NKB = BN / 32;
   constexpr int RB = D * 2;                // bytes per row in HBM
   constexpr int LRB = lds_width(D) * 2;    // bytes per row in LDS
   constexpr int TILE = BN * LRB;  // bytes per K (or V) tile
-  __shared__ __attribute__((aligned(16))) char smem[2][2 * TILE];
+  // per buffer: the K tiles of the NL layers, then the V tile
+  __shared__ __attribute__((aligned(16))) char smem[2][(NL + 1) * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, ln = lane & 31;
@@ -319,14 +329,18 @@ __global__ __launch_bounds__(kBwdThreads, D == 256 ? 1 : 2) void fa_bwd_dq_kerne
   const int b = bh / p.Hq, hk = (bh - b * p.Hq) / p.group;
   const int64_t kv_head = int64_t(b) * p.Hkv + hk;
   const int64_t row_base = int64_t(bh) * p.Nq;
-  const T* Qh = static_cast<const T*>(p.q) + row_base * D;
   const T* Gh = static_cast<const T*>(p.dout) + row_base * D;
-  const T* Kh = static_cast<const T*>(p.k) + kv_head * p.Nk * D;
   const T* Vh = static_cast<const T*>(p.v) + kv_head * p.Nk * D;
-  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(Qh, uint32_t(p.Nq) * RB);
   const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(Gh, uint32_t(p.Nq) * RB);
-  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh, uint32_t(p.Nk) * RB);
   const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh, uint32_t(p.Nk) * RB);
+  __amdgpu_buffer_rsrc_t q_rs[NL], k_rs[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    const T* Ql = static_cast<const T*>(NL > 1 ? p.chain_q[l] : p.q) + row_base * D;
+    const T* Kl = static_cast<const T*>(NL > 1 ? p.chain_k[l] : p.k) + kv_head * p.Nk * D;
+    q_rs[l] = make_rsrc(Ql, uint32_t(p.Nq) * RB);
+    k_rs[l] = make_rsrc(Kl, uint32_t(p.Nk) * RB);
+  }
 
   const int q_blk = tile * 128;
   const int wq0 = q_blk + wave * 32;
@@ -335,12 +349,15 @@ __global__ __launch_bounds__(kBwdThreads, D == 256 ? 1 : 2) void fa_bwd_dq_kerne
   const int wq_last = min(wq0 + 31, p.Nq - 1);
   const int blk_last = min(q_blk + 127, p.Nq - 1);
 
-  // Q and dO rows of this lane: B operands of S^T = K Q^T and dP^T = V dO^T
-  Frag qf[NS], gf[NS];
+  // Q (every layer's) and dO rows of this lane: B operands of S^T = K Q^T
+  // and dP^T = V dO^T
+  Frag qf[NL][NS], gf[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     const int off = qi * RB + (16 * st + 8 * g) * 2;
-    qf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(q_rs, off, 0, 0));
+#pragma unroll
+    for (int l = 0; l < NL; ++l)
+      qf[l][st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(q_rs[l], off, 0, 0));
     gf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(g_rs, off, 0, 0));
   }
   const bool row_ok = qi < p.Nq;
@@ -396,22 +413,27 @@ __global__ __launch_bounds__(kBwdThreads, D == 256 ? 1 : 2) void fa_bwd_dq_kerne
   const int wave_key_lo = W > 0 ? max(0, wq0 - W + 1) : 0;
 
   auto issue = [&](int j, int buf) {
-    tl.issue(k_rs, smem[buf], wave, uint32_t(j) * BN * RB);
-    tl.issue(v_rs, smem[buf] + TILE, wave, uint32_t(j) * BN * RB);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) tl.issue(k_rs[l], smem[buf] + l * TILE, wave, uint32_t(j) * BN * RB);
+    tl.issue(v_rs, smem[buf] + NL * TILE, wave, uint32_t(j) * BN * RB);
   };
 
+  // (the K tile dQ is formed against: the target layer's)
+  const int tgt = NL > 1 ? p.target : 0;
   auto compute = [&](int j, int buf) {
-    const char* sK = smem[buf];
-    const char* sV = smem[buf] + TILE;
+    const char* sV = smem[buf] + NL * TILE;
+    const char* sKt = smem[buf] + tgt * TILE;
     const int key0 = j * BN;
     f32x16 s[NKB], dp[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const Frag kf = lds_frag<T>(sK + kb * 32 * LRB + of.row_off[st]);
-        s[kb] = E::mma(kf, qf[st], st == 0 ? f32x16{} : s[kb]);
-      }
+      for (int l = 0; l < NL; ++l)
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          const Frag kf = lds_frag<T>(smem[buf] + l * TILE + kb * 32 * LRB + of.row_off[st]);
+          s[kb] = E::mma(kf, qf[l][st], (l == 0 && st == 0) ? f32x16{} : s[kb]);
+        }
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         const Frag vf = lds_frag<T>(sV + kb * 32 * LRB + of.row_off[st]);
@@ -470,7 +492,7 @@ __global__ __launch_bounds__(kBwdThreads, D == 256 ? 1 : 2) void fa_bwd_dq_kerne
         const Frag dsf = pack_half<T>(s[kb], h);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const Frag kt = lds_frag_tr<T>(sK + (kb * 32 + 16 * h) * LRB, of.tr_off[0][db], of.tr_off[1][db]);
+          const Frag kt = lds_frag_tr<T>(sKt + (kb * 32 + 16 * h) * LRB, of.tr_off[0][db], of.tr_off[1][db]);
           acc[db] = E::mma(kt, dsf, acc[db]);
         }
       }
@@ -499,22 +521,23 @@ __global__ __launch_bounds__(kBwdThreads, D == 256 ? 1 : 2) void fa_bwd_dq_kerne
 // dK, dV: one workgroup per (b, hk, 128-key block), 64-row query tiles over
 // the group's packed rows r = (hq - hk*group)*Nq + i (query position r % Nq).
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW>
-__global__ __launch_bounds__(kBwdThreads, (D == 64 ? (BIAS ? 2 : FA_DKDV_MINB64)
-                                                   : dkdv_pair(D, CAUSAL, BIAS) ? 2 : 1))
+template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW, int NL = 1>
+__global__ __launch_bounds__(kBwdThreads, (D == 64 ? ((BIAS || NL > 1) ? 2 : FA_DKDV_MINB64)
+                                                   : (dkdv_pair(D, CAUSAL, BIAS) && NL == 1) ? 2 : 1))
 void fa_bwd_dkdv_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
+  static_assert(NL == 1 || (!BIAS && !WINDOW && D <= 128), "chain instances");
   constexpr int BQ = dkdv_qtile(D, CAUSAL, BIAS);
   constexpr int NS = (D + 15) / 16, NDB = (D + 31) / 32, NQB = BQ / 32;
   constexpr int RB = D * 2;                   // bytes per row in HBM
   constexpr int LRB = lds_width(D) * 2;       // bytes per row in LDS
-  constexpr int TILE = BQ * LRB;              // bytes per Q (or dO) tile
+  constexpr int TILE = BQ * LRB;              // bytes per Q (or dO) tile (each layer's Q)
   constexpr bool K_LDS = dkdv_k_in_lds(D, CAUSAL, BIAS);  // the block's K in LDS, else registers
   constexpr bool V_LDS = dkdv_v_in_lds(D, CAUSAL, BIAS);  // the block's V in LDS, else registers
   constexpr int KB_BYTES = 128 * LRB;                       // bytes of the block's K (or V)
-  // per stage: Q tile, dO tile, lse2[BQ], delta[BQ]
-  constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
+  // per stage: the Q tiles of the NL layers, dO tile, lse2[BQ], delta[BQ]
+  constexpr int STAGE = (NL + 1) * TILE + 2 * BQ * 4;
   constexpr int KV_BYTES = (K_LDS ? KB_BYTES : 0) + (V_LDS ? KB_BYTES : 0);
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE + (KV_BYTES ? KV_BYTES : 16)];
 
@@ -542,12 +565,22 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int R = p.group * p.Nq;  // packed query rows of this KV head
   const T* Kh = static_cast<const T*>(p.k) + kv_head * p.Nk * D;
   const T* Vh = static_cast<const T*>(p.v) + kv_head * p.Nk * D;
-  const T* Qg = static_cast<const T*>(p.q) + row_base * D;
+
   const T* Gg = static_cast<const T*>(p.dout) + row_base * D;
   const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(Kh, uint32_t(p.Nk) * RB);
   const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(Vh, uint32_t(p.Nk) * RB);
-  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(Qg, uint32_t(R) * RB);
   const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(Gg, uint32_t(R) * RB);
+  __amdgpu_buffer_rsrc_t q_rs[NL], kl_rs[NL];
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    const T* Ql = static_cast<const T*>(NL > 1 ? p.chain_q[l] : p.q) + row_base * D;
+    const T* Kl = static_cast<const T*>(NL > 1 ? p.chain_k[l] : p.k) + kv_head * p.Nk * D;
+    q_rs[l] = make_rsrc(Ql, uint32_t(R) * RB);
+    kl_rs[l] = make_rsrc(Kl, uint32_t(p.Nk) * RB);
+  }
+  // the layer whose dK this launch forms; dV with the first launch only
+  const int tgt = NL > 1 ? p.target : 0;
+  const bool with_dv = NL == 1 || p.target == 0;
   const __amdgpu_buffer_rsrc_t l_rs = make_rsrc(p.lse2 + row_base, uint32_t(R) * 4);
   const __amdgpu_buffer_rsrc_t d_rs = make_rsrc(p.delta + row_base, uint32_t(R) * 4);
 
@@ -562,7 +595,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 
   // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T,
   // held in registers or read from the block's copy in LDS
-  Frag kf[K_LDS ? 1 : NS], vf[V_LDS ? 1 : NS];
+  Frag kf[NL][K_LDS ? 1 : NS], vf[V_LDS ? 1 : NS];
   char* sK = smem + 2 * STAGE;
   char* sV = sK + (K_LDS ? KB_BYTES : 0);
   if constexpr (K_LDS || V_LDS) {
@@ -575,7 +608,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   for (int st = 0; st < NS; ++st) {
     const int off = kj * RB + (16 * st + 8 * g) * 2;
     if constexpr (!K_LDS)
-      kf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(k_rs, off, 0, 0));
+#pragma unroll
+      for (int l = 0; l < NL; ++l)
+        kf[l][st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(kl_rs[l], off, 0, 0));
     if constexpr (!V_LDS)
       vf[st] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(v_rs, off, 0, 0));
   }
@@ -603,25 +638,27 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   auto issue = [&](int r0, int buf) {
     char* st = smem + buf * STAGE;
     const uint32_t soff = uint32_t(r0) * RB;
-    tl.issue(q_rs, st, wave, soff);
-    tl.issue(g_rs, st + TILE, wave, soff);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) tl.issue(q_rs[l], st + l * TILE, wave, soff);
+    tl.issue(g_rs, st + NL * TILE, wave, soff);
     // lse2 and delta: BQ floats each, 16 bytes per lane of waves 0 and 1
     if (wave == 0) {
       if (lane < BQ / 4)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(l_rs, (lds_void*)(st + 2 * TILE), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(l_rs, (lds_void*)(st + (NL + 1) * TILE), 16,
                                                  unsigned(lane * 16), uint32_t(r0) * 4, 0, 0);
     } else if (wave == 1) {
       if (lane < BQ / 4)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d_rs, (lds_void*)(st + 2 * TILE + BQ * 4), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d_rs, (lds_void*)(st + (NL + 1) * TILE + BQ * 4), 16,
                                                  unsigned(lane * 16), uint32_t(r0) * 4, 0, 0);
     }
   };
 
   auto compute = [&](int r0, int i0, int buf) {
     const auto ofs = of.fresh();
-    const char* sQ = smem + buf * STAGE;
-    const char* sG = sQ + TILE;
-    const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
+    const char* sQ = smem + buf * STAGE;            // layer 0's Q tile
+    const char* sQt = sQ + tgt * TILE;              // the target layer's
+    const char* sG = sQ + NL * TILE;
+    const float* sL = reinterpret_cast<const float*>(sQ + (NL + 1) * TILE);
     const float* sD = sL + BQ;
     // bias rows of this tile (reads past the group's rows or keys return 0)
     const T* btile = BIAS ? static_cast<const T*>(p.bias) + (row_base + r0) * p.Nk
@@ -635,14 +672,16 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       const int ib1 = min(ib0 + 31, p.Nq - 1);  // and of its last valid row
       if (CAUSAL && ib1 < kw0) continue;  // all masked
       if (W > 0 && ib0 > kw0 + 31 + W - 1) continue;
-      const bool want_dv = !TWO || pass == 0, want_dk = !TWO || pass == 1;
+      const bool want_dv = (!TWO || pass == 0) && with_dv, want_dk = !TWO || pass == 1;
       f32x16 s, dp = f32x16{};
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const Frag qa = lds_frag<T>(sQ + qb * 32 * LRB + ofs.row(st));
-        const Frag kb = K_LDS ? lds_frag<T>(sK + wave * 32 * LRB + ofs.row(st)) : kf[st];
-        s = E::mma(qa, kb, st == 0 ? f32x16{} : s);
-      }
+      for (int l = 0; l < NL; ++l)
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          const Frag qa = lds_frag<T>(sQ + l * TILE + qb * 32 * LRB + ofs.row(st));
+          const Frag kb = K_LDS ? lds_frag<T>(sK + wave * 32 * LRB + ofs.row(st)) : kf[l][st];
+          s = E::mma(qa, kb, (l == 0 && st == 0) ? f32x16{} : s);
+        }
       if (want_dk) {
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
@@ -705,7 +744,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             dva[db] = E::mma(gt, pf, dva[db]);
           }
           if (want_dk) {
-            const Frag qt = lds_frag_tr<T>(sQ + (qb * 32 + 16 * h) * LRB, ofs.tr(0, db), ofs.tr(1, db));
+            const Frag qt = lds_frag_tr<T>(sQt + (qb * 32 + 16 * h) * LRB, ofs.tr(0, db), ofs.tr(1, db));
             if constexpr (TWO) dva[db] = E::mma(qt, dsf, dva[db]);
             else dka[db] = E::mma(qt, dsf, dka[db]);
           }
@@ -749,7 +788,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       else store_rows<T, NDB, D>(dk_row, dva, p.scale, g, key_ok);
     } else {
       store_rows<T, NDB, D>(dk_row, dka, p.scale, g, key_ok);
-      store_rows<T, NDB, D>(dv_row, dva, 1.f, g, key_ok);
+      if (with_dv) store_rows<T, NDB, D>(dv_row, dva, 1.f, g, key_ok);
     }
   }
 }
@@ -796,7 +835,85 @@ hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool bias, hipStream_t 
 
 }  // namespace
 
+// Chain: one dQ and one dK/dV launch per layer t (target t), in order on the
+// stream; each dQ launch also rewrites the same row sums into the workspace,
+// which the dK/dV launch after it reads.
+template <typename T, int D, int NL>
+hipError_t launch_bwd_chain_nl(BwdParams& p, bool causal, hipStream_t s, unsigned g_dq,
+                               unsigned g_kv, void* const* dq_layers, void* const* dk_layers) {
+  const void* dq = causal ? reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, false, false, NL>)
+                          : reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, false, false, false, NL>);
+  const void* kv = causal ? reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, false, false, NL>)
+                          : reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, false, false, false, NL>);
+  for (int t = 0; t < NL; ++t) {
+    p.target = t;
+    p.dq = dq_layers[t];
+    p.dk = dk_layers[t];
+    void* args[] = {&p};  // (the arguments are copied at each launch)
+    hipError_t e = hipSuccess;
+    if (g_dq) e = hipLaunchKernel(dq, dim3(g_dq), dim3(kBwdThreads), args, 0, s);
+    if (e == hipSuccess && g_kv) e = hipLaunchKernel(kv, dim3(g_kv), dim3(kBwdThreads), args, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+static BwdParams make_bwd_params(const BwdArgs& a);
+
 int launch_backward(const BwdArgs& a) {
+  BwdParams p = make_bwd_params(a);
+  const unsigned g_dq = unsigned(p.n_qblk) * unsigned(p.BH);
+  const unsigned g_kv = unsigned(p.n_kblk) * unsigned(p.BHkv);
+  hipStream_t s = static_cast<hipStream_t>(a.stream);
+  hipError_t e;
+  auto launch = [&](auto tag) {
+    using T = decltype(tag);
+    switch (a.D) {
+      case 64: return launch_bwd_d<T, 64>(p, a.causal, a.bias, s, g_dq, g_kv);
+      case 80: return launch_bwd_d<T, 80>(p, a.causal, a.bias, s, g_dq, g_kv);
+      case 96: return launch_bwd_d<T, 96>(p, a.causal, a.bias, s, g_dq, g_kv);
+      case 256: return launch_bwd_d<T, 256>(p, a.causal, a.bias, s, g_dq, g_kv);
+      default: return launch_bwd_d<T, 128>(p, a.causal, a.bias, s, g_dq, g_kv);
+    }
+  };
+  if (a.dtype == FA_DTYPE_BF16) {
+    e = launch(__bf16{});
+  } else {
+    e = launch(_Float16{});
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int launch_backward_chain(const BwdArgs& a, const void* const* q_layers,
+                          const void* const* k_layers, void* const* dq_layers,
+                          void* const* dk_layers, int n_layers) {
+  if (n_layers == 1) return launch_backward(a);
+  BwdParams p = make_bwd_params(a);
+  for (int l = 0; l < kMaxChainLayers; ++l) {
+    p.chain_q[l] = l < n_layers ? q_layers[l] : nullptr;
+    p.chain_k[l] = l < n_layers ? k_layers[l] : nullptr;
+  }
+  const unsigned g_dq = unsigned(p.n_qblk) * unsigned(p.BH);
+  const unsigned g_kv = unsigned(p.n_kblk) * unsigned(p.BHkv);
+  hipStream_t s = static_cast<hipStream_t>(a.stream);
+  auto launch_d = [&](auto tag, auto dtag) {
+    using T = decltype(tag);
+    constexpr int D = decltype(dtag)::value;
+    switch (n_layers) {
+      case 2: return launch_bwd_chain_nl<T, D, 2>(p, a.causal, s, g_dq, g_kv, dq_layers, dk_layers);
+      case 3: return launch_bwd_chain_nl<T, D, 3>(p, a.causal, s, g_dq, g_kv, dq_layers, dk_layers);
+      default: return launch_bwd_chain_nl<T, D, 4>(p, a.causal, s, g_dq, g_kv, dq_layers, dk_layers);
+    }
+  };
+  auto launch = [&](auto tag) {
+    return a.D == 64 ? launch_d(tag, std::integral_constant<int, 64>{})
+                     : launch_d(tag, std::integral_constant<int, 128>{});
+  };
+  const hipError_t e = a.dtype == FA_DTYPE_BF16 ? launch(__bf16{}) : launch(_Float16{});
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+static BwdParams make_bwd_params(const BwdArgs& a) {
   BwdParams p;
   p.q = a.q;
   p.k = a.k;
@@ -824,26 +941,9 @@ int launch_backward(const BwdArgs& a) {
   p.scale = a.scale;
   p.bias_vec = (a.Nk % 4) == 0;
   p.window = a.window;
-  const unsigned g_dq = unsigned(p.n_qblk) * unsigned(p.BH);
-  const unsigned g_kv = unsigned(p.n_kblk) * unsigned(p.BHkv);
-  hipStream_t s = static_cast<hipStream_t>(a.stream);
-  hipError_t e;
-  auto launch = [&](auto tag) {
-    using T = decltype(tag);
-    switch (a.D) {
-      case 64: return launch_bwd_d<T, 64>(p, a.causal, a.bias, s, g_dq, g_kv);
-      case 80: return launch_bwd_d<T, 80>(p, a.causal, a.bias, s, g_dq, g_kv);
-      case 96: return launch_bwd_d<T, 96>(p, a.causal, a.bias, s, g_dq, g_kv);
-      case 256: return launch_bwd_d<T, 256>(p, a.causal, a.bias, s, g_dq, g_kv);
-      default: return launch_bwd_d<T, 128>(p, a.causal, a.bias, s, g_dq, g_kv);
-    }
-  };
-  if (a.dtype == FA_DTYPE_BF16) {
-    e = launch(__bf16{});
-  } else {
-    e = launch(_Float16{});
-  }
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  for (int l = 0; l < kMaxChainLayers; ++l) p.chain_q[l] = p.chain_k[l] = nullptr;
+  p.target = 0;
+  return p;
 }
 
 }  // namespace fa

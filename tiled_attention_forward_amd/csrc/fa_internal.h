@@ -70,6 +70,13 @@ struct BwdArgs {
 
 // Arguments are already validated.  Returns FA_OK or FA_ERR_HIP.
 int launch_backward(const BwdArgs& a);
+// Backward of the residual chain (n_layers 1 .. kMaxChainLayers, D = 64 or
+// 128, no bias or window): a as for the last layer (a.dq, a.dk unused),
+// q/k_layers the layers' inputs and dq/dk_layers their gradients, oldest
+// first; a.dv receives dV.
+int launch_backward_chain(const BwdArgs& a, const void* const* q_layers,
+                          const void* const* k_layers, void* const* dq_layers,
+                          void* const* dk_layers, int n_layers);
 
 // Backward workspace: delta fp32 [rows], then lse2 fp32 [rows] from the next
 // 256-byte boundary (rows = B*Hq*Nq).
