@@ -126,13 +126,20 @@ struct BwdParams {
   int window;    // causal sliding window (keys i-window+1 .. i), 0 = none
   int64_t rows;  // B * Hq * Nq
   // Block Attention Residual chain (NL > 1 instances): every layer's Q and K,
-  // oldest first (the logits are the sum of their products), and the layer
-  // whose dQ (dQ kernel) and dK (dK/dV kernel) this launch forms; dq and dk
-  // point at that layer's gradients, and dV is formed with target 0 only.
+  // oldest first (the logits are the sum of their products), their dQ and dK,
+  // and the first of the chain_targets(D, NL) layers whose dQ (dQ kernel) and
+  // dK (dK/dV kernel) this launch forms; dV is formed with target 0 only.
   const void* chain_q[kMaxChainLayers];
   const void* chain_k[kMaxChainLayers];
+  void* chain_dq[kMaxChainLayers];
+  void* chain_dk[kMaxChainLayers];
   int target;
 };
+
+// Chain layers whose gradients one launch forms: all of them at D = 64 (four
+// dQ or dK accumulators of 32 registers), two at D = 128 (64 each beside the
+// layers' Q or K fragments, 128 registers).
+constexpr int chain_targets(int D, int NL) { return D == 64 ? NL : (NL < 2 ? NL : 2); }
 
 // Direct LDS loads of an R x D tile (16-bit, row-major in HBM at a buffer
 // resource, first row at byte soff) into the swizzled LDS layout.  Load i of
@@ -293,7 +300,7 @@ __device__ __forceinline__ void store_rows(T* dst_row, const f32x16 (&acc)[NDB],
 // them in the workspace for the dK/dV kernel, which runs after it.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW, int NL = 1>
-__global__ __launch_bounds__(kBwdThreads, (D == 256 || (D == 128 && NL > 1)) ? 1 : 2)
+__global__ __launch_bounds__(kBwdThreads, (D == 256 || (D == 128 && NL > 1) || NL > 2) ? 1 : 2)
 void fa_bwd_dq_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
@@ -401,9 +408,13 @@ void fa_bwd_dq_kernel(BwdParams p) {
   Offsets<D> of;
   of.init(lane);
 
-  f32x16 acc[NDB];
+  // one accumulator set per target layer of this launch
+  constexpr int NT = chain_targets(D, NL);
+  f32x16 acc[NT][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[i][db] = f32x16{};
 
   int n_kv = (p.Nk + BN - 1) / BN;
   if (CAUSAL) n_kv = min(n_kv, blk_last / BN + 1);
@@ -418,11 +429,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
     tl.issue(v_rs, smem[buf] + NL * TILE, wave, uint32_t(j) * BN * RB);
   };
 
-  // (the K tile dQ is formed against: the target layer's)
+  // (the K tiles dQ is formed against: the target layers')
   const int tgt = NL > 1 ? p.target : 0;
   auto compute = [&](int j, int buf) {
     const char* sV = smem[buf] + NL * TILE;
-    const char* sKt = smem[buf] + tgt * TILE;
     const int key0 = j * BN;
     f32x16 s[NKB], dp[NKB];
 #pragma unroll
@@ -491,9 +501,14 @@ void fa_bwd_dq_kernel(BwdParams p) {
       for (int h = 0; h < 2; ++h) {
         const Frag dsf = pack_half<T>(s[kb], h);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const Frag kt = lds_frag_tr<T>(sKt + (kb * 32 + 16 * h) * LRB, of.tr_off[0][db], of.tr_off[1][db]);
-          acc[db] = E::mma(kt, dsf, acc[db]);
+        for (int i = 0; i < NT; ++i) {
+          if (NT > 1 && tgt + i >= NL) break;
+          const char* sKt = smem[buf] + (tgt + i) * TILE;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const Frag kt = lds_frag_tr<T>(sKt + (kb * 32 + 16 * h) * LRB, of.tr_off[0][db], of.tr_off[1][db]);
+            acc[i][db] = E::mma(kt, dsf, acc[i][db]);
+          }
         }
       }
   };
@@ -513,8 +528,12 @@ void fa_bwd_dq_kernel(BwdParams p) {
     __syncthreads();
   }
 
-  T* dst = static_cast<T*>(p.dq) + (row_base + qi) * D;
-  store_rows<T, NDB, D>(dst, acc, p.scale, g, row_ok);
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    if (NT > 1 && tgt + i >= NL) break;
+    T* dst = static_cast<T*>(NL > 1 ? p.chain_dq[tgt + i] : p.dq) + (row_base + qi) * D;
+    store_rows<T, NDB, D>(dst, acc[i], p.scale, g, row_ok);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -522,8 +541,9 @@ void fa_bwd_dq_kernel(BwdParams p) {
 // the group's packed rows r = (hq - hk*group)*Nq + i (query position r % Nq).
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW, int NL = 1>
-__global__ __launch_bounds__(kBwdThreads, (D == 64 ? ((BIAS || NL > 1) ? 2 : FA_DKDV_MINB64)
-                                                   : (dkdv_pair(D, CAUSAL, BIAS) && NL == 1) ? 2 : 1))
+__global__ __launch_bounds__(kBwdThreads, (NL > 2 ? 1
+                                          : D == 64 ? ((BIAS || NL > 1) ? 2 : FA_DKDV_MINB64)
+                                                    : (dkdv_pair(D, CAUSAL, BIAS) && NL == 1) ? 2 : 1))
 void fa_bwd_dkdv_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
@@ -619,7 +639,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   // otherwise one pass with both accumulators
   constexpr bool TWO = D == 256;
   int pass = 0;
-  f32x16 dva[NDB], dka[TWO ? 1 : NDB];
+  constexpr int NTG = chain_targets(D, NL);  // target layers of this launch (dK)
+  f32x16 dva[NDB], dka[NTG][TWO ? 1 : NDB];
 
   // Query tiles: BQ rows i0 .. i0+BQ-1 of one query head h of the group
   // (packed row r0 = h*Nq + i0), so a row's query position is i0 plus its
@@ -744,9 +765,14 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             dva[db] = E::mma(gt, pf, dva[db]);
           }
           if (want_dk) {
-            const Frag qt = lds_frag_tr<T>(sQt + (qb * 32 + 16 * h) * LRB, ofs.tr(0, db), ofs.tr(1, db));
-            if constexpr (TWO) dva[db] = E::mma(qt, dsf, dva[db]);
-            else dka[db] = E::mma(qt, dsf, dka[db]);
+#pragma unroll
+            for (int i = 0; i < NTG; ++i) {
+              if (NTG > 1 && tgt + i >= NL) break;
+              const Frag qt = lds_frag_tr<T>(sQt + i * TILE + (qb * 32 + 16 * h) * LRB,
+                                             ofs.tr(0, db), ofs.tr(1, db));
+              if constexpr (TWO) dva[db] = E::mma(qt, dsf, dva[db]);
+              else dka[i][db] = E::mma(qt, dsf, dka[i][db]);
+            }
           }
         }
       }
@@ -754,7 +780,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   };
 
   const bool key_ok = kj < p.Nk;
-  T* dk_row = static_cast<T*>(p.dk) + (kv_head * p.Nk + kj) * D;
+  const int64_t krow = (kv_head * p.Nk + kj) * D;
+  T* dk_row = static_cast<T*>(p.dk) + krow;
   T* dv_row = static_cast<T*>(p.dv) + (kv_head * p.Nk + kj) * D;
   // the visible tiles in order: head h, tile ti (i0 = ti * BQ)
   const int n_tiles = n_vis > 0 ? p.group * n_vis : 0;
@@ -762,7 +789,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       dva[db] = f32x16{};
-      if constexpr (!TWO) dka[db] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < NTG; ++i)
+        if constexpr (!TWO) dka[i][db] = f32x16{};
     }
     int h = 0, ti = ti_lo;
     if (n_tiles > 0) issue(ti * BQ, 0);
@@ -787,7 +816,12 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       if (pass == 0) store_rows<T, NDB, D>(dv_row, dva, 1.f, g, key_ok);
       else store_rows<T, NDB, D>(dk_row, dva, p.scale, g, key_ok);
     } else {
-      store_rows<T, NDB, D>(dk_row, dka, p.scale, g, key_ok);
+#pragma unroll
+      for (int i = 0; i < NTG; ++i) {
+        if (NTG > 1 && tgt + i >= NL) break;
+        T* row = NL > 1 ? static_cast<T*>(p.chain_dk[tgt + i]) + krow : dk_row;
+        store_rows<T, NDB, D>(row, dka[i], p.scale, g, key_ok);
+      }
       if (with_dv) store_rows<T, NDB, D>(dv_row, dva, 1.f, g, key_ok);
     }
   }
@@ -835,9 +869,10 @@ hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool bias, hipStream_t 
 
 }  // namespace
 
-// Chain: one dQ and one dK/dV launch per layer t (target t), in order on the
-// stream; each dQ launch also rewrites the same row sums into the workspace,
-// which the dK/dV launch after it reads.
+// Chain: one dQ and one dK/dV launch per group of chain_targets(D, NL) layers
+// (targets t .. t + NT - 1), in order on the stream; each dQ launch also
+// rewrites the same row sums into the workspace, which the dK/dV launch after
+// it reads.
 template <typename T, int D, int NL>
 hipError_t launch_bwd_chain_nl(BwdParams& p, bool causal, hipStream_t s, unsigned g_dq,
                                unsigned g_kv, void* const* dq_layers, void* const* dk_layers) {
@@ -845,10 +880,12 @@ hipError_t launch_bwd_chain_nl(BwdParams& p, bool causal, hipStream_t s, unsigne
                           : reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, false, false, false, NL>);
   const void* kv = causal ? reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, false, false, NL>)
                           : reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, false, false, false, NL>);
-  for (int t = 0; t < NL; ++t) {
+  for (int l = 0; l < NL; ++l) {
+    p.chain_dq[l] = dq_layers[l];
+    p.chain_dk[l] = dk_layers[l];
+  }
+  for (int t = 0; t < NL; t += chain_targets(D, NL)) {
     p.target = t;
-    p.dq = dq_layers[t];
-    p.dk = dk_layers[t];
     void* args[] = {&p};  // (the arguments are copied at each launch)
     hipError_t e = hipSuccess;
     if (g_dq) e = hipLaunchKernel(dq, dim3(g_dq), dim3(kBwdThreads), args, 0, s);
@@ -941,7 +978,10 @@ static BwdParams make_bwd_params(const BwdArgs& a) {
   p.scale = a.scale;
   p.bias_vec = (a.Nk % 4) == 0;
   p.window = a.window;
-  for (int l = 0; l < kMaxChainLayers; ++l) p.chain_q[l] = p.chain_k[l] = nullptr;
+  for (int l = 0; l < kMaxChainLayers; ++l) {
+    p.chain_q[l] = p.chain_k[l] = nullptr;
+    p.chain_dq[l] = p.chain_dk[l] = nullptr;
+  }
   p.target = 0;
   return p;
 }
