@@ -157,6 +157,44 @@ def cpu_baseline_backward(w, q, k, v, dout, target_s: float):
                       f"fp64 NumPy, {t_used:.1f} s"}
 
 
+def chain_backward_factor(layers: int) -> float:
+    """Products of the chain backward per visible pair against the chain
+    forward's: the logits (layers), dP, dQ and dK of every layer, and dV, so
+    3*layers + 2 against layers + 1."""
+    return (3 * layers + 2) / (layers + 1)
+
+
+def cpu_baseline_chain_backward(w, q_layers, k_layers, v, dout, target_s: float):
+    """Time the oracle's chain backward on whole (batch, KV head) groups until
+    about target_s."""
+    import numpy as np
+
+    from oracle import attention_chain_backward
+
+    grp = w.Hq // w.Hkv
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    done, t_used = 0, 0.0
+    for b in range(w.B):
+        for hk in range(w.Hkv):
+            hs = slice(hk * grp, (hk + 1) * grp)
+            qs = [f(t[b:b + 1, hs]) for t in q_layers]
+            ks = [f(t[b:b + 1, hk:hk + 1]) for t in k_layers]
+            t0 = time.perf_counter()
+            attention_chain_backward(qs, ks, f(v[b:b + 1, hk:hk + 1]), f(dout[b:b + 1, hs]),
+                                     scale=w.scale, causal=w.causal)
+            t_used += time.perf_counter() - t0
+            done += grp
+            if t_used >= target_s:
+                break
+        if t_used >= target_s:
+            break
+    per_head = chain_backward_factor(w.layers) * w.useful_flops() / (w.B * w.Hq)
+    return {"value": round(per_head * done / t_used / 1e12, 6), "unit": "TFLOPS",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"chain backward of {done} of {w.B * w.Hq} (batch, head) slices of "
+                      f"{w.name}, fp64 NumPy, {t_used:.1f} s"}
+
+
 def cpu_baseline_chain(w, q_layers, k_layers, v, target_s: float, o_gpu=None, lse_gpu=None):
     """Time the oracle's chain on whole heads until about target_s (and the
     error of the GPU output on those heads)."""
@@ -337,10 +375,27 @@ def main():
                  w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal), dtype_code)
     splits = None
     backward = args.pass_ == "backward"
-    if w.layers and (backward or w.path != "fused"):
-        print("the chain workload is timed on the fused forward only", file=sys.stderr)
+    if w.layers and w.path != "fused":
+        print("the chain workload is timed on its fused path only", file=sys.stderr)
         sys.exit(2)
-    if backward:
+    if backward and w.layers:
+        import ctypes
+        g = torch.Generator(device=dev).manual_seed(args.seed + 1000)
+        dout = torch.randn(q.shape, generator=g, device=dev).to(q.dtype)
+        binding.forward_chain(q_layers, k_layers, v, causal=w.causal, scale=w.scale, out=o,
+                              lse=lse)
+        dqs = [torch.empty_like(t) for t in q_layers]
+        dks = [torch.empty_like(t) for t in k_layers]
+        dv = torch.empty_like(v)
+        ws_bytes = binding.fa_backward_workspace_bytes(w.B, w.Hq, w.Nq)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        arr = lambda ts: (ctypes.c_void_p * w.layers)(*[t.data_ptr() for t in ts])  # noqa: E731
+        entry = lib.fa_backward_chain
+        call_args = (arr(q_layers), arr(k_layers), w.layers, v.data_ptr(), o.data_ptr(),
+                     lse.data_ptr(), dout.data_ptr(), arr(dqs), arr(dks), dv.data_ptr(), w.B,
+                     w.Hq, w.Hkv, w.Nq, w.Nk, w.D, float(w.scale), int(w.causal), dtype_code,
+                     workspace.data_ptr(), ws_bytes, stream.cuda_stream)
+    elif backward:
         if w.bias or w.dtype in ("fp32", "fp8"):
             print("the backward is timed on bias-free 16-bit workloads", file=sys.stderr)
             sys.exit(2)
@@ -425,7 +480,8 @@ def main():
     mem_peak = torch.cuda.max_memory_allocated(dev)
     assert torch.isfinite(lse).all(), "non-finite LSE in the benchmark output"
 
-    fl = BACKWARD_FLOP_FACTOR if backward else 1.0
+    fl = (chain_backward_factor(w.layers) if w.layers else BACKWARD_FLOP_FACTOR) if backward \
+        else 1.0
     # windowed attention: count the visible pairs only (the dense formula
     # would credit work the window removes)
     metric_flops = w.useful_flops() if (w.window or w.layers) else w.metric_flops()
@@ -442,7 +498,10 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
     roof["traffic"] = traffic_for(w.name, args.pass_)
 
-    if w.layers:
+    if w.layers and backward:
+        metric = (f"chain attention backward TFLOPS over visible pairs "
+                  f"(2·D·(3·layers+2)·pairs/t) at {w.name}")
+    elif w.layers:
         metric = (f"chain attention TFLOPS over visible pairs (2·D·(layers+1)·pairs/t) at "
                   f"{w.name}")
     elif w.window:
@@ -493,7 +552,10 @@ def main():
     if not args.no_cpu_baseline:
         # the oracle on the host; for the forward its results on the heads it
         # ran also give the error of this run's GPU output there
-        if backward:
+        if backward and w.layers:
+            out["cpu_baseline"] = cpu_baseline_chain_backward(w, q_layers, k_layers, v, dout,
+                                                              args.cpu_seconds)
+        elif backward:
             out["cpu_baseline"] = cpu_baseline_backward(w, q, k, v, dout, args.cpu_seconds)
         elif w.layers:
             out["cpu_baseline"], out["error_vs_oracle"] = cpu_baseline_chain(
