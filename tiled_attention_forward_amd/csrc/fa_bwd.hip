@@ -12,7 +12,8 @@
 // tiles), so no atomics are needed and the results are deterministic, at the
 // price of computing S and dP twice.
 //
-// Kernels (16-bit types, D in {64, 128}), launched in this order:
+// Kernels (16-bit types; D = 64, 128, and 80, 96 in 128-wide tiles, 256
+// without a logit term), launched in this order:
 //  * fa_bwd_dq_kernel: the forward's layout -- each wave owns 32 query rows,
 //    one per lane; S^T = K Q^T and dP^T = V dO^T on 32x32x16 MFMAs with Q and
 //    dO rows held in registers and K/V tiles streamed through LDS; then
@@ -26,6 +27,12 @@
 //    dK^T += Q^T dS with Q and dO read transposed from LDS.
 // P and dS are rounded to the input type for the MFMAs (as P is in the
 // forward); all sums are fp32.
+//
+// The Block Attention Residual chain (NL = 2-4 layers, the "Block Attention
+// Residual" post): the logits are the sum of every layer's Q_l K_l^T * scale,
+// so both kernels take every layer's Q and K, form S from all their products,
+// and then dQ_l = scale dS K_l (dQ kernel) and dK_l = scale dS^T Q_l (dK/dV
+// kernel) for a group of layers per launch.
 //
 // LDS tiles are row-major and unpadded, filled straight from HBM by buffer
 // loads with the LDS flag; the 16-byte chunk c of tile row r is stored at
