@@ -53,53 +53,21 @@ namespace {
 
 constexpr int kWaves = 4;              // waves per workgroup
 constexpr int kThreads = kWaves * 64;
+// Build-time tuning knobs.  The defaults are the measured best on MI355X; a
+// variant is compiled with -D<knob>=<value> (build.build(extra_flags=...)).
+// Keys per K/V tile and 32-row query blocks per wave of the fused instances:
 #ifndef FA_BN64
-#define FA_BN64 64
+#define FA_BN64 64  // D = 64
 #endif
 #ifndef FA_BN128
-#define FA_BN128 64
+#define FA_BN128 64  // D = 80, 96, 128 (those the two lines further down do not set)
 #endif
 #ifndef FA_QB64
-#define FA_QB64 1
+#define FA_QB64 1  // D = 64, 16-bit, no bias
 #endif
 #ifndef FA_QB128
-#define FA_QB128 1
+#define FA_QB128 1  // D = 128 instances other than the non-causal bias-free one
 #endif
-#ifndef FA_MINB64
-#define FA_MINB64 2
-#endif
-// Key-split instances at D = 128 without a bias (decode-like shapes, bound by
-// the K/V stream): 32-key tiles, 163-166 VGPRs, so three workgroups fit a
-// compute unit (decode B8 20/4 heads, 32768 keys: 96.2 us against 100.5 with
-// 64-key tiles; a third LDS buffer adds nothing, 96.8 us).
-#ifndef FA_OPAQUE_KOFF
-#define FA_OPAQUE_KOFF 1
-#endif
-#ifndef FA_SCALAR_WAVE
-#define FA_SCALAR_WAVE 1
-#endif
-#ifndef FA_SPLIT_KV_STREAM
-#define FA_SPLIT_KV_STREAM 1
-#endif
-constexpr int kPolicyNT = 2;  // buffer-load cache policy: non-temporal
-#ifndef FA_SPLIT_BN128
-#define FA_SPLIT_BN128 32
-#endif
-// Key halves per workgroup of the causal D = 64 fused instances (1 or 2)
-#ifndef FA_BIAS_LDS
-#define FA_BIAS_LDS 1
-#endif
-#ifndef FA_KH64
-#define FA_KH64 1
-#endif
-#ifndef FA_KH64_F8
-#define FA_KH64_F8 2
-#endif
-
-constexpr int kBN64 = FA_BN64;         // keys per K/V tile, D = 64
-constexpr int kBN128 = FA_BN128;       // keys per K/V tile, D = 128
-constexpr int kQB64 = FA_QB64;         // 32-row query blocks per wave, D = 64
-constexpr int kQB128 = FA_QB128;       // 32-row query blocks per wave, D = 128
 // 16-bit fused non-causal instances at D = 128 without a bias: two 32-row
 // query blocks per wave over 32-key tiles (256 VGPRs; the 24-byte spill is
 // the prologue's and the epilogue's, none in the loop), which halves the LDS
@@ -111,6 +79,47 @@ constexpr int kQB128 = FA_QB128;       // 32-row query blocks per wave, D = 128
 #ifndef FA_BN128N
 #define FA_BN128N 32
 #endif
+// Workgroups per compute unit asked of the compiler at D = 64
+#ifndef FA_MINB64
+#define FA_MINB64 2
+#endif
+// K fragment offsets kept opaque to the compiler (one add per read)
+#ifndef FA_OPAQUE_KOFF
+#define FA_OPAQUE_KOFF 1
+#endif
+// The wave index read as a scalar, so the direct-load destinations are scalar
+#ifndef FA_SCALAR_WAVE
+#define FA_SCALAR_WAVE 1
+#endif
+// Key-split instances over one row block (decode): K/V loads non-temporal
+#ifndef FA_SPLIT_KV_STREAM
+#define FA_SPLIT_KV_STREAM 1
+#endif
+constexpr int kPolicyNT = 2;  // buffer-load cache policy: non-temporal
+// Key-split instances at D = 128 without a bias (decode-like shapes, bound by
+// the K/V stream): 32-key tiles, 163-166 VGPRs, so three workgroups fit a
+// compute unit (decode B8 20/4 heads, 32768 keys: 96.2 us against 100.5 with
+// 64-key tiles; a third LDS buffer adds nothing, 96.8 us).
+#ifndef FA_SPLIT_BN128
+#define FA_SPLIT_BN128 32
+#endif
+// Logit tiles staged through LDS by direct loads (16-bit, 64-key tiles)
+#ifndef FA_BIAS_LDS
+#define FA_BIAS_LDS 1
+#endif
+// Key halves per workgroup of the causal D = 64 fused instances (1 or 2):
+// 16-bit, and FP8
+#ifndef FA_KH64
+#define FA_KH64 1
+#endif
+#ifndef FA_KH64_F8
+#define FA_KH64_F8 2
+#endif
+
+constexpr int kBN64 = FA_BN64;         // keys per K/V tile, D = 64
+constexpr int kBN128 = FA_BN128;       // keys per K/V tile, D = 128
+constexpr int kQB64 = FA_QB64;         // 32-row query blocks per wave, D = 64
+constexpr int kQB128 = FA_QB128;       // 32-row query blocks per wave, D = 128
 constexpr int kQB128N = FA_QB128N;
 constexpr int kBN128N = FA_BN128N;
 constexpr float kTau = 8.f;            // lazy-rescale threshold (log2 units)
