@@ -13,8 +13,9 @@ Each case therefore places Q, K, V, the bias (and for the backward dO) in
 device memory whose neighbours are NaN: the heads of one KV group carry real
 values, every other head and the padding after the last head hold NaN, all
 inside one allocation (so no access leaves it).  The checked heads must give
-finite results that match the oracle, for the fused, key-split, window and
-backward paths, with Nq and Nk not multiples of the tile sizes.
+finite results that match the oracle, for the fused, key-split, window,
+backward and residual-chain (forward and backward) paths, with Nq and Nk not
+multiples of the tile sizes.
 """
 
 import numpy as np
@@ -144,3 +145,59 @@ def test_backward_reads_stay_in_the_head(gpu_device, case, group_checked):
                               window=window)
     got = (dq[:, heads], dk[:, [heads[0] // grp]], dv[:, [heads[0] // grp]])
     _log(compare(got, refs, w.dtype, str(case)))
+
+
+CHAIN_CASES = [
+    # layers, B, Hq, Hkv, Nq, Nk, D, dtype, causal
+    (3, 1, 4, 2, 200, 333, 64, "bf16", True),
+    (2, 1, 4, 2, 130, 70, 128, "fp16", False),
+    (4, 1, 4, 2, 97, 161, 128, "bf16", True),
+]
+
+
+def _chain_setup(case, group_checked, dev, seed=9):
+    """Every layer's Q and K, and V, in NaN-neighboured allocations; returns
+    the device tensors, the checked heads' host slices and the buffers."""
+    from tiled_attention_forward_amd.workloads import make_chain_inputs
+    n, B, Hq, Hkv, Nq, Nk, D, dt, causal = case
+    w = custom(B, Hq, Hkv, Nq, Nk, D, dt, causal, False)
+    qs, ks, v = make_chain_inputs(w, n, seed=seed)
+    grp = Hq // Hkv
+    heads = list(range(group_checked * grp, (group_checked + 1) * grp))
+    dev_q = [_poisoned(t, heads, dev) for t in qs]
+    dev_k = [_poisoned(t, [group_checked], dev) for t in ks]
+    vd, vbuf = _poisoned(v, [group_checked], dev)
+    host = ([t[:, heads] for t in qs], [t[:, [group_checked]] for t in ks],
+            v[:, [group_checked]])
+    dev_t = ([t for t, _ in dev_q], [t for t, _ in dev_k], vd)
+    bufs = [b for _, b in dev_q] + [b for _, b in dev_k] + [vbuf]
+    return w, heads, dev_t, host, bufs
+
+
+@pytest.mark.parametrize("group_checked", [0, 1])
+@pytest.mark.parametrize("case", CHAIN_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_chain_reads_stay_in_the_head(gpu_device, case, group_checked):
+    """Chain forward and backward (every layer's Q and K streamed per tile)."""
+    from oracle import attention_chain, attention_chain_backward
+    _log(f"chain tail case {case} group {group_checked}")
+    w, heads, (qs, ks, v), (hq, hk, hv), bufs = _chain_setup(case, group_checked, gpu_device)
+    o, lse = binding.forward_chain(qs, ks, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = attention_chain([f64(t) for t in hq], [f64(t) for t in hk], f64(hv),
+                                   scale=w.scale, causal=w.causal)
+    st = errors(f64(o[:, heads]), lse[:, heads].cpu().numpy(), o_ref, l_ref)
+    _log(st)
+    assert_within(st, w.dtype, str(case))
+
+    g = torch.Generator().manual_seed(78)
+    dout_h = torch.randn(qs[-1].shape, generator=g).to(qs[-1].dtype)
+    dout, dbuf = _poisoned(dout_h, heads, gpu_device)
+    dqs, dks, dv = binding.backward_chain(qs, ks, v, o, lse, dout, causal=w.causal,
+                                          scale=w.scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = attention_chain_backward([f64(t) for t in hq], [f64(t) for t in hk], f64(hv),
+                                          f64(dout_h[:, heads]), scale=w.scale, causal=w.causal)
+    hk0 = heads[0] // (w.Hq // w.Hkv)
+    for l in range(case[0]):
+        got = (dqs[l][:, heads], dks[l][:, [hk0]], dv[:, [hk0]])
+        _log(l, compare(got, (rq[l], rk[l], rv), w.dtype, f"{case} layer {l}"))
