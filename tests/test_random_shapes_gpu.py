@@ -1,5 +1,5 @@
-"""Seeded random sweep of the forward entry points, and of the backward,
-against the oracle.
+"""Seeded random sweep of the forward entry points, of the backward and of
+the residual chain (forward and backward), against the oracle.
 
 Each case draws a shape (batch, query heads, KV-head group, query and key
 counts with ragged tails), an element type, a head dimension, the causal flag,
@@ -130,3 +130,56 @@ def test_random_backward_case(gpu_device, case):
                               scale=w.scale, causal=causal, window=window)
     atol = cancellation_floor(q, k, v, dout, w.scale)
     print(compare((dq, dk, dv), refs, dt, str(case), atol=atol), flush=True)
+
+
+def _chain_cases(n=24, seed=6060):
+    r = random.Random(seed)
+    out = []
+    while len(out) < n:
+        layers = r.choice([1, 2, 3, 4])
+        D = r.choice([64, 128])
+        dtype = r.choice(["bf16", "fp16"])
+        causal = r.random() < 0.5
+        hkv = r.choice([1, 2, 3])
+        group = r.choice([1, 2, 5])
+        nq = r.choice([1, 7, 64, 127, 200, 333])
+        nk = r.choice([1, 63, 64, 65, 190, 400]) if not causal else r.choice([nq, nq + 17, 300])
+        out.append((layers, r.choice([1, 2]), hkv * group, hkv, nq, nk, D, dtype, causal))
+    return out
+
+
+@pytest.mark.parametrize("case", _chain_cases(), ids=lambda c: "-".join(map(str, c)))
+def test_random_chain_case(gpu_device, case):
+    """The residual chain (fa_forward_chain, then fa_backward_chain) on the same
+    kind of sweep: O and LSE at the forward's bars (with the output-spacing
+    rule), every layer's dQ and dK and dV at the backward's."""
+    from oracle import attention_chain, attention_chain_backward
+    from tests.parity import O_TOL, assert_within, errors, f64, output_spacing_check
+    from tests.test_backward_gpu import cancellation_floor, compare
+    from tiled_attention_forward_amd.workloads import make_chain_inputs
+    layers, B, Hq, Hkv, Nq, Nk, D, dt, causal = case
+    print(f"random chain case {case}", flush=True)
+    w = custom(B, Hq, Hkv, Nq, Nk, D, dt, causal, False)
+    seed = zlib.crc32(repr(case).encode()) % 100000
+    qs, ks, v = make_chain_inputs(w, layers, seed=seed)
+    qs, ks, v = [t.to(gpu_device) for t in qs], [t.to(gpu_device) for t in ks], v.to(gpu_device)
+    g = torch.Generator().manual_seed(seed + 1)
+    dout = torch.randn(qs[-1].shape, generator=g).to(qs[-1].dtype).to(gpu_device)
+    o, lse = binding.forward_chain(qs, ks, v, causal=causal, scale=w.scale)
+    dqs, dks, dv = binding.backward_chain(qs, ks, v, o, lse, dout, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    hq, hk = [f64(t) for t in qs], [f64(t) for t in ks]
+    o_ref, l_ref = attention_chain(hq, hk, f64(v), scale=w.scale, causal=causal)
+    st = errors(f64(o), lse.cpu().numpy(), o_ref, l_ref)
+    if st["max_abs"] > O_TOL[dt][0]:
+        output_spacing_check(f64(o), o_ref, st, dt, str(case))
+    else:
+        assert_within(st, dt, str(case))
+    rq, rk, rv = attention_chain_backward(hq, hk, f64(v), f64(dout), scale=w.scale,
+                                          causal=causal)
+    # the one-layer backward's cancellation floor (dP - D_i is a contraction
+    # over D whatever the chain length), with each layer's Q and K
+    atol = max(cancellation_floor(ql, kl, v, dout, w.scale) for ql, kl in zip(qs, ks))
+    for l in range(layers):
+        print(l, compare((dqs[l], dks[l], dv), (rq[l], rk[l], rv), dt, f"{case} layer {l}",
+                         atol=atol), flush=True)
