@@ -1,5 +1,6 @@
-"""Seeded random sweep of the forward entry points, of the backward and of
-the residual chain (forward and backward), against the oracle.
+"""Seeded random sweep of the forward entry points (16-bit, fp32 and FP8
+inputs), of the backward and of the residual chain (forward and backward),
+against the oracle.
 
 Each case draws a shape (batch, query heads, KV-head group, query and key
 counts with ragged tails), an element type, a head dimension, the causal flag,
@@ -183,3 +184,37 @@ def test_random_chain_case(gpu_device, case):
     for l in range(layers):
         print(l, compare((dqs[l], dks[l], dv), (rq[l], rk[l], rv), dt, f"{case} layer {l}",
                          atol=atol), flush=True)
+
+
+def _fp8_cases(n=16, seed=7070):
+    r = random.Random(seed)
+    out = []
+    while len(out) < n:
+        D = r.choice([64, 128])
+        causal = r.random() < 0.5
+        hkv = r.choice([1, 2, 3])
+        group = r.choice([1, 2, 5])
+        nq = r.choice([1, 7, 64, 127, 200, 333])
+        nk = r.choice([1, 63, 64, 65, 190, 400]) if not causal else r.choice([nq, nq + 17, 300])
+        splits = r.choice([None, None, 2, 3])
+        out.append((r.choice([1, 2]), hkv * group, hkv, nq, nk, D, causal, splits))
+    return out
+
+
+@pytest.mark.parametrize("case", _fp8_cases(), ids=lambda c: "-".join(map(str, c)))
+def test_random_fp8_case(gpu_device, case):
+    """FP8 (E4M3) inputs through the fused path or the key split, at the bound
+    of tests/parity.py ``fp8_bound_check``."""
+    from tests.parity import fp8_bound_check
+    B, Hq, Hkv, Nq, Nk, D, causal, splits = case
+    print(f"random fp8 case {case}", flush=True)
+    w = custom(B, Hq, Hkv, Nq, Nk, D, "fp8", causal, False)
+    seed = zlib.crc32(repr(case).encode()) % 100000
+    q, k, v = (t.to(gpu_device) for t in make_inputs(w, seed=seed)[:3])
+    if splits is None:
+        o, lse = binding.forward(q, k, v, None, causal=causal, scale=w.scale)
+    else:
+        o, lse = binding.forward_split(q, k, v, None, causal=causal, scale=w.scale,
+                                       num_splits=splits)
+    torch.cuda.synchronize()
+    fp8_bound_check(q, k, v, w.scale, causal, o, lse, str(case))
