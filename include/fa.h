@@ -295,17 +295,20 @@ int fa_merge(const float* part_o, const float* part_lse, int64_t num_parts, int6
  *   workspace: device scratch owned by the caller, 16-byte aligned, at least
  *     fa_backward_workspace_bytes(B, Hq, Nq) bytes; holds D_i and LSE_i*log2(e)
  *     (float32) on return.  NULL is allowed when B*Hq*Nq == 0.
- * bf16 and fp16 only (FA_ERR_DTYPE for fp32); head sizes 64, 80, 96, 128, and
- * 256 without a logit term (FA_ERR_HEAD_DIM for 256 with one).  Products run on the matrix
- * cores with float32 accumulation; P and dS are rounded to the input type
- * before their products, as P is in the forward.  Results are deterministic
- * (no atomics: dQ has its own kernel).  Errors as for fa_forward, plus
+ * bf16 and fp16: head sizes 64, 80, 96, 128, and 256 without a logit term
+ * (FA_ERR_HEAD_DIM for 256 with one).  Products run on the matrix cores with
+ * float32 accumulation; P and dS are rounded to the input type before their
+ * products, as P is in the forward.  Two kernels are enqueued on stream (dQ,
+ * which also forms the row sums D_i, then dK/dV).  fp32: head sizes 64 and
+ * 128 (FA_ERR_HEAD_DIM otherwise), every step in fp32 vector arithmetic with
+ * no rounding of P or dS; three kernels (dQ with D_i, then dV, then dK).
+ * FP8 has no backward (FA_ERR_DTYPE).  Results are deterministic (no atomics:
+ * dQ has its own kernel).  Errors as for fa_forward, plus
  * FA_ERR_NULL_POINTER for a missing dout/dq (rows present) or dk/dv/k/v (keys
  * present), FA_ERR_WORKSPACE, and FA_ERR_OVERLAP if dq, dk, dv or the
  * workspace overlap an input or each other.  With no query rows (B, Hq or
- * Nq == 0) but keys present, dk and dv are set to zero.  Two kernels are
- * enqueued on stream (dQ, which also forms the row sums D_i, then dK/dV); the
- * call returns without waiting.
+ * Nq == 0) but keys present, dk and dv are set to zero.  The call returns
+ * without waiting.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* bias,
                 const void* o, const float* lse, const void* dout,

@@ -11,6 +11,11 @@ O, and each gradient is rounded once more on output.  Each source moves an
 element by about u relative to the gradient's own scale, so per tensor:
     bf16: max |dG - dG_ref| <= 3e-2 * max |dG_ref|,  mean <= 1e-2 * mean |dG_ref|
     fp16: max |dG - dG_ref| <= 6e-3 * max |dG_ref|,  mean <= 2e-3 * mean |dG_ref|
+fp32 inputs take no rounding of P or dS: every step is an fp32 operation, the
+longest sums run over Nk keys or D columns (relative error up to about
+(Nk + D) 2^-24 in the worst case, 1e-6 typically), and exp2 is v_exp_f32
+(about one ulp).  So
+    fp32: max |dG - dG_ref| <= 1e-4 * max |dG_ref|,  mean <= 1e-5 * mean |dG_ref|
 """
 
 import numpy as np
@@ -24,7 +29,7 @@ from tiled_attention_forward_amd.workloads import WORKLOADS, custom, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": (3e-2, 1e-2), "fp16": (6e-3, 2e-3)}
+TOL = {"bf16": (3e-2, 1e-2), "fp16": (6e-3, 2e-3), "fp32": (1e-4, 1e-5)}
 
 
 def _log(*a):
@@ -106,6 +111,14 @@ CASES = [
     (1, 4, 2, 97, 200, 256, "fp16", False, False),   # group 2: row tiles cross heads
     (1, 3, 1, 33, 31, 256, "bf16", True, False),     # group 3, rows < one tile, key tail
     (1, 2, 2, 300, 129, 256, "bf16", False, False),
+    # fp32 (head sizes 64 and 128): plain fp32 arithmetic, one row or key per lane
+    (1, 1, 1, 256, 256, 64, "fp32", False, False),    # the fp32 parity workload's shape
+    (1, 2, 2, 200, 200, 64, "fp32", True, False),
+    (2, 4, 2, 130, 170, 64, "fp32", True, True),
+    (1, 4, 1, 100, 300, 128, "fp32", True, False),    # group 4
+    (1, 3, 1, 97, 64, 128, "fp32", False, True),      # group 3, bias
+    (1, 2, 2, 1, 1, 128, "fp32", False, False),
+    (1, 5, 1, 300, 129, 64, "fp32", False, False),    # group 5, key tail
 ]
 
 
@@ -182,6 +195,8 @@ WINDOW_CASES = [
     (1, 3, 1, 20, 20, 128, "bf16", False, 6),         # group 3, fewer rows than a tile
     (1, 2, 2, 200, 200, 96, "bf16", False, 50),
     (1, 4, 2, 150, 180, 80, "fp16", True, 64),
+    (1, 2, 2, 300, 300, 64, "fp32", False, 37),
+    (1, 4, 1, 200, 260, 128, "fp32", True, 100),      # GQA, bias, Nk > Nq
 ]
 
 

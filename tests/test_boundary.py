@@ -293,7 +293,12 @@ def test_backward_workspace_bytes():
 
 
 def test_backward_rejections_before_launch():
-    assert bwd_status(dtype=binding.FA_DTYPE_FP32) == 5       # 16-bit types only
+    assert bwd_status(dtype=binding.FA_DTYPE_FP8_E4M3) == 5   # no FP8 backward
+    # fp32: head sizes 64 and 128 (as its forward); those pass to the workspace check
+    assert bwd_status(dtype=binding.FA_DTYPE_FP32, D=96) == 4
+    assert bwd_status(dtype=binding.FA_DTYPE_FP32, D=256) == 4
+    assert bwd_status(dtype=binding.FA_DTYPE_FP32, workspace=None) == 11
+    assert bwd_status(dtype=binding.FA_DTYPE_FP32, D=128, workspace=None) == 11
     assert bwd_status(D=72) == 4 and bwd_status(q=None) == 1   # the forward's checks first
     assert bwd_status(D=256, bias=BIAS) == 4                   # D = 256 takes no logit term
     assert bwd_status(D=256, workspace=None) == 11             # D = 256 passes the head check
@@ -327,7 +332,8 @@ def test_window_rejections_before_launch():
     bargs = (a["q"], a["k"], a["v"], None, a["o"], a["lse"], GO, DQ, DK, DV, a["B"], a["Hq"],
              a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"])
     assert lib.fa_backward_window(*bargs, 0, a["dtype"], WS, 1 << 40, None) == 2
-    assert lib.fa_backward_window(*bargs, 8, binding.FA_DTYPE_FP32, WS, 1 << 40, None) == 5
+    assert lib.fa_backward_window(*bargs, 8, binding.FA_DTYPE_FP8_E4M3, WS, 1 << 40, None) == 5
+    assert lib.fa_backward_window(*bargs, 8, binding.FA_DTYPE_FP32, None, 0, None) == 11
     assert lib.fa_backward_window(*bargs[:15], 256, a["scale"], 8, a["dtype"], WS, 1 << 40,
                                   None) == 4   # no window at D = 256, as in the forward
 

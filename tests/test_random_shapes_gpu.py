@@ -95,8 +95,8 @@ def _backward_cases(n=40, seed=4048):
     r = random.Random(seed)
     out = []
     while len(out) < n:
-        dtype = r.choice(["bf16", "bf16", "fp16"])
-        D = r.choice([64, 80, 96, 128, 256])
+        dtype = r.choice(["bf16", "bf16", "fp16", "fp32"])
+        D = r.choice([64, 128] if dtype == "fp32" else [64, 80, 96, 128, 256])
         # (head size 256: no logit term and no window in the backward)
         window = None if D == 256 else r.choice([None, None, None, 1, 16, 100])
         causal = window is not None or r.random() < 0.5

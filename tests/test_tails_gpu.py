@@ -123,6 +123,9 @@ BWD_CASES = [
     (1, 4, 2, 130, 170, 80, "bf16", False, False, None),
     (1, 4, 2, 77, 129, 96, "fp16", True, True, None),
     (1, 4, 2, 131, 170, 256, "bf16", True, False, None),
+    (1, 4, 2, 130, 170, 64, "fp32", True, True, None),
+    (1, 4, 2, 97, 161, 128, "fp32", False, False, None),
+    (1, 4, 2, 300, 333, 64, "fp32", True, False, 100),
 ]
 
 

@@ -435,9 +435,10 @@ def backward(q, k, v, o, lse, dout, bias=None, *, causal=False, scale=None, dq=N
     """dQ, dK, dV of attention(q, k, v [, bias]) through fa_backward.
 
     ``o`` and ``lse`` are the outputs of ``forward`` on the same arguments and
-    ``dout`` the gradient with respect to ``o``.  bf16/fp16 tensors; outputs
-    and the workspace are allocated with torch unless given.  ``window``
-    (requires ``causal``) calls fa_backward_window.
+    ``dout`` the gradient with respect to ``o``.  bf16/fp16 tensors, or fp32
+    at head sizes 64 and 128; outputs and the workspace are allocated with
+    torch unless given.  ``window`` (requires ``causal``) calls
+    fa_backward_window.
     """
     import torch
     lib = load_library()

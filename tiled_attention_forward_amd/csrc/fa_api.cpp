@@ -348,11 +348,13 @@ int backward_prepare(const void* q, const void* k, const void* v, const void* bi
                      int64_t D, float scale, int causal, int window, int dtype, void* workspace,
                      int64_t workspace_bytes, void* stream, fa::BwdArgs* a, bool* empty) {
   *empty = false;
-  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;  // 16-bit only
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_FP32)
+    return FA_ERR_DTYPE;  // no FP8 backward
   int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (D != 64 && D != 80 && D != 96 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;  // the backward kernels' tiles
   if (D == 256 && bias != nullptr) return FA_ERR_HEAD_DIM;  // D = 256: no logit term
+  if (dtype == FA_DTYPE_FP32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;  // as the fp32 forward
   const int esz = elem_bytes(dtype);
   const bool no_rows = (B == 0 || Hq == 0 || Nq == 0);
   const bool no_keys = (B == 0 || Hkv == 0 || Nk == 0);
@@ -372,6 +374,7 @@ int backward_prepare(const void* q, const void* k, const void* v, const void* bi
   if (Hkv > 0 && __int128(Hq / Hkv) * Nq * D * esz >= lim31) return FA_ERR_TOO_LARGE;
   if (Nk * D * esz >= lim31) return FA_ERR_TOO_LARGE;
   if (__int128(B) * Hkv * ((Nk + 127) / 128) >= lim31) return FA_ERR_TOO_LARGE;
+  if (__int128(B) * Hq * ((Nq + 127) / 128) >= lim31) return FA_ERR_TOO_LARGE;  // dQ grid
   if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
     return FA_ERR_ALIGNMENT;
   const int64_t rows = B * Hq * Nq;
@@ -467,6 +470,7 @@ extern "C" int fa_backward_chain(const void* const* q_layers, const void* const*
   if (q_layers == nullptr || k_layers == nullptr || dq_layers == nullptr || dk_layers == nullptr)
     return FA_ERR_NULL_POINTER;
   if (num_layers < 1 || num_layers > fa::kMaxChainLayers) return FA_ERR_BAD_SIZE;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;  // as fa_forward_chain
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;  // as fa_forward_chain
   const int n = int(num_layers);
   fa::BwdArgs a;

@@ -26,7 +26,9 @@
 //    delta and lse2: S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
 //    dK^T += Q^T dS with Q and dO read transposed from LDS.
 // P and dS are rounded to the input type for the MFMAs (as P is in the
-// forward); all sums are fp32.
+// forward); all sums are fp32.  fp32 inputs (D = 64, 128) take three plain
+// vector-arithmetic kernels instead (fa_bwd32_dq_kernel, then
+// fa_bwd32_kv_kernel for dV and for dK), described where they are defined.
 //
 // The Block Attention Residual chain (NL = 2-4 layers, the "Block Attention
 // Residual" post): the logits are the sum of every layer's Q_l K_l^T * scale,
@@ -874,6 +876,216 @@ hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool bias, hipStream_t 
   return e;
 }
 
+
+// ---- fp32 inputs ---------------------------------------------------------------
+// The same chain rule in plain fp32 vector arithmetic: no rounding of P or dS
+// and no reduced-precision products (the matrix cores' fp32 rate is a
+// sixteenth of their 16-bit rate, and fp32 is the parity dtype, not the
+// throughput one).  One lane per query row (dQ kernel) or per key (dV and dK
+// kernels); the other side streams through LDS in 32-row tiles, and each lane
+// reads the tile's rows from LDS as broadcasts.  Head sizes 64 and 128.
+constexpr int kB32Threads = 128;  // rows (or keys) per workgroup
+constexpr int kB32Tile = 32;      // streamed rows per LDS tile
+
+struct Bwd32Params {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* bias;  // [B, Hq, Nq, Nk] or null
+  const float* o;
+  const float* dout;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;       // workspace: delta_i per row
+  float* lse2;        // workspace: LSE_i log2(e) per row (+inf for LSE = -inf)
+  int B, Hq, Hkv, Nq, Nk, window;
+  int n_qblk, n_kblk;
+  float scale;
+  float c;            // scale * log2(e)
+};
+
+__device__ __forceinline__ bool b32_visible(int i, int j, int Nq, int Nk, bool causal, int window) {
+  return i < Nq && j < Nk && (!causal || j <= i) && (window <= 0 || j > i - window);
+}
+
+// dQ and delta: lane = query row i of head (b, h)
+template <int D, bool CAUSAL, bool BIAS>
+__global__ __launch_bounds__(kB32Threads) void fa_bwd32_dq_kernel(Bwd32Params p) {
+  __shared__ float sK[kB32Tile][D];
+  __shared__ float sV[kB32Tile][D];
+  __shared__ float sB[kB32Threads][kB32Tile + 1];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / p.n_qblk;
+  const int row0 = (blockIdx.x % p.n_qblk) * kB32Threads;
+  const int i = row0 + tid;
+  const int b = bh / p.Hq, h = bh % p.Hq, hk = h / (p.Hq / p.Hkv);
+  const bool valid = i < p.Nq;
+  const size_t qrow = (size_t(bh) * p.Nq + (valid ? i : 0)) * D;
+  const size_t kv0 = size_t(b * p.Hkv + hk) * p.Nk * D;
+  // D = 128: the dQ columns in two halves, each a pass over the keys (the
+  // Q and dO rows and a full accumulator would not fit the registers)
+  constexpr int NH = D > 64 ? 2 : 1, DH = D / NH;
+  float q[D], dov[D], dq[DH];
+  float delta = 0.f;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    q[d] = valid ? p.q[qrow + d] : 0.f;
+    dov[d] = valid ? p.dout[qrow + d] : 0.f;
+    delta = fmaf(dov[d], valid ? p.o[qrow + d] : 0.f, delta);
+  }
+  const float l = valid ? p.lse[size_t(bh) * p.Nq + i] : 0.f;
+  const float lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;   // rows with no key: P = 0
+  if (valid) {
+    p.delta[size_t(bh) * p.Nq + i] = delta;
+    p.lse2[size_t(bh) * p.Nq + i] = lse2;
+  }
+  // keys any row of the block can see
+  const int last_row = min(p.Nq, row0 + kB32Threads) - 1;
+  const int j_end = CAUSAL ? min(p.Nk, last_row + 1) : p.Nk;
+  const int j_begin = p.window > 0 ? max(0, row0 - p.window + 1) : 0;
+#pragma unroll 1
+  for (int hf = 0; hf < NH; ++hf) {
+#pragma unroll
+  for (int d = 0; d < DH; ++d) dq[d] = 0.f;
+  for (int t0 = (j_begin / kB32Tile) * kB32Tile; t0 < j_end; t0 += kB32Tile) {
+    __syncthreads();   // the previous tile's reads are done
+    for (int e = tid; e < kB32Tile * D; e += kB32Threads) {
+      const int r = e / D, d = e % D;
+      const bool in = t0 + r < p.Nk;
+      sK[r][d] = in ? p.k[kv0 + size_t(t0 + r) * D + d] : 0.f;
+      sV[r][d] = in ? p.v[kv0 + size_t(t0 + r) * D + d] : 0.f;
+    }
+    if constexpr (BIAS) {
+      for (int e = tid; e < kB32Threads * kB32Tile; e += kB32Threads) {
+        const int r = e / kB32Tile, c = e % kB32Tile;
+        const bool in = row0 + r < p.Nq && t0 + c < p.Nk;
+        sB[r][c] = in ? p.bias[(size_t(bh) * p.Nq + row0 + r) * p.Nk + t0 + c] : 0.f;
+      }
+    }
+    __syncthreads();
+    for (int jj = 0; jj < kB32Tile; ++jj) {
+      if (!b32_visible(i, t0 + jj, p.Nq, p.Nk, CAUSAL, p.window)) continue;
+      float sdot = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        sdot = fmaf(q[d], sK[jj][d], sdot);
+        dp = fmaf(dov[d], sV[jj][d], dp);
+      }
+      const float off = BIAS ? fmaf(sB[tid][jj], kLog2e, -lse2) : -lse2;
+      const float pr = exp2f(fmaf(sdot, p.c, off));
+      const float ds = pr * (dp - delta);
+#pragma unroll
+      for (int d = 0; d < DH; ++d) dq[d] = fmaf(ds, sK[jj][hf * DH + d], dq[d]);
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int d = 0; d < DH; ++d) p.dq[qrow + hf * DH + d] = dq[d] * p.scale;
+  }
+  }
+}
+
+// dV (PASS 0) or dK (PASS 1): lane = key j of KV head (b, hk); the query rows
+// of every head of the group stream through LDS with their lse2 and delta
+template <int D, bool CAUSAL, bool BIAS, int PASS>
+__global__ __launch_bounds__(kB32Threads) void fa_bwd32_kv_kernel(Bwd32Params p) {
+  __shared__ float sQ[kB32Tile][D];
+  __shared__ float sO[kB32Tile][D];   // dO rows
+  __shared__ float sL[kB32Tile];      // lse2
+  __shared__ float sD[kB32Tile];      // delta
+  const int tid = threadIdx.x;
+  const int bhk = blockIdx.x / p.n_kblk;
+  const int key0 = (blockIdx.x % p.n_kblk) * kB32Threads;
+  const int j = key0 + tid;
+  const int b = bhk / p.Hkv, hk = bhk % p.Hkv;
+  const int grp = p.Hq / p.Hkv;
+  const bool valid = j < p.Nk;
+  const size_t krow = (size_t(bhk) * p.Nk + (valid ? j : 0)) * D;
+  // dK at D = 128: the columns in two halves, each a pass over the rows
+  constexpr int NH = (PASS == 1 && D > 64) ? 2 : 1, DH = D / NH;
+  float kr[D], vr[PASS == 1 ? D : 1], acc[DH];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    kr[d] = valid ? p.k[krow + d] : 0.f;
+    if constexpr (PASS == 1) vr[d] = valid ? p.v[krow + d] : 0.f;
+  }
+  // rows any key of the block is visible to
+  const int last_key = min(p.Nk, key0 + kB32Threads) - 1;
+  const int i_begin = CAUSAL ? key0 : 0;
+  const int i_end = p.window > 0 ? min(p.Nq, last_key + p.window) : p.Nq;
+#pragma unroll 1
+  for (int hf = 0; hf < NH; ++hf) {
+#pragma unroll
+  for (int d = 0; d < DH; ++d) acc[d] = 0.f;
+  for (int hh = 0; hh < grp; ++hh) {
+    const int bh = b * p.Hq + hk * grp + hh;
+    for (int t0 = (i_begin / kB32Tile) * kB32Tile; t0 < i_end; t0 += kB32Tile) {
+      __syncthreads();
+      for (int e = tid; e < kB32Tile * D; e += kB32Threads) {
+        const int r = e / D, d = e % D;
+        const bool in = t0 + r < p.Nq;
+        const size_t g = (size_t(bh) * p.Nq + (in ? t0 + r : 0)) * D + d;
+        sQ[r][d] = in ? p.q[g] : 0.f;
+        sO[r][d] = in ? p.dout[g] : 0.f;
+      }
+      if (tid < kB32Tile) {
+        const bool in = t0 + tid < p.Nq;
+        sL[tid] = in ? p.lse2[size_t(bh) * p.Nq + t0 + tid] : INFINITY;
+        sD[tid] = in ? p.delta[size_t(bh) * p.Nq + t0 + tid] : 0.f;
+      }
+      __syncthreads();
+      for (int ii = 0; ii < kB32Tile; ++ii) {
+        const int i = t0 + ii;
+        if (!b32_visible(i, j, p.Nq, p.Nk, CAUSAL, p.window)) continue;
+        float sdot = 0.f, dp = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          sdot = fmaf(sQ[ii][d], kr[d], sdot);
+          if constexpr (PASS == 1) dp = fmaf(sO[ii][d], vr[d], dp);
+        }
+        const float bv = BIAS ? p.bias[(size_t(bh) * p.Nq + i) * p.Nk + j] : 0.f;
+        const float off = BIAS ? fmaf(bv, kLog2e, -sL[ii]) : -sL[ii];
+        const float pr = exp2f(fmaf(sdot, p.c, off));
+        if constexpr (PASS == 0) {
+#pragma unroll
+          for (int d = 0; d < DH; ++d) acc[d] = fmaf(pr, sO[ii][d], acc[d]);
+        } else {
+          const float ds = pr * (dp - sD[ii]);
+#pragma unroll
+          for (int d = 0; d < DH; ++d) acc[d] = fmaf(ds, sQ[ii][hf * DH + d], acc[d]);
+        }
+      }
+    }
+  }
+  if (valid) {
+    float* out = PASS == 0 ? p.dv : p.dk;
+    const float f = PASS == 0 ? 1.f : p.scale;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) out[krow + hf * DH + d] = acc[d] * f;
+  }
+  }
+}
+
+template <int D, bool CAUSAL, bool BIAS>
+hipError_t launch_bwd32_cb(const Bwd32Params& p, hipStream_t s) {
+  const unsigned g_dq = unsigned(p.n_qblk) * unsigned(p.B * p.Hq);
+  const unsigned g_kv = unsigned(p.n_kblk) * unsigned(p.B * p.Hkv);
+  if (g_dq) fa_bwd32_dq_kernel<D, CAUSAL, BIAS><<<g_dq, kB32Threads, 0, s>>>(p);
+  if (g_kv) {
+    fa_bwd32_kv_kernel<D, CAUSAL, BIAS, 0><<<g_kv, kB32Threads, 0, s>>>(p);
+    fa_bwd32_kv_kernel<D, CAUSAL, BIAS, 1><<<g_kv, kB32Threads, 0, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd32_d(const Bwd32Params& p, bool causal, bool bias, hipStream_t s) {
+  if (causal) return bias ? launch_bwd32_cb<D, true, true>(p, s) : launch_bwd32_cb<D, true, false>(p, s);
+  return bias ? launch_bwd32_cb<D, false, true>(p, s) : launch_bwd32_cb<D, false, false>(p, s);
+}
+
 }  // namespace
 
 // Chain: one dQ and one dK/dV launch per group of chain_targets(D, NL) layers
@@ -904,7 +1116,40 @@ hipError_t launch_bwd_chain_nl(BwdParams& p, bool causal, hipStream_t s, unsigne
 
 static BwdParams make_bwd_params(const BwdArgs& a);
 
+// fp32 inputs (D = 64 or 128): delta and dQ, then dV, then dK, in order on the
+// stream; the dV and dK kernels read delta from the workspace.
+static int launch_backward_f32(const BwdArgs& a) {
+  Bwd32Params p{};
+  p.q = static_cast<const float*>(a.q);
+  p.k = static_cast<const float*>(a.k);
+  p.v = static_cast<const float*>(a.v);
+  p.bias = static_cast<const float*>(a.bias);
+  p.o = static_cast<const float*>(a.o);
+  p.dout = static_cast<const float*>(a.dout);
+  p.lse = a.lse;
+  p.dq = static_cast<float*>(a.dq);
+  p.dk = static_cast<float*>(a.dk);
+  p.dv = static_cast<float*>(a.dv);
+  p.delta = static_cast<float*>(a.workspace);
+  p.lse2 = p.delta + backward_lse2_offset(int64_t(a.B) * a.Hq * a.Nq);
+  p.B = a.B;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.Nq = a.Nq;
+  p.Nk = a.Nk;
+  p.window = a.causal ? a.window : 0;
+  p.n_qblk = (a.Nq + kB32Threads - 1) / kB32Threads;
+  p.n_kblk = (a.Nk + kB32Threads - 1) / kB32Threads;
+  p.scale = a.scale;
+  p.c = a.scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(a.stream);
+  const hipError_t e = a.D == 64 ? launch_bwd32_d<64>(p, a.causal, a.bias != nullptr, s)
+                                 : launch_bwd32_d<128>(p, a.causal, a.bias != nullptr, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int launch_backward(const BwdArgs& a) {
+  if (a.dtype == FA_DTYPE_FP32) return launch_backward_f32(a);
   BwdParams p = make_bwd_params(a);
   const unsigned g_dq = unsigned(p.n_qblk) * unsigned(p.BH);
   const unsigned g_kv = unsigned(p.n_kblk) * unsigned(p.BHkv);
