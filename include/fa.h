@@ -73,13 +73,12 @@ typedef enum fa_status {
                            /* k or v is NULL while Nk > 0                             */
   FA_ERR_BAD_SIZE = 2,     /* a size is negative, or Hkv < 1 while Hq > 0                */
   FA_ERR_HEAD_GROUPS = 3,  /* Hq is not a multiple of Hkv                                */
-  FA_ERR_HEAD_DIM = 4,     /* D is not 64 or 128, nor 80 or 96 with bf16/fp16 (these     */
-                           /* forward-only sizes run in 128-wide tiles, per the xnwp.cn  */
-                           /* post, §5.1 and §6.4: a block narrower than the head drops  */
-                           /* or misreads columns), nor 256 with bf16/fp16 in fa_forward */
-                           /* (fused, no window); the residual chain takes 64 and 128,   */
-                           /* the backward 64, 80, 96, 128 and 256 (256 without a logit  */
-                           /* term).  Other sizes are rejected, never silently truncated */
+  FA_ERR_HEAD_DIM = 4,     /* D is not 64 or 128, nor 80, 96 or 256 with bf16/fp16 (80   */
+                           /* and 96 run in 128-wide tiles, per the xnwp.cn post, §5.1   */
+                           /* and §6.4: a block narrower than the head drops or misreads */
+                           /* columns); the backward takes 256 without a logit term, its */
+                           /* fp32 form 64 and 128, and the residual chain 64 and 128.   */
+                           /* Other sizes are rejected, never silently truncated         */
   FA_ERR_DTYPE = 5,        /* dtype is not one of fa_dtype                               */
   FA_ERR_SCALE = 6,        /* scale is NaN or infinite                                   */
   FA_ERR_ALIGNMENT = 7,    /* a tensor pointer is not aligned as required above          */
@@ -319,8 +318,7 @@ int fa_backward(const void* q, const void* k, const void* v, const void* bias,
 
 /*
  * Backward of fa_forward_window: as fa_backward, with causal = 1 and the same
- * window (window >= 1, FA_ERR_BAD_SIZE otherwise); no D = 256
- * (FA_ERR_HEAD_DIM), as for fa_forward_window.
+ * window (window >= 1, FA_ERR_BAD_SIZE otherwise).
  */
 int fa_backward_window(const void* q, const void* k, const void* v, const void* bias,
                        const void* o, const float* lse, const void* dout,

@@ -195,6 +195,8 @@ WINDOW_CASES = [
     (1, 3, 1, 20, 20, 128, "bf16", False, 6),         # group 3, fewer rows than a tile
     (1, 2, 2, 200, 200, 96, "bf16", False, 50),
     (1, 4, 2, 150, 180, 80, "fp16", True, 64),
+    (1, 2, 2, 200, 200, 256, "bf16", False, 50),      # head size 256
+    (1, 4, 2, 150, 180, 256, "fp16", False, 64),
     (1, 2, 2, 300, 300, 64, "fp32", False, 37),
     (1, 4, 1, 200, 260, 128, "fp32", True, 100),      # GQA, bias, Nk > Nq
 ]

@@ -178,6 +178,7 @@ def test_split_workspace_bytes_layout():
         o_pad = (o_bytes + 255) // 256 * 256
         assert binding.fa_split_workspace_bytes(2, 4, 100, 64, s) == o_pad + s * rows * 4
     assert binding.fa_split_workspace_bytes(1, 1, 1, 128, 1) == 512 + 4
+    assert binding.fa_split_workspace_bytes(1, 1, 1, 256, 1) == 1024 + 4   # head size 256
     assert binding.fa_split_workspace_bytes(0, 4, 100, 64, 2) == 0
     for bad, code in ((dict(num_splits=0), 2), (dict(num_splits=1025), 2), (dict(D=72), 4),
                       (dict(B=-1), 2)):
@@ -214,7 +215,7 @@ def test_split_rejections_before_launch():
     assert split_status(workspace=O) == 8            # workspace over the output
     assert split_status(workspace=Q - 256) == 8      # runs into q
     assert split_status(D=72) == 4 and split_status(q=None) == 1   # the common checks first
-    assert split_status(D=256) == 4
+    assert split_status(D=256, workspace=None) == 11   # 256 passes the head check
     # packed rows of one KV head: (Hq/Hkv) * Nq * D * 2 bytes must stay below 2^31
     assert split_status(Hq=64, Hkv=1, Nq=1 << 18, B=1, workspace_bytes=1 << 62) == 9
     # empty problem: nothing launched, no workspace needed
@@ -233,7 +234,7 @@ def test_split_noalloc_rejections_before_launch():
     the workspace), and refuses partials larger than its scratch array before
     touching the GPU."""
     assert noalloc_status(num_splits=0) == 2 and noalloc_status(num_splits=1025) == 2
-    assert noalloc_status(D=72) == 4 and noalloc_status(D=256) == 4
+    assert noalloc_status(D=72) == 4 and noalloc_status(D=256, o=Q) == 8   # 256 passes
     assert noalloc_status(q=None) == 1 and noalloc_status(o=O + 8) == 7
     assert noalloc_status(o=Q) == 8
     # FP8 is accepted (the decode step over an FP8 KV cache): the scratch
@@ -328,14 +329,16 @@ def test_window_rejections_before_launch():
     assert lib.fa_forward_window(*args, -3, a["dtype"], None) == 2
     assert lib.fa_forward_window(*args, 1 << 30, a["dtype"], None) == 9
     assert lib.fa_forward_window(*args[:11], 72, a["scale"], 16, a["dtype"], None) == 4
-    assert lib.fa_forward_window(*args[:11], 256, a["scale"], 16, a["dtype"], None) == 4
+    # 256 passes the head check (the overlap check after it fails)
+    args_o = (a["q"], a["k"], a["v"], a["bias"], a["q"]) + args[5:11]
+    assert lib.fa_forward_window(*args_o, 256, a["scale"], 16, a["dtype"], None) == 8
     bargs = (a["q"], a["k"], a["v"], None, a["o"], a["lse"], GO, DQ, DK, DV, a["B"], a["Hq"],
              a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"])
     assert lib.fa_backward_window(*bargs, 0, a["dtype"], WS, 1 << 40, None) == 2
     assert lib.fa_backward_window(*bargs, 8, binding.FA_DTYPE_FP8_E4M3, WS, 1 << 40, None) == 5
     assert lib.fa_backward_window(*bargs, 8, binding.FA_DTYPE_FP32, None, 0, None) == 11
-    assert lib.fa_backward_window(*bargs[:15], 256, a["scale"], 8, a["dtype"], WS, 1 << 40,
-                                  None) == 4   # no window at D = 256, as in the forward
+    assert lib.fa_backward_window(*bargs[:15], 256, a["scale"], 8, a["dtype"], None, 0,
+                                  None) == 11   # 256 passes the head check
 
 
 def test_chain_rejections_before_launch():

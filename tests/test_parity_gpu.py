@@ -198,6 +198,8 @@ WINDOW_CASES = [
     (1, 2, 2, 200, 200, 64, "bf16", False, 200),     # window = Nk: plain causal
     (1, 2, 2, 300, 300, 96, "bf16", False, 50),
     (1, 2, 1, 513, 513, 80, "fp16", True, 100),
+    (1, 2, 2, 300, 300, 256, "bf16", False, 50),     # head size 256
+    (1, 4, 2, 200, 260, 256, "fp16", True, 64),
 ]
 
 

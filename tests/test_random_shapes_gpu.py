@@ -37,8 +37,6 @@ def _cases(n=80, seed=2024):
         dtype = r.choice(["bf16", "bf16", "fp16", "fp32"])
         D = r.choice([64, 128] if dtype == "fp32" else [64, 80, 96, 128, 256])
         path = r.choice(["fused", "fused", "window", "split"])
-        if D == 256 and path != "fused":
-            path = "fused"
         causal = path == "window" or r.random() < 0.5
         bias = r.random() < 0.3
         hkv = r.choice([1, 2, 3])
@@ -97,8 +95,8 @@ def _backward_cases(n=40, seed=4048):
     while len(out) < n:
         dtype = r.choice(["bf16", "bf16", "fp16", "fp32"])
         D = r.choice([64, 128] if dtype == "fp32" else [64, 80, 96, 128, 256])
-        # (head size 256: no logit term and no window in the backward)
-        window = None if D == 256 else r.choice([None, None, None, 1, 16, 100])
+        # (head size 256: no logit term in the backward)
+        window = r.choice([None, None, None, 1, 16, 100])
         causal = window is not None or r.random() < 0.5
         bias = D != 256 and r.random() < 0.3
         hkv = r.choice([1, 2, 3])

@@ -41,6 +41,8 @@ SPLIT_CASES = [
     (1, 2, 2, 700, 1, 128, "bf16", True, False, 3),       # one key, splits mostly empty
     (2, 8, 2, 1, 1000, 96, "bf16", False, False, 3),      # head dims 80 and 96
     (1, 4, 2, 300, 300, 80, "fp16", True, True, 4),
+    (2, 8, 2, 1, 1000, 256, "bf16", False, False, 3),     # head size 256
+    (1, 4, 2, 200, 333, 256, "fp16", True, True, 4),
 ]
 
 

@@ -87,6 +87,8 @@ FWD_CASES = [
     ("window", 1, 4, 2, 300, 333, 64, "bf16", True, True, 100),
     ("window", 1, 4, 2, 300, 336, 64, "bf16", True, True, 100),
     ("window", 1, 4, 2, 200, 260, 128, "bf16", True, False, 64),
+    ("window", 1, 4, 2, 200, 260, 256, "bf16", True, True, 64),
+    ("split", 1, 4, 2, 150, 333, 256, "bf16", True, False, 3),
 ]
 
 
@@ -126,6 +128,7 @@ BWD_CASES = [
     (1, 4, 2, 130, 170, 64, "fp32", True, True, None),
     (1, 4, 2, 97, 161, 128, "fp32", False, False, None),
     (1, 4, 2, 300, 333, 64, "fp32", True, False, 100),
+    (1, 4, 2, 200, 260, 256, "bf16", True, False, 64),
 ]
 
 

@@ -125,7 +125,6 @@ extern "C" int fa_forward_window(const void* q, const void* k, const void* v, co
   if (window < 1) return FA_ERR_BAD_SIZE;
   if (window >= (int64_t(1) << 30)) return FA_ERR_TOO_LARGE;
   if (dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_DTYPE;  // fused FP8 forward only
-  if (D == 256) return FA_ERR_HEAD_DIM;                 // fused forward only
   return forward_common(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, 1, int(window),
                         dtype, stream);
 }
@@ -189,7 +188,7 @@ extern "C" int fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64
   if (bytes == nullptr) return FA_ERR_NULL_POINTER;
   if (B < 0 || Hq < 0 || Nq < 0 || D < 0) return FA_ERR_BAD_SIZE;
   if (num_splits < 1 || num_splits > fa::kMaxSplits) return FA_ERR_BAD_SIZE;
-  if (D != 64 && D != 80 && D != 96 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 64 && D != 80 && D != 96 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
   const __int128 rows = __int128(B) * Hq * Nq;
   if (rows * D * 4 * num_splits >= (__int128(1) << 62)) return FA_ERR_TOO_LARGE;
   *bytes = fa::split_workspace_bytes(int64_t(rows), D, num_splits);
@@ -202,7 +201,7 @@ extern "C" int fa_split_count(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, in
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || D < 0) return FA_ERR_BAD_SIZE;
   if (Hq > 0 && Hkv < 1) return FA_ERR_BAD_SIZE;
   if (Hq > 0 && Hq % Hkv != 0) return FA_ERR_HEAD_GROUPS;
-  if (D != 64 && D != 80 && D != 96 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 64 && D != 80 && D != 96 && D != 128 && D != 256) return FA_ERR_HEAD_DIM;
   *num_splits = 1;
   if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
   const int64_t lim = int64_t(1) << 30;
@@ -233,7 +232,6 @@ int split_common(const void* q, const void* k, const void* v, const void* bias, 
                  float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                  int64_t D, float scale, int causal, int dtype, int64_t num_splits,
                  void* stream, fa::LaunchArgs* a, int64_t* need) {
-  if (D == 256) return FA_ERR_HEAD_DIM;                 // fused forward only
   int st = fa_check_args(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, dtype);
   if (st != FA_OK) return st;
   *need = 0;
@@ -455,7 +453,6 @@ extern "C" int fa_backward_window(const void* q, const void* k, const void* v, c
                                   void* stream) {
   if (window < 1) return FA_ERR_BAD_SIZE;
   if (window >= (int64_t(1) << 30)) return FA_ERR_TOO_LARGE;
-  if (D == 256) return FA_ERR_HEAD_DIM;  // as fa_forward_window
   return backward_common(q, k, v, bias, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, D, scale,
                          1, int(window), dtype, workspace, workspace_bytes, stream);
 }
@@ -520,8 +517,9 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_BAD_SIZE: return "a size is negative, or Hkv < 1";
     case FA_ERR_HEAD_GROUPS: return "Hq is not a multiple of Hkv";
     case FA_ERR_HEAD_DIM:
-      return "head dimension D must be 64 or 128 (80, 96: bf16/fp16 forward, window, key split "
-             "and backward; 256: bf16/fp16 fused forward, and backward without a logit term)";
+      return "head dimension D must be 64 or 128 (80, 96 and 256: bf16/fp16 forward, window, "
+             "key split and backward, 256 with no logit term in the backward; the residual "
+             "chain takes 64 and 128)";
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_SCALE: return "scale is not finite";
     case FA_ERR_ALIGNMENT: return "a tensor pointer is misaligned (16 bytes; lse 4 bytes)";

@@ -844,8 +844,11 @@ hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool bias, hipStream_t 
   const void* dq;
   const void* kv;
   if constexpr (D == 256) {
-    // (no logit term and no window at D = 256: the API refuses both)
-    if (causal) {
+    // (no logit term at D = 256: the API refuses one)
+    if (causal && p.window > 0) {
+      dq = reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, false, true>);
+      kv = reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, false, true>);
+    } else if (causal) {
       dq = reinterpret_cast<const void*>(&fa_bwd_dq_kernel<T, D, true, false, false>);
       kv = reinterpret_cast<const void*>(&fa_bwd_dkdv_kernel<T, D, true, false, false>);
     } else {

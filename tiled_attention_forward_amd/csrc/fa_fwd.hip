@@ -204,10 +204,10 @@ template <typename T, int D, int BN, int QB, bool CAUSAL, bool BIAS, bool SPLIT,
           int NL, int KVPOL, int KH>
 // (waves per SIMD asked of the compiler: fp32 at D = 128 with 64-key tiles
 // holds 137 KB of LDS, so one workgroup per compute unit, and the D = 256
-// bias instances keep their accumulators in AGPRs at one)
+// bias and window instances keep their accumulators in AGPRs at one)
 __global__ __launch_bounds__(kThreads * KH,
                              (D == 64                                                  ? FA_MINB64
-                              : (D == 256 && BIAS)                                     ? 1
+                              : (D == 256 && (BIAS || WINDOW))                         ? 1
                               : (std::is_same<T, float>::value && D == 128 && BN == 64) ? 1
                                                                                         : 2))
 void fa_fwd_kernel(Params p) {
@@ -1330,13 +1330,18 @@ hipError_t launch_d(const Params& p, unsigned grid, hipStream_t s, bool causal, 
 // instances take one workgroup per compute unit and the accumulator registers
 // (B2 H16 S4096 causal: 322 us at two, 414 at one; with a bias, H8: 549 us
 // spilling at two, 214 at one).
-template <typename T>
+template <typename T, bool SPLIT>
 hipError_t launch_d256(const Params& p, unsigned grid, hipStream_t s, bool causal, bool bias) {
+  if constexpr (!SPLIT) {
+    if (causal && p.window > 0)
+      return bias ? launch_one<T, 256, 32, 1, true, true, false, true>(p, grid, s)
+                  : launch_one<T, 256, 32, 1, true, false, false, true>(p, grid, s);
+  }
   if (causal)
-    return bias ? launch_one<T, 256, 32, 1, true, true, false>(p, grid, s)
-                : launch_one<T, 256, 32, 1, true, false, false>(p, grid, s);
-  return bias ? launch_one<T, 256, 32, 1, false, true, false>(p, grid, s)
-              : launch_one<T, 256, 32, 1, false, false, false>(p, grid, s);
+    return bias ? launch_one<T, 256, 32, 1, true, true, SPLIT>(p, grid, s)
+                : launch_one<T, 256, 32, 1, true, false, SPLIT>(p, grid, s);
+  return bias ? launch_one<T, 256, 32, 1, false, true, SPLIT>(p, grid, s)
+              : launch_one<T, 256, 32, 1, false, false, SPLIT>(p, grid, s);
 }
 
 // 32-row query blocks per wave.  Two blocks (64 rows) halve the K/V operand
@@ -1369,9 +1374,7 @@ hipError_t launch_t(const Params& p, unsigned grid, hipStream_t s, int D, bool c
   if constexpr (!std::is_same<T, float>::value) {
     if (D == 80) return launch_d<T, 80, kBN128, 1, SPLIT>(p, grid, s, causal, bias);
     if (D == 96) return launch_d<T, 96, kBN128, 1, SPLIT>(p, grid, s, causal, bias);
-    if constexpr (!SPLIT) {
-      if (D == 256) return launch_d256<T>(p, grid, s, causal, bias);
-    }
+    if (D == 256) return launch_d256<T, SPLIT>(p, grid, s, causal, bias);
   }
   if constexpr (SPLIT) {
     // (32-key tiles without a bias, 64 with one)
