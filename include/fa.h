@@ -77,7 +77,7 @@ typedef enum fa_status {
                            /* and 96 run in 128-wide tiles, per the xnwp.cn post, §5.1   */
                            /* and §6.4: a block narrower than the head drops or misreads */
                            /* columns); the backward takes 256 without a logit term, its */
-                           /* fp32 form 64 and 128, and the residual chain 64 and 128.   */
+                           /* fp32 form 64 and 128, and the residual chain 64 to 128.    */
                            /* Other sizes are rejected, never silently truncated         */
   FA_ERR_DTYPE = 5,        /* dtype is not one of fa_dtype                               */
   FA_ERR_SCALE = 6,        /* scale is NaN or infinite                                   */
@@ -152,9 +152,10 @@ int fa_forward_window(const void* q, const void* k, const void* v, const void* b
  *   v: the current layer's V, [B, Hkv, Nk, D];
  *   o, lse, sizes, scale, causal, stream: as fa_forward; scale multiplies every
  *     layer's product.
- * bf16 and fp16 only (FA_ERR_DTYPE for fp32).  Errors as fa_forward for each
- * layer's (Q_l, K_l) with v, o and lse, plus FA_ERR_NULL_POINTER for a NULL
- * array.  The arrays are read during the call only.
+ * bf16 and fp16 only (FA_ERR_DTYPE for fp32); D = 64, 80, 96 or 128
+ * (FA_ERR_HEAD_DIM otherwise).  Errors as fa_forward for each layer's
+ * (Q_l, K_l) with v, o and lse, plus FA_ERR_NULL_POINTER for a NULL array.
+ * The arrays are read during the call only.
  */
 int fa_forward_chain(const void* const* q_layers, const void* const* k_layers,
                      int64_t num_layers, const void* v, void* o, float* lse,
@@ -344,7 +345,7 @@ int fa_backward_window(const void* q, const void* k, const void* v, const void* 
  *   dq_layers[l]: out, [B, Hq, Nq, D]; dk_layers[l]: out, [B, Hkv, Nk, D];
  *   dv: out, [B, Hkv, Nk, D]; all dtype;
  *   workspace, workspace_bytes: as for fa_backward.
- * bf16 and fp16, D = 64 or 128 (FA_ERR_HEAD_DIM), 1 to 4 layers
+ * bf16 and fp16, D = 64, 80, 96 or 128 (FA_ERR_HEAD_DIM), 1 to 4 layers
  * (FA_ERR_BAD_SIZE); NULL layer arrays give FA_ERR_NULL_POINTER.  Every
  * layer's arguments are checked as fa_backward checks its own, and
  * FA_ERR_OVERLAP is returned if an output overlaps any layer's input or

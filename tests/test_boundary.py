@@ -358,7 +358,8 @@ def test_chain_rejections_before_launch():
     assert chain([], []) == 2                                 # no layer
     assert chain([Q0, Q] * 2 + [Q], [K0, K] * 2 + [K]) == 2   # five layers
     assert chain([Q0, Q], [K0, K], dtype=binding.FA_DTYPE_FP32) == 5
-    assert chain([Q0, Q], [K0, K], D=96) == 4                 # chain: 64 and 128 only
+    assert chain([Q0, Q], [K0, K], D=72) == 4 and chain([Q0, Q], [K0, K], D=256) == 4
+    assert chain([Q0, Q], [K0, K], D=96, o=Q0) == 8           # 80 and 96 pass the head check
     assert chain([Q0, Q], [K0, K], Hq=3) == 3
     assert chain([None, Q], [K0, K]) == 1                     # a layer's Q missing
     assert chain([Q0, Q], [K0 + 8, K]) == 7                   # a layer's K misaligned
@@ -384,7 +385,8 @@ def test_chain_backward_rejections_before_launch():
     assert bchain([Q0, Q] * 2 + [Q], [K0, K] * 2 + [K], [DQ0, DQ] * 2 + [DQ],
                   [DK0, DK] * 2 + [DK]) == 2                               # five layers
     assert bchain(*ok, dtype=binding.FA_DTYPE_FP32) == 5                   # 16-bit only
-    assert bchain(*ok, D=96) == 4 and bchain(*ok, D=256) == 4              # 64 and 128 only
+    assert bchain(*ok, D=72) == 4 and bchain(*ok, D=256) == 4              # no 256 chain
+    assert bchain(*ok, D=96, workspace=None) == 11                         # 80, 96 pass
     assert bchain(*ok, Hq=3) == 3
     assert bchain([None, Q], [K0, K], [DQ0, DQ], [DK0, DK]) == 1           # a layer's Q missing
     assert bchain([Q0, Q], [K0, K], [None, DQ], [DK0, DK]) == 1            # a layer's dQ missing

@@ -35,6 +35,8 @@ CASES = [
     (4, 1, 5, 1, 77, 64, 128, "fp16", True),      # group 5, ragged rows
     (4, 1, 2, 2, 33, 31, 128, "bf16", False),     # rows < one tile, key tail
     (1, 1, 2, 2, 64, 64, 64, "bf16", True),       # one layer: the plain backward
+    (3, 1, 4, 2, 150, 200, 80, "bf16", True),     # head sizes 80 and 96
+    (4, 1, 2, 1, 97, 130, 96, "fp16", False),
 ]
 
 

@@ -34,6 +34,9 @@ CASES = [
     (4, 1, 2, 2, 1, 1, 64, "bf16", False),
     (3, 1, 2, 2, 50, 300, 128, "bf16", True),     # keys 50.. seen by no query
     (2, 1, 2, 2, 77, 1, 128, "fp16", False),      # one key: O = V_0
+    # head sizes 80 and 96 (128-wide tiles, the padding columns read as 0)
+    (3, 1, 4, 2, 200, 333, 80, "bf16", True),
+    (4, 1, 2, 1, 130, 97, 96, "fp16", False),
 ]
 
 

@@ -136,7 +136,7 @@ def _chain_cases(n=24, seed=6060):
     out = []
     while len(out) < n:
         layers = r.choice([1, 2, 3, 4])
-        D = r.choice([64, 128])
+        D = r.choice([64, 80, 96, 128])
         dtype = r.choice(["bf16", "fp16"])
         causal = r.random() < 0.5
         hkv = r.choice([1, 2, 3])

@@ -136,7 +136,7 @@ extern "C" int fa_forward_chain(const void* const* q_layers, const void* const* 
   if (q_layers == nullptr || k_layers == nullptr) return FA_ERR_NULL_POINTER;
   if (num_layers < 1 || num_layers > fa::kMaxChainLayers) return FA_ERR_BAD_SIZE;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;
-  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 64 && D != 80 && D != 96 && D != 128) return FA_ERR_HEAD_DIM;
   // each layer's operands against v, o and lse (sizes, pointers, overlap)
   for (int64_t l = 0; l < num_layers; ++l) {
     const int st = fa_check_args(q_layers[l], k_layers[l], v, nullptr, o, lse, B, Hq, Hkv, Nq,
@@ -468,7 +468,7 @@ extern "C" int fa_backward_chain(const void* const* q_layers, const void* const*
     return FA_ERR_NULL_POINTER;
   if (num_layers < 1 || num_layers > fa::kMaxChainLayers) return FA_ERR_BAD_SIZE;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_DTYPE;  // as fa_forward_chain
-  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;  // as fa_forward_chain
+  if (D != 64 && D != 80 && D != 96 && D != 128) return FA_ERR_HEAD_DIM;  // as fa_forward_chain
   const int n = int(num_layers);
   fa::BwdArgs a;
   bool empty = false;
@@ -519,7 +519,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_HEAD_DIM:
       return "head dimension D must be 64 or 128 (80, 96 and 256: bf16/fp16 forward, window, "
              "key split and backward, 256 with no logit term in the backward; the residual "
-             "chain takes 64 and 128)";
+             "chain takes 64, 80, 96 and 128)";
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_SCALE: return "scale is not finite";
     case FA_ERR_ALIGNMENT: return "a tensor pointer is misaligned (16 bytes; lse 4 bytes)";

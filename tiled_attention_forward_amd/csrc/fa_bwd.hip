@@ -109,7 +109,7 @@ constexpr int dkdv_qtile(int D, bool causal, bool bias) {
 // Keys per tile in the dQ kernel: 64, and 32 at D = 256, whose Q and dO
 // fragments (128 VGPRs) and dQ accumulator (128) take one workgroup per
 // compute unit already.
-constexpr int dq_ktile(int D, int NL) { return (D == 256 || (D == 128 && NL > 1)) ? 32 : 64; }
+constexpr int dq_ktile(int D, int NL) { return (D == 256 || (D > 64 && NL > 1)) ? 32 : 64; }
 
 struct BwdParams {
   const void* q;
@@ -309,7 +309,7 @@ __device__ __forceinline__ void store_rows(T* dst_row, const f32x16 (&acc)[NDB],
 // them in the workspace for the dK/dV kernel, which runs after it.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL, bool BIAS, bool WINDOW, int NL = 1>
-__global__ __launch_bounds__(kBwdThreads, (D == 256 || (D == 128 && NL > 1) || NL > 2) ? 1 : 2)
+__global__ __launch_bounds__(kBwdThreads, (D == 256 || (D > 64 && NL > 1) || NL > 2) ? 1 : 2)
 void fa_bwd_dq_kernel(BwdParams p) {
   using E = Elem<T>;
   using Frag = typename E::Frag;
@@ -1198,8 +1198,12 @@ int launch_backward_chain(const BwdArgs& a, const void* const* q_layers,
     }
   };
   auto launch = [&](auto tag) {
-    return a.D == 64 ? launch_d(tag, std::integral_constant<int, 64>{})
-                     : launch_d(tag, std::integral_constant<int, 128>{});
+    switch (a.D) {
+      case 64: return launch_d(tag, std::integral_constant<int, 64>{});
+      case 80: return launch_d(tag, std::integral_constant<int, 80>{});
+      case 96: return launch_d(tag, std::integral_constant<int, 96>{});
+      default: return launch_d(tag, std::integral_constant<int, 128>{});
+    }
   };
   const hipError_t e = a.dtype == FA_DTYPE_BF16 ? launch(__bf16{}) : launch(_Float16{});
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

@@ -1305,8 +1305,12 @@ hipError_t launch_chain_d(const Params& p, unsigned grid, hipStream_t s, bool ca
 template <typename T>
 hipError_t launch_chain_t(const Params& p, unsigned grid, hipStream_t s, int D, bool causal,
                           int nl) {
-  return D == 64 ? launch_chain_d<T, 64>(p, grid, s, causal, nl)
-                 : launch_chain_d<T, 128>(p, grid, s, causal, nl);
+  switch (D) {
+    case 64: return launch_chain_d<T, 64>(p, grid, s, causal, nl);
+    case 80: return launch_chain_d<T, 80>(p, grid, s, causal, nl);
+    case 96: return launch_chain_d<T, 96>(p, grid, s, causal, nl);
+    default: return launch_chain_d<T, 128>(p, grid, s, causal, nl);
+  }
 }
 
 template <typename T, int D, int BN, int QB, bool SPLIT>
