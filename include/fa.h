@@ -55,10 +55,10 @@ extern "C" {
  * of "FlashAttention principles and Triton practice" (xnwp.cn/news/15505), §7,
  * which asks for its precision loss to be evaluated: the probabilities are
  * rounded to E4M3 for the P.V product (the other arithmetic as for 16-bit
- * inputs).  fa_forward (fused) and the key-split entry points (fa_forward_split,
- * fa_forward_split_noalloc: the decode step over an FP8 KV cache), with or
- * without the causal mask, D = 64 or 128; the other entry points return
- * FA_ERR_DTYPE for it. */
+ * inputs).  fa_forward (fused), fa_forward_window and the key-split entry
+ * points (fa_forward_split, fa_forward_split_noalloc: the decode step over an
+ * FP8 KV cache), with or without the causal mask, D = 64 or 128; the other
+ * entry points return FA_ERR_DTYPE for it. */
 typedef enum fa_dtype {
   FA_DTYPE_BF16 = 0,
   FA_DTYPE_FP16 = 1,

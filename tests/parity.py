@@ -149,7 +149,7 @@ def rounding_bound_check(q, k, v, bias, scale, causal, dtype, o, lse, what=""):
     assert np.abs(lse.cpu().numpy() - l_ref).max() <= LSE_TOL, f"{what}: LSE"
 
 
-def fp8_bound_check(q, k, v, scale, causal, o, lse, what=""):
+def fp8_bound_check(q, k, v, scale, causal, o, lse, what="", window=None):
     """FP8 (E4M3) inputs: the kernel rounds each probability to E4M3 before P.V,
     as p' = p * 2^7 relative to its running max reference (p' in (0, 2^8]):
     relative error <= 2^-4 for normal values, absolute <= 2^-10 below E4M3's
@@ -161,12 +161,15 @@ def fp8_bound_check(q, k, v, scale, causal, o, lse, what=""):
     rounding; LSE is formed from the unrounded p and keeps its 1e-3 bar.
     Returns (max |dO|, mean |dO|, worst err / bound)."""
     bq, bk, bv = f64(q), f64(k), f64(v)
-    o_ref, l_ref = attention_forward(bq, bk, bv, None, scale=scale, causal=causal)
-    o_abs, _ = attention_forward(bq, bk, np.abs(bv), None, scale=scale, causal=causal)
+    o_ref, l_ref = attention_forward(bq, bk, bv, None, scale=scale, causal=causal, window=window)
+    o_abs, _ = attention_forward(bq, bk, np.abs(bv), None, scale=scale, causal=causal,
+                                 window=window)
     m_abs, _ = attention_forward(np.zeros_like(bq), bk, np.abs(bv), None, scale=scale,
-                                 causal=causal)
+                                 causal=causal, window=window)
     nq, nk = bq.shape[2], bk.shape[2]
     count = (np.minimum(np.arange(nq) + 1, nk) if causal else np.full(nq, nk)).astype(np.float64)
+    if window is not None:
+        count = np.minimum(count, float(window))
     bound = (2.0 ** -4 * o_abs + 2.0 ** -17 * m_abs * count[None, None, :, None]
              + 2.0 ** -9 * np.abs(o_ref) + 1e-4)
     err = np.abs(f64(o) - o_ref)

@@ -410,7 +410,11 @@ def test_fp8_rejections_before_launch():
     a = dict(OK_ARGS)
     args = (a["q"], a["k"], a["v"], None, a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
             a["Nq"], a["Nk"], a["D"], a["scale"])
-    assert lib.fa_forward_window(*args, 16, fp8, None) == 5
+    # the window takes FP8 (no bias): past the type check, an overlap is what fails
+    o_over = args[:4] + (a["q"],) + args[5:]
+    assert lib.fa_forward_window(*o_over, 16, fp8, None) == 8
+    bias_w = args[:3] + (BIAS,) + args[4:]
+    assert lib.fa_forward_window(*bias_w, 16, fp8, None) == 5
     # the key split takes FP8 (no bias): past the type check, a missing
     # workspace is what fails
     assert lib.fa_forward_split(*args, 1, fp8, 2, None, 0, None) == 11

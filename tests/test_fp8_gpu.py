@@ -70,8 +70,8 @@ def test_fp8_rejections(gpu_device):
         binding.forward(q, k, v, b)
     with pytest.raises(binding.FaError):          # nor on the key-split path
         binding.forward_split(q, k, v, b, num_splits=2)
-    with pytest.raises(binding.FaError):          # no window with FP8
-        binding.forward(q, k, v, None, causal=True, window=16)
+    with pytest.raises(binding.FaError):          # nor with the window
+        binding.forward(q, k, v, b, causal=True, window=16)
 
 
 def test_fp8_full_size_sampled(gpu_device):
@@ -145,3 +145,26 @@ def test_fp8_decode_full_size(gpu_device):
     _log(f"  max {mx:.2e} mean {mean:.2e} worst err/bound {ratio:.2f}")
     del q, k, v, o, lse
     torch.cuda.empty_cache()
+
+
+WINDOW_CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, window
+    (1, 2, 2, 300, 300, 64, 37),
+    (1, 4, 2, 513, 600, 128, 100),     # GQA, Nk > Nq
+    (2, 2, 1, 1000, 1000, 64, 256),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_fp8_window_within_bound(gpu_device, case):
+    """FP8 inputs with the causal sliding window (fa_forward_window): the same
+    bound over each row's visible keys."""
+    B, Hq, Hkv, Nq, Nk, D, win = case
+    w = custom(B, Hq, Hkv, Nq, Nk, D, "fp8", True, False)
+    _log(f"fp8 window case {case}")
+    q, k, v, _ = (None if t is None else t.to(gpu_device) for t in make_inputs(w, seed=57))
+    o, lse = binding.forward(q, k, v, None, causal=True, scale=w.scale, window=win)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    mx, mean, ratio = fp8_bound_check(q, k, v, w.scale, True, o, lse, str(case), window=win)
+    _log(f"  max {mx:.2e} mean {mean:.2e} worst err/bound {ratio:.2f}")

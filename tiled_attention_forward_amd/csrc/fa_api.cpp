@@ -124,7 +124,6 @@ extern "C" int fa_forward_window(const void* q, const void* k, const void* v, co
                                  int dtype, void* stream) {
   if (window < 1) return FA_ERR_BAD_SIZE;
   if (window >= (int64_t(1) << 30)) return FA_ERR_TOO_LARGE;
-  if (dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_DTYPE;  // fused FP8 forward only
   return forward_common(q, k, v, bias, o, lse, B, Hq, Hkv, Nq, Nk, D, scale, 1, int(window),
                         dtype, stream);
 }

@@ -256,7 +256,7 @@ void fa_fwd_kernel(Params p) {
   static_assert(VTR || KCH * kThreads * VEC == BN * D, "K tile must split evenly");
   static_assert(NL >= 1 && NL <= kMaxChainLayers, "chain length");
   static_assert(NL == 1 || (VTR && !BIAS && !SPLIT && !WINDOW), "chain instances");
-  static_assert(!F8 || (NL == 1 && !BIAS && !WINDOW && D == DL && BN == 64), "FP8 instances");
+  static_assert(!F8 || (NL == 1 && !BIAS && D == DL && BN == 64), "FP8 instances");
   static_assert(KH == 1 || (KH == 2 && VTR && NL == 1 && !SPLIT && !BIAS), "key-half instances");
   // FP8: P is stored as e4m3 for the P.V product.  It is taken as
   // 2^(t - m_ref + 7) with the rescale threshold at 1, so every p lies in
@@ -1435,6 +1435,9 @@ Params make_params(const LaunchArgs& a, int rows_per_block, int n_rows) {
 // FP8 inputs: fused forward without a bias, D = 64 or 128 (checked by the API).
 hipError_t launch_f8(const Params& p, unsigned grid, hipStream_t s, int D, bool causal) {
   using F8 = fp8e4m3;
+  if (causal && p.window > 0)
+    return D == 64 ? launch_one<F8, 64, 64, 1, true, false, false, true>(p, grid, s)
+                   : launch_one<F8, 128, 64, 1, true, false, false, true>(p, grid, s);
   if (D == 64)
     return causal ? launch_one<F8, 64, 64, 1, true, false, false, false, 1, FA_KH64_F8>(p, grid,
                                                                                          s)
