@@ -137,7 +137,8 @@ def rounding_bound_check(q, k, v, bias, scale, causal, dtype, o, lse, what=""):
     input type (2^-8 bf16, 2^-11 fp16), each probability is rounded before P.V
     (relative error <= u per term) and O is rounded once (<= u relative), so
     elementwise |dO| <= u * (P.|V|) + u * |O| + 1e-4, the last term covering fp32
-    accumulation and the exp2 approximation.  LSE keeps its 1e-3 bar."""
+    accumulation and the exp2 approximation.  The mean of |dO| keeps the
+    stated mean bar (1e-3), and LSE its 1e-3 bar."""
     u = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}[dtype]
     bq, bk, bv = f64(q), f64(k), f64(v)
     bb = None if bias is None else f64(bias)
@@ -146,6 +147,7 @@ def rounding_bound_check(q, k, v, bias, scale, causal, dtype, o, lse, what=""):
     bound = u * o_abs + u * np.abs(o_ref) + 1e-4
     err = np.abs(f64(o) - o_ref)
     assert np.all(err <= bound), f"{what}: worst err/bound {float((err / bound).max())}"
+    assert err.mean() <= O_TOL[dtype][1], f"{what}: mean abs {float(err.mean())}"
     assert np.abs(lse.cpu().numpy() - l_ref).max() <= LSE_TOL, f"{what}: LSE"
 
 
