@@ -1168,16 +1168,18 @@ __global__ __launch_bounds__(kMergeWaves * 64) void fa_merge_kernel(
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (ok && m != -INFINITY) {
+      // (every part's O is read, so that the loads of one wave's parts do not
+      // wait on their LSE; an empty part's O, which may be any bits, is
+      // selected away rather than multiplied by 0)
 #pragma unroll 4
       for (int sp = wave; sp < n_parts; sp += kMergeWaves) {
         const float ls = part_lse[sp * rows + row];
-        if (ls != -INFINITY) {
-          const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
-          const f32x4 x = *reinterpret_cast<const f32x4*>(part_o + (sp * rows + row) * D + 4 * c4);
-          wsum += w;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(part_o + (sp * rows + row) * D + 4 * c4);
+        const bool live = ls != -INFINITY;
+        const float w = live ? __builtin_amdgcn_exp2f((ls - m) * kLog2e) : 0.f;
+        wsum += w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, x[e], acc[e]);
-        }
+        for (int e = 0; e < 4; ++e) acc[e] = live ? fmaf(w, x[e], acc[e]) : acc[e];
       }
     }
     s_m[wave][lane] = m;
